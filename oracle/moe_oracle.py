@@ -1,0 +1,379 @@
+"""Oracle for the post-router MoE layer: plain, slow, obviously correct, CPU, fp64.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the package's smoke() entry and the
+benchmark's cpu_baseline leg may import or run this module; the HIP library
+never calls it and shares no code with it.
+
+What the layer computes (Megatron-LM PR #6572, Summary and Design: the backend
+replaces the post-router path, meaning dispatch, routed and shared expert
+computation, and combine; Megatron Core API docs, mok.backend,
+MoKMegakernel.forward(hidden_states, probs, routing_map) returns an output of
+the hidden states' shape):
+
+    out[t] = FFN_shared(x_t) + sum_{k : e_tk != -1} w_tk * FFN_{e_tk}(x_t)
+    FFN_W(x) = W_down (silu(W_gate x) * (W_up x)),   silu(z) = z / (1 + exp(-z))
+
+with the fixed-width routing table (e_tk, w_tk) produced from the dense
+routing map as described in PR #6572, Design > Authoritative routing maps.
+
+Precision: inputs are the exact stored bits (BF16, or E4M3 payload times E8M0
+block scale) decoded to float64; all arithmetic is float64.  The oracle does
+not model any rounding the fast path applies to intermediate activations.
+
+Readings of points the pages leave open:
+  * expert IDs in a table row are ascending, valid IDs first, -1 trailing;
+    the gathered probability at a -1 slot is 0;
+  * a row with more than topk routes is invalid input (raises);
+  * inside an expert's segment, routed (token, k) pairs are ordered by
+    ascending token;
+  * FC1 holds the gate rows [0, I) then the up rows [I, 2I);
+  * the shared expert has weight 1 and no output gate;
+  * grad_probs is the full gradient of the dense probs tensor (zero off the
+    map); main_grad receives the weight gradient by accumulation (+=);
+  * MXFP8 forward uses the rowwise copy, dgrad the columnwise copy.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_decode", "e4m3_decode", "e8m0_decode", "mxfp8_decode_rowwise",
+    "mxfp8_decode_colwise", "compact_routing", "dispatch_index", "silu", "dsilu",
+    "swiglu_ffn", "Weights", "moe_forward", "moe_forward_f64", "moe_backward",
+    "moe_backward_f64", "RouteOverflow",
+]
+
+
+class RouteOverflow(ValueError):
+    """A routing-map row has more true entries than the fixed table width."""
+
+
+# ----------------------------------------------------------------------------------
+# storage decoding
+# ----------------------------------------------------------------------------------
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns -> float64: a bfloat16 is the top half of a float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3FN codes -> float64 (BASELINE workload: "FP8 E4M3 payload").
+
+    sign s, exponent field f (4 bits, bias 7), mantissa m (3 bits):
+      f >= 1 : (-1)^s * 2^(f-7) * (1 + m/8)
+      f == 0 : (-1)^s * 2^-6 * (m/8)              (subnormal)
+      f == 15 and m == 7 : NaN (the format has no infinities)
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = c >> 7
+    f = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(f == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, f - 7))
+    val = np.where(s == 1, -mag, mag)
+    return np.where((f == 15) & (m == 7), np.nan, val)
+
+
+def e8m0_decode(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale byte b -> 2^(b - 127); b == 255 is NaN."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+def mxfp8_decode_rowwise(payload: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """W[r, c] = E4M3(payload[r, c]) * E8M0(scale[r, c // 32])."""
+    R, C = payload.shape
+    assert scale.shape == (R, C // 32), (scale.shape, (R, C // 32))
+    return e4m3_decode(payload) * np.repeat(e8m0_decode(scale), 32, axis=1)
+
+
+def mxfp8_decode_colwise(payload: np.ndarray, colscale: np.ndarray) -> np.ndarray:
+    """W[r, c] = E4M3(payload[r, c]) * E8M0(colscale[r // 32, c]); the column
+    scale has shape (rows // 32, columns) (Megatron-LM PR #8210, review thread
+    on the per-expert MXFP8 scale conversion)."""
+    R, C = payload.shape
+    assert colscale.shape == (R // 32, C), (colscale.shape, (R // 32, C))
+    return e4m3_decode(payload) * np.repeat(e8m0_decode(colscale), 32, axis=0)
+
+
+# ----------------------------------------------------------------------------------
+# routing: dense map -> fixed-width table -> expert-contiguous dispatch order
+# ----------------------------------------------------------------------------------
+def compact_routing(routing_map: np.ndarray, probs: np.ndarray, topk: int):
+    """Dense routing map -> fixed-width expert-ID table with gathered probabilities.
+
+    Megatron-LM PR #6572, Design > Authoritative routing maps: the dense map is
+    converted to a fixed-width representation and the router probabilities at
+    those routes are gathered; a missing route is expert ID -1, so a token with
+    fewer than topk routes keeps exactly its routing decisions.
+
+    Returns top_experts int32 [T, K] and router_weights [T, K] in probs' dtype
+    (a copy of probs at the listed routes, 0 at -1 slots).
+    """
+    T, E = routing_map.shape
+    top = np.full((T, topk), -1, dtype=np.int32)
+    rw = np.zeros((T, topk), dtype=np.asarray(probs).dtype)
+    for t in range(T):
+        listed = [e for e in range(E) if routing_map[t, e]]
+        if len(listed) > topk:
+            raise RouteOverflow(f"token {t} has {len(listed)} routes > topk={topk}")
+        for k, e in enumerate(listed):
+            top[t, k] = e
+            rw[t, k] = probs[t, e]
+    return top, rw
+
+
+def dispatch_index(top_experts: np.ndarray, num_experts: int):
+    """Token dispatch on one device: the permutation of routed (token, k) pairs
+    into expert-contiguous segments (PR #6572 Summary: "dispatch").
+
+    counts[e]     number of (t, k) with top_experts[t, k] == e
+    offsets[e]    exclusive prefix sum of counts (offsets[E] = S, all valid slots)
+    slot_of[t,k]  offsets[e] + (number of earlier tokens t' < t routed to e); -1 at pads
+    slot_token[s] t * K + k of the pair placed at slot s
+    """
+    T, K = top_experts.shape
+    counts = np.zeros(num_experts, dtype=np.int32)
+    for t in range(T):
+        for k in range(K):
+            e = int(top_experts[t, k])
+            if e >= 0:
+                counts[e] += 1
+    offsets = np.zeros(num_experts + 1, dtype=np.int32)
+    for e in range(num_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+    S = int(offsets[num_experts])
+    slot_of = np.full((T, K), -1, dtype=np.int32)
+    slot_token = np.full(S, -1, dtype=np.int32)
+    seen = np.zeros(num_experts, dtype=np.int32)
+    for t in range(T):                      # ascending token order inside each expert
+        for k in range(K):
+            e = int(top_experts[t, k])
+            if e >= 0:
+                s = offsets[e] + seen[e]
+                seen[e] += 1
+                slot_of[t, k] = s
+                slot_token[s] = t * K + k
+    return counts, offsets, slot_of, slot_token
+
+
+# ----------------------------------------------------------------------------------
+# one SwiGLU expert
+# ----------------------------------------------------------------------------------
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def dsilu(z):
+    """d/dz [z * sigmoid(z)] = sigmoid(z) * (1 + z * (1 - sigmoid(z)))."""
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def swiglu_ffn(X, Wg, Wu, Wd):
+    """Rows of X through one SwiGLU expert: a = X Wg^T, b = X Wu^T,
+    h = silu(a) * b, y = h Wd^T.  Returns (a, b, h, y)."""
+    a = X @ Wg.T
+    b = X @ Wu.T
+    h = silu(a) * b
+    y = h @ Wd.T
+    return a, b, h, y
+
+
+class Weights:
+    """Float64 views of the six weights, in the runtime's argument order
+    (Megatron Core API docs, mok.runtime, _MoKWeightArguments: shared gate,
+    shared up, shared down, routed gate, routed up, routed down).
+
+    shared      : (Wg [I,H], Wu [I,H], Wd [H,I])
+    routed(e)   : (Wg, Wu, Wd) as used by the forward
+    routed_t(e) : (Wg, Wu, Wd) as used by dgrad (columnwise decode for MXFP8)
+
+    Construct with `from_bits` from the stored payloads; routed experts are
+    decoded on demand, one at a time.
+    """
+
+    def __init__(self, shared, routed_fn, routed_dgrad_fn=None):
+        self.shared = shared
+        self._routed = routed_fn
+        self._routed_t = routed_dgrad_fn or routed_fn
+
+    def routed(self, e):
+        return self._routed(e)
+
+    def routed_t(self, e):
+        return self._routed_t(e)
+
+    @staticmethod
+    def from_bits(inter: int, shared_fc1, shared_fc2, routed_getter, routed_dtype: str):
+        """shared_fc1 u16 [2I, H], shared_fc2 u16 [H, I]; routed_getter(e) -> dict of
+        bits (see moe_inputs.routed_expert).  Gate = FC1 rows [0, I), up = rows [I, 2I)
+        (Megatron Core API docs, mok.runtime, _gate_up_weight_arguments: gate and up
+        are row views of the combined FC1)."""
+        I = inter
+        s1 = bf16_decode(shared_fc1)
+        s2 = bf16_decode(shared_fc2)
+        shared = (s1[:I], s1[I:2 * I], s2)
+
+        if routed_dtype == "bf16":
+            def fwd(e):
+                d = routed_getter(e)
+                w1 = bf16_decode(d["fc1"])
+                return w1[:I], w1[I:2 * I], bf16_decode(d["fc2"])
+            return Weights(shared, fwd)
+
+        def fwd(e):
+            d = routed_getter(e)
+            w1 = mxfp8_decode_rowwise(d["fc1"], d["fc1_s"])
+            return w1[:I], w1[I:2 * I], mxfp8_decode_rowwise(d["fc2"], d["fc2_s"])
+
+        def bwd(e):
+            d = routed_getter(e)
+            w1 = mxfp8_decode_colwise(d["fc1_c"], d["fc1_cs"])
+            return w1[:I], w1[I:2 * I], mxfp8_decode_colwise(d["fc2_c"], d["fc2_cs"])
+        return Weights(shared, fwd, bwd)
+
+
+# ----------------------------------------------------------------------------------
+# the layer
+# ----------------------------------------------------------------------------------
+def _routes_by_expert(top_experts, router_weights, tokens, num_experts):
+    """For each expert, the (token, k, weight) triples among `tokens` routed to it."""
+    by = [[] for _ in range(num_experts)]
+    for t in tokens:
+        for k in range(top_experts.shape[1]):
+            e = int(top_experts[t, k])
+            if e >= 0:
+                by[e].append((t, k, float(router_weights[t, k])))
+    return by
+
+
+def moe_forward(x_bits, probs, routing_map, topk, weights: Weights, tokens=None):
+    """out rows for `tokens` (all tokens when None), float64 [len(tokens), H],
+    from BF16 hidden-state bits."""
+    T = routing_map.shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    return moe_forward_f64(bf16_decode(x_bits[tokens]), probs, routing_map, topk, weights, tokens)
+
+
+def moe_forward_f64(x, probs, routing_map, topk, weights: Weights, tokens=None):
+    """The forward on float64 hidden states x [len(tokens), H] (rows of `tokens`).
+
+    out[t] = FFN_shared(x_t) + sum over valid routes of w_tk * FFN_{e_tk}(x_t)
+    (shared expert weight 1, no output gate: Megatron-LM PR #6572, Supported
+    configurations, the shared output gate is not supported).
+    """
+    T, E = routing_map.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    top, rw = compact_routing(routing_map, probs, topk)
+    x = np.asarray(x, dtype=np.float64)
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    _, _, _, out = swiglu_ffn(x, *weights.shared)
+    for e, lst in enumerate(_routes_by_expert(top, rw, tokens, E)):
+        if not lst:
+            continue
+        rows = np.array([pos[t] for t, _, _ in lst])
+        w = np.array([w for _, _, w in lst])
+        _, _, _, y = swiglu_ffn(x[rows], *weights.routed(e))
+        for j, r in enumerate(rows):     # fixed order; np.add.at would also do
+            out[r] += w[j] * y[j]
+    return out
+
+
+def moe_backward(dy_bits, x_bits, probs, routing_map, topk, weights: Weights,
+                 tokens=None, experts=None, shared_grads=True):
+    """moe_backward_f64 on BF16 bits of dy and x."""
+    return moe_backward_f64(bf16_decode(dy_bits), bf16_decode(x_bits), probs, routing_map,
+                            topk, weights, tokens, experts, shared_grads)
+
+
+def moe_backward_f64(dy_all, x_all, probs, routing_map, topk, weights: Weights,
+                     tokens=None, experts=None, shared_grads=True):
+    """Gradients of sum(dy * out) with respect to x, probs and the six weights.
+
+    Returns dict:
+      dx      float64 [len(tokens), H]        rows for `tokens` (all when None)
+      dprobs  float64 [len(tokens), E]        zero where routing_map is false
+      dW      {e: (dWg, dWu, dWd)} for e in `experts` (all when None), computed from
+              every token routed to e;  "shared": (dWg, dWu, dWd) when shared_grads
+
+    Per route (t, k) to expert e with weight w, g = dy[t]:
+      a = Wg x, b = Wu x, h = silu(a) b, y = Wd h
+      dprobs[t, e] = g . y
+      gh = w Wd^T g ; da = gh * b * silu'(a) ; db = gh * silu(a)
+      dx[t] += Wg^T da + Wu^T db
+      dWd += w g h^T ; dWg += da x^T ; dWu += db x^T
+    and the shared expert likewise with w = 1 and no probability gradient.
+    The weight gradients are what the caller's main_grad receives by
+    accumulation (Megatron-LM PR #6572, Design > Gradient accumulation; PR #8210,
+    review thread on the wgrad accumulation precision).
+    """
+    T, E = routing_map.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    experts = range(E) if experts is None else experts
+    top, rw = compact_routing(routing_map, probs, topk)
+
+    x_all = np.asarray(x_all, dtype=np.float64)
+    dy_all = np.asarray(dy_all, dtype=np.float64)
+
+    # --- token-side gradients for the requested tokens ---
+    x = x_all[tokens]
+    g = dy_all[tokens]
+    pos = {int(t): i for i, t in enumerate(tokens)}
+    dx = np.zeros_like(x)
+    dprobs = np.zeros((len(tokens), E))
+
+    Wg, Wu, Wd = weights.shared
+    a, b, h, _ = swiglu_ffn(x, Wg, Wu, Wd)
+    gh = g @ Wd
+    da = gh * b * dsilu(a)
+    db = gh * silu(a)
+    dx += da @ Wg + db @ Wu
+
+    for e, lst in enumerate(_routes_by_expert(top, rw, tokens, E)):
+        if not lst:
+            continue
+        rows = np.array([pos[t] for t, _, _ in lst])
+        w = np.array([w for _, _, w in lst])
+        Wg, Wu, Wd = weights.routed(e)
+        a, b, h, y = swiglu_ffn(x[rows], Wg, Wu, Wd)
+        dprobs[rows, e] = np.sum(g[rows] * y, axis=1)
+        Tg, Tu, Td = weights.routed_t(e)
+        gh = w[:, None] * (g[rows] @ Td)
+        da = gh * b * dsilu(a)
+        db = gh * silu(a)
+        dxe = da @ Tg + db @ Tu
+        for j, r in enumerate(rows):
+            dx[r] += dxe[j]
+
+    # --- weight gradients: every token routed to the requested experts ---
+    dW = {}
+    need = set(int(e) for e in experts)
+    if need:
+        all_by = _routes_by_expert(top, rw, range(T), E)
+        for e in sorted(need):
+            lst = all_by[e]
+            Wg, Wu, Wd = weights.routed(e)
+            if not lst:
+                dW[e] = (np.zeros_like(Wg), np.zeros_like(Wu), np.zeros_like(Wd))
+                continue
+            ts = np.array([t for t, _, _ in lst])
+            w = np.array([w for _, _, w in lst])
+            X = x_all[ts]
+            G = dy_all[ts]
+            a, b, h, _ = swiglu_ffn(X, Wg, Wu, Wd)
+            Tg, Tu, Td = weights.routed_t(e)
+            gh = w[:, None] * (G @ Td)
+            da = gh * b * dsilu(a)
+            db = gh * silu(a)
+            dW[e] = (da.T @ X, db.T @ X, (w[:, None] * G).T @ h)
+    if shared_grads:
+        X = x_all
+        G = dy_all
+        Wg, Wu, Wd = weights.shared
+        a, b, h, _ = swiglu_ffn(X, Wg, Wu, Wd)
+        gh = G @ Wd
+        da = gh * b * dsilu(a)
+        db = gh * silu(a)
+        dW["shared"] = (da.T @ X, db.T @ X, G.T @ h)
+    return {"dx": dx, "dprobs": dprobs, "dW": dW}
