@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Benchmark of the post-router MoE layer (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One step = moe_forward + moe_backward over one batch of seeded synthetic input
+(routing compaction, dispatch, routed + shared SwiGLU experts, combine, and the
+backward with FP32 main_grad accumulation and the dense probability gradient).
+Inputs are resident in HBM before the timed region.  Prints one JSON line.
+
+Throughput is algorithmic TFLOPS: 18 * H * I * (S + T) flops per step, S = valid
+routed slots, T = tokens (shared expert).  The roofline object describes the
+dominant kernel, timed live with HIP events on the stream it runs on; the
+cpu_baseline object times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK = {"bf16": 2516.6, "mxfp8": 5033.2}   # dense TFLOP/s, MI355X
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2: 4096-token BF16 layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    return ap.parse_args()
+
+
+def wgrad_fc1_bytes(cfg, slots):
+    """Algorithmic HBM bytes of one launch of the FC1 weight-gradient kernel: every routed
+    and shared FC1 main_grad element (2I x H FP32 per expert) read and written once, plus
+    the dfc1 (2I) and input (H) bf16 rows of every routed slot and every token read once."""
+    E, H, I, T = cfg.experts, cfg.hidden, cfg.inter, cfg.tokens
+    return (E + 1) * 2 * I * H * 8 + (slots + T) * (2 * I + H) * 2
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "moe_megakernel_amd", "csrc")
+    for n in sorted(os.listdir(d)):
+        with open(os.path.join(d, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, dp, n_tokens):
+    """The oracle, as it stands, on the first n_tokens tokens of the same workload
+    (forward + backward incl. every routed expert's and the shared expert's weight
+    gradients over those tokens)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as O
+
+    n = min(n_tokens, cfg.tokens)
+    rm = dp.np_rmap[:n]
+    pr = dp.np_probs[:n]
+    W = O.Weights.from_bits(cfg.inter, dp.np_s1, dp.np_s2, lambda e: dp.np_routed[e], cfg.routed)
+    t0 = time.perf_counter()
+    O.moe_forward(dp.np_x[:n], pr, rm, cfg.topk, W)
+    O.moe_backward(dp.np_dy[:n], dp.np_x[:n], pr, rm, cfg.topk, W)
+    dt = time.perf_counter() - t0
+    s = int(rm.sum())
+    flops = 18.0 * cfg.hidden * cfg.inter * (s + n)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n} of {cfg.tokens} tokens ({s} routed slots), fp64 numpy oracle, "
+                      f"forward+backward incl. all weight gradients; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import moe_inputs as gen
+    import moe_megakernel_amd as mk
+    from moe_inputs.device import DeviceProblem
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    mk.load()
+    cfg = gen.config(args.config)
+    t0 = time.time()
+    dp = DeviceProblem(cfg, backward=True)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s: {cfg.name}", file=sys.stderr, flush=True)
+
+    def step():
+        dp.forward()
+        dp.backward()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    mk.moe_kernel_timer_read()                      # drop warmup records
+    mk.moe_kernel_timer_enable(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    mk.moe_kernel_timer_enable(False)
+    ktimes = mk.moe_kernel_timer_read()
+
+    ms = elapsed / args.steps * 1e3
+    slots = dp.slots
+    flops = 18.0 * cfg.hidden * cfg.inter * (slots + cfg.tokens)
+    tflops = flops / (ms * 1e-3) / 1e12
+    dtype = cfg.routed
+    routed_fl = 18.0 * cfg.hidden * cfg.inter * slots
+    shared_fl = 18.0 * cfg.hidden * cfg.inter * cfg.tokens
+    mfma_frac = (routed_fl / (MFMA_PEAK[dtype] * 1e12) + shared_fl / (MFMA_PEAK["bf16"] * 1e12)) / (ms * 1e-3)
+
+    dom = "wgrad_fc1"
+    n_l, tot_ms = ktimes.get(dom, (0, 0.0))
+    avg_ms = tot_ms / max(n_l, 1)
+    alg_bytes = wgrad_fc1_bytes(cfg, slots)
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": counter_traffic(dom), "avg_launch_ms": round(avg_ms, 4),
+                "alg_bytes_per_launch": alg_bytes}
+
+    line = {
+        "metric": "MoE layer fwd+bwd TFLOPS and % of MFMA peak, 4096 tokens, 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "mfma_peak_frac": round(mfma_frac, 4),
+        "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden,
+                   "experts": cfg.experts, "topk": cfg.topk, "intermediate": cfg.inter,
+                   "routed_slots": slots, "routed_weights": cfg.routed, "layout": cfg.layout,
+                   "routing": cfg.routing, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, dp, args.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

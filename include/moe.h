@@ -1,0 +1,208 @@
+/*
+ * moe.h -- C ABI of the MI355X post-router MoE layer library (libmoe_mi355x.so).
+ *
+ * The library executes the post-router part of a Mixture-of-Experts layer on
+ * one GPU: token dispatch, the routed SwiGLU experts, the fused shared expert
+ * and the probability-weighted combine, forward and backward.  That is the
+ * path the megakernel backend replaces (Megatron-LM PR #6572, Summary; the
+ * forward takes hidden_states, probs and routing_map and returns an output of
+ * the hidden states' shape: Megatron Core API docs, mok.backend,
+ * MoKMegakernel.forward).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Ownership.  The caller owns every byte: inputs, outputs, weights,
+ *    main_grad, the forward->backward context `saved` and the workspace.  The
+ *    library never allocates device memory, never frees, never copies weight
+ *    payloads and keeps no pointer across calls: arguments are non-owning
+ *    references (Megatron Core API docs, mok.runtime, _MoKWeightArguments).
+ *    Pointer tables (`table` fields) are device arrays owned by the caller.
+ *  Streams.  All work is enqueued on the caller's `stream`; no host
+ *    synchronisation and no device-to-host copy happens inside a call, so a
+ *    call can be captured into a HIP graph.  Calls that use distinct `saved`
+ *    and workspace buffers may run concurrently.
+ *  Errors.  Arguments are validated on the host before anything is enqueued;
+ *    a non-OK status means nothing was launched.  MOE_ERR_HIP reports a
+ *    failed kernel launch.  Data-dependent errors found on the device (a
+ *    routing-map row with more than `topk` true entries) set a status word in
+ *    `saved` (see moe_saved_view); outputs of that call are then unspecified.
+ *    No entry point throws or aborts.
+ *  Layouts.  Every matrix is row-major; strides are in elements.
+ *
+ * Sizes: T tokens (all leading dims of hidden_states flattened), H hidden,
+ * I intermediate (one value for routed and shared experts: PR #6572,
+ * Supported configurations, current limitations), E local routed experts,
+ * K = topk.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,            /* a required pointer is NULL                               */
+  MOE_ERR_SHAPE = 2,           /* a size is out of range or not a multiple the kernels need */
+  MOE_ERR_DTYPE = 3,           /* unsupported element type (e.g. non-BF16 shared expert)  */
+  MOE_ERR_LAYOUT = 4,          /* inconsistent strides / both or neither of base and table */
+  MOE_ERR_UNSUPPORTED = 5,     /* a configuration the pages reject (no shared expert,
+                                  shared output gate, SwiGLU clamp)                        */
+  MOE_ERR_WORKSPACE = 6,       /* saved / workspace buffer missing or too small            */
+  MOE_ERR_ROUTE_OVERFLOW = 7,  /* device status word: a row had more than topk routes      */
+  MOE_ERR_HIP = 8              /* a HIP launch failed                                      */
+} moe_status;
+
+typedef enum { MOE_BF16 = 1, MOE_FP32 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
+
+#define MOE_FLAG_HAS_SHARED 1u
+
+/* Problem sizes and options. */
+typedef struct {
+  int64_t tokens;        /* T >= 0                                                        */
+  int64_t hidden;        /* H, multiple of 128                                            */
+  int64_t intermediate;  /* I, multiple of 128                                            */
+  int32_t experts;       /* E in [1, 255]                                                 */
+  int32_t topk;          /* K in [1, min(8, E)]                                           */
+  int32_t routed_dtype;  /* MOE_BF16 or MOE_MXFP8_E4M3 (PR #6572, Supported configurations) */
+  uint32_t flags;        /* MOE_FLAG_HAS_SHARED must be set: the fused shared expert is
+                            required (PR #8210, review thread on the config guards)        */
+  float swiglu_limit;    /* must be 0 (no clamp)                                          */
+} moe_problem;
+
+/* One logical matrix per expert, [rows][cols], row-major.  Exactly one of
+ * `base` (single grouped tensor, expert e at base + e*expert_stride elements;
+ * PR #6572, MCore-owned parameters, moe_single_grouped_weight) and `table`
+ * (per-expert allocations: a DEVICE array of E base pointers; the non-single
+ * layout exposed through descriptor tables) is non-NULL.  For the shared
+ * expert E == 1 and expert_stride is ignored. */
+typedef struct {
+  const void* base;
+  int64_t expert_stride;     /* elements between experts when `base` is used                */
+  const void* const* table;  /* device array of E pointers, or NULL                         */
+  int64_t ld;                /* elements between rows                                       */
+} moe_mat;
+
+/* A weight operand: logical shape [rows][cols] per expert.  `row_offset`
+ * selects the first row inside the storage, so gate (row_offset 0) and up
+ * (row_offset I) may alias one combined FC1 tensor [2I][H] (Megatron Core
+ * API docs, mok.runtime, _gate_up_weight_arguments: gate/up are zero-copy row
+ * views of the combined FC1; logical gate/up offsets inside one payload).
+ *
+ * BF16: `data` only.
+ * MXFP8 (routed only): `data` is the E4M3 payload with blocks of 32 along
+ * cols and `scale` its E8M0 bytes [rows][cols/32]; `col_data` is the
+ * columnwise payload (same [rows][cols] shape and layout, blocks of 32 along
+ * rows) and `col_scale` its E8M0 bytes [rows/32][cols] (PR #8210, review
+ * thread on the MXFP8 scale conversion: column scale shape (rows // 32,
+ * columns)).  The forward reads the rowwise copy, the backward's data
+ * gradient the columnwise copy; `row_offset` must then be a multiple of 32. */
+typedef struct {
+  int32_t dtype;             /* moe_dtype                                                   */
+  int64_t rows, cols;        /* logical per-expert shape                                    */
+  int64_t row_offset;        /* first logical row inside the storage                        */
+  moe_mat data, scale, col_data, col_scale;
+} moe_weight;
+
+/* The six weights in the runtime's argument order (Megatron Core API docs,
+ * mok.runtime, _MoKWeightArguments): shared gate [I][H], shared up [I][H],
+ * shared down [H][I], routed gate [E][I][H], routed up [E][I][H], routed
+ * down [E][H][I].  Shared weights must be BF16 (PR #6572, Supported
+ * configurations: shared expert parameters must remain BF16). */
+typedef struct {
+  moe_weight shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
+} moe_weights;
+
+/* An FP32 main_grad buffer [rows][cols] per expert, same addressing as moe_mat. */
+typedef struct {
+  float* base;
+  int64_t expert_stride;
+  float* const* table;       /* device array of E pointers, or NULL                         */
+  int64_t ld;
+  int64_t row_offset;
+} moe_grad;
+
+/* main_grad buffers in the same six-buffer order (Megatron Core API docs,
+ * mok.runtime, _gate_up_main_grad_arguments).  The backward accumulates
+ * (+=) in FP32 into all six (PR #6572, Design > Gradient accumulation;
+ * PR #8210, review thread on the wgrad accumulation precision: FP32
+ * accumulator, FP32 main_grad stays FP32 through the reduction-store). */
+typedef struct {
+  moe_grad shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
+} moe_main_grads;
+
+/* Byte offsets of the integer routing state inside `saved` (for tests and
+ * callers that want the compacted routing).  All arrays are int32 unless
+ * stated.  Offsets are relative, so `saved` may be copied elsewhere. */
+typedef struct {
+  size_t top_experts;     /* int32 [T][K], -1 for a missing route                            */
+  size_t router_weights;  /* float [T][K], probs gathered at top_experts, 0 at -1            */
+  size_t counts;          /* int32 [E]                                                       */
+  size_t offsets;         /* int32 [E+1], exclusive prefix sum of counts                     */
+  size_t slot_of;         /* int32 [T][K], slot of route (t,k) in expert-major order, -1 pad */
+  size_t slot_token;      /* int32 [T*K], t*K+k of the route at each slot (first S valid)    */
+  size_t status_word;     /* int32, 0 or MOE_ERR_ROUTE_OVERFLOW                              */
+} moe_saved_layout;
+
+/* Bytes of the forward->backward context for this problem (0 on invalid input). */
+size_t moe_saved_bytes(const moe_problem* p);
+
+/* Workspace bytes for moe_forward (for_backward = 0) or moe_backward (1). */
+size_t moe_workspace_bytes(const moe_problem* p, int for_backward);
+
+/* Fills `layout` with the offsets of the routing state inside `saved`. */
+moe_status moe_saved_view(const moe_problem* p, moe_saved_layout* layout);
+
+/* Forward.
+ *  hidden       bf16  [T][H]  (device)
+ *  probs        float [T][E]  read only where routing_map is non-zero
+ *  routing_map  uint8 [T][E]  0/1; at most K non-zero per row.  Converted to a
+ *               fixed-width [T][K] table of ascending expert IDs with -1 for a
+ *               missing route and the gathered probabilities (PR #6572, Design >
+ *               Authoritative routing maps)
+ *  out          bf16  [T][H]  overwritten:
+ *               out[t] = shared(x_t) + sum_k w_tk * expert_{e_tk}(x_t)
+ *  saved        moe_saved_bytes(p) bytes, written; pass it to moe_backward
+ *  workspace    moe_workspace_bytes(p, 0) bytes of scratch
+ */
+moe_status moe_forward(const moe_problem* p, const void* hidden, const float* probs,
+                       const uint8_t* routing_map, const moe_weights* w, void* out,
+                       void* saved, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of sum(grad_out * out).
+ *  grad_out     bf16  [T][H]
+ *  hidden       the same bf16 [T][H] tensor given to moe_forward
+ *  saved        the context moe_forward wrote (unchanged since)
+ *  grad_hidden  bf16  [T][H]  overwritten
+ *  grad_probs   float [T][E]  overwritten in full; zero where routing_map was 0
+ *               (the router-weight gradient scattered back into the dense
+ *               probability tensor: PR #6572, Design > Authoritative routing maps)
+ *  mg           FP32 main_grad buffers, accumulated (+=)
+ *  workspace    moe_workspace_bytes(p, 1) bytes of scratch
+ */
+moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* hidden,
+                        const moe_weights* w, const void* saved, void* grad_hidden,
+                        float* grad_probs, const moe_main_grads* mg, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* A static description of a status code. */
+const char* moe_status_str(moe_status s);
+
+/* Per-kernel launch timing for measurement.  When enabled, every kernel the
+ * library launches is bracketed by HIP events on the caller's stream (the
+ * events are created by the library on first use and kept).  Read and reset
+ * with moe_kernel_timer_read, which waits for the recorded events.  The
+ * timer is process-wide and not thread-safe; it is off by default. */
+void moe_kernel_timer_enable(int on);
+/* Copies up to `cap` entries: the kernel name, the number of launches timed
+ * and their total milliseconds; returns the number of distinct kernels. */
+int moe_kernel_timer_read(const char** names, int* launches, double* total_ms, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

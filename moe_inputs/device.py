@@ -1,0 +1,147 @@
+"""Places the seeded synthetic inputs of one configuration in GPU memory and
+builds the C descriptors the library takes (caller-side plumbing: torch owns
+every buffer).  Used by the GPU tests, the benchmark and the smoke entry.
+
+Routed weights use the configuration's layout: "single" stores one grouped
+tensor per projection ([E, 2I, H] and [E, H, I]); "table" gives every expert
+its own allocations, handed over as device arrays of per-expert pointers.  In
+both, gate and up are row views of the combined FC1 (row offsets 0 and I).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_inputs as gen
+import moe_megakernel_amd as mk
+
+
+def _bf16(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def _u8(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
+    """In-place ((i mod 7) - 3) * 2^-10 over the flat index, the same exact pattern
+    as moe_inputs.main_grad_pattern, built on the device in slices."""
+    flat = t.view(-1)
+    n = flat.numel()
+    step = 1 << 26
+    for s in range(0, n, step):
+        m = min(step, n - s)
+        i = torch.arange(phase + s, phase + s + m, device=t.device, dtype=torch.int64)
+        flat[s:s + m] = ((i % 7) - 3).to(torch.float32) * (2.0 ** -10)
+
+
+class DeviceProblem:
+    def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
+                 routing=None):
+        """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
+        configuration's router output (edge cases)."""
+        self.cfg = cfg
+        self.device = device
+        T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
+        self.backward_enabled = cfg.backward if backward is None else backward
+        probs, rmap = gen.routing(cfg) if routing is None else routing
+        self.np_probs, self.np_rmap = probs, rmap
+        self.np_x = gen.hidden(cfg)
+        self.np_dy = gen.grad_out(cfg) if self.backward_enabled else None
+        self.np_s1, self.np_s2 = gen.shared_weights(cfg)
+        self.np_routed = gen.routed_all(cfg, threads=threads)
+        self.slots = int(rmap.sum())
+
+        self.x = _bf16(self.np_x, device)
+        self.probs = torch.from_numpy(probs).to(device)
+        self.rmap = torch.from_numpy(rmap).to(device)
+        self.dy = _bf16(self.np_dy, device) if self.np_dy is not None else None
+        self.s1 = _bf16(self.np_s1, device)
+        self.s2 = _bf16(self.np_s2, device)
+        self._keep = []
+        mx = cfg.routed == "mxfp8"
+        dt = mk.MOE_MXFP8_E4M3 if mx else mk.MOE_BF16
+        self.p = mk.problem(T, H, I, E, K, dt)
+
+        def routed_mat(key, rows, cols, conv, elem_cols):
+            """moe_mat for a routed tensor stored [E][rows][cols] (single) or per expert (table)."""
+            if cfg.layout == "single":
+                t = conv(np.stack([r[key] for r in self.np_routed]), device)
+                self._keep.append(t)
+                return mk.mat(base=t, expert_stride=rows * cols, ld=elem_cols), t
+            ts = [conv(r[key], device) for r in self.np_routed]
+            tab = torch.tensor([int(t.data_ptr()) for t in ts], dtype=torch.int64, device=device)
+            self._keep += ts + [tab]
+            return mk.mat(table=tab, ld=elem_cols), ts
+
+        if not mx:
+            fc1, self.fc1 = routed_mat("fc1", 2 * I, H, _bf16, H)
+            fc2, self.fc2 = routed_mat("fc2", H, I, _bf16, I)
+            rg = mk.weight(mk.MOE_BF16, I, H, fc1, row_offset=0)
+            ru = mk.weight(mk.MOE_BF16, I, H, fc1, row_offset=I)
+            rd = mk.weight(mk.MOE_BF16, H, I, fc2)
+        else:
+            fc1, _ = routed_mat("fc1", 2 * I, H, _u8, H)
+            fc1s, _ = routed_mat("fc1_s", 2 * I, H // 32, _u8, H // 32)
+            fc1c, _ = routed_mat("fc1_c", 2 * I, H, _u8, H)
+            fc1cs, _ = routed_mat("fc1_cs", 2 * I // 32, H, _u8, H)
+            fc2, _ = routed_mat("fc2", H, I, _u8, I)
+            fc2s, _ = routed_mat("fc2_s", H, I // 32, _u8, I // 32)
+            fc2c, _ = routed_mat("fc2_c", H, I, _u8, I)
+            fc2cs, _ = routed_mat("fc2_cs", H // 32, I, _u8, I)
+            rg = mk.weight(dt, I, H, fc1, 0, fc1s, fc1c, fc1cs)
+            ru = mk.weight(dt, I, H, fc1, I, fc1s, fc1c, fc1cs)
+            rd = mk.weight(dt, H, I, fc2, 0, fc2s, fc2c, fc2cs)
+        sg = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=0)
+        su = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=I)
+        sd = mk.weight(mk.MOE_BF16, H, I, mk.mat(base=self.s2, ld=I))
+        self.weights = mk.moe_weights(sg, su, sd, rg, ru, rd)
+
+        self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
+        self.layer = mk.Layer(self.p, device=device)
+        if self.backward_enabled:
+            self.dx = torch.empty(T, H, dtype=torch.bfloat16, device=device)
+            self.dprobs = torch.empty(T, E, dtype=torch.float32, device=device)
+            self.mg_s1 = torch.empty(2 * I, H, dtype=torch.float32, device=device)
+            self.mg_s2 = torch.empty(H, I, dtype=torch.float32, device=device)
+            if cfg.layout == "single":
+                self.mg_r1 = torch.empty(E, 2 * I, H, dtype=torch.float32, device=device)
+                self.mg_r2 = torch.empty(E, H, I, dtype=torch.float32, device=device)
+                g1 = dict(base=self.mg_r1, expert_stride=2 * I * H)
+                g2 = dict(base=self.mg_r2, expert_stride=H * I)
+                self.mg_r1_list = [self.mg_r1[e] for e in range(E)]
+                self.mg_r2_list = [self.mg_r2[e] for e in range(E)]
+            else:
+                self.mg_r1_list = [torch.empty(2 * I, H, dtype=torch.float32, device=device) for _ in range(E)]
+                self.mg_r2_list = [torch.empty(H, I, dtype=torch.float32, device=device) for _ in range(E)]
+                t1 = torch.tensor([int(t.data_ptr()) for t in self.mg_r1_list], dtype=torch.int64, device=device)
+                t2 = torch.tensor([int(t.data_ptr()) for t in self.mg_r2_list], dtype=torch.int64, device=device)
+                self._keep += [t1, t2]
+                g1 = dict(table=t1)
+                g2 = dict(table=t2)
+            self.reset_main_grads()
+            self.main_grads = mk.moe_main_grads(
+                mk.grad(base=self.mg_s1, ld=H, row_offset=0), mk.grad(base=self.mg_s1, ld=H, row_offset=I),
+                mk.grad(base=self.mg_s2, ld=I),
+                mk.grad(ld=H, row_offset=0, **g1), mk.grad(ld=H, row_offset=I, **g1), mk.grad(ld=I, **g2))
+
+    # ------------------------------------------------------------------
+    def reset_main_grads(self):
+        """Every main_grad buffer starts from the exact pattern (expert e's phase = e)."""
+        fill_main_grad_pattern(self.mg_s1, 0)
+        fill_main_grad_pattern(self.mg_s2, 0)
+        for e, (a, b) in enumerate(zip(self.mg_r1_list, self.mg_r2_list)):
+            fill_main_grad_pattern(a, e)
+            fill_main_grad_pattern(b, e)
+
+    def main_grad_start(self, shape, phase) -> np.ndarray:
+        n = int(np.prod(shape))
+        return gen.main_grad_pattern(n, phase).reshape(shape)
+
+    def forward(self):
+        self.layer.forward(self.x, self.probs, self.rmap, self.weights, self.out)
+        return self.out
+
+    def backward(self):
+        self.layer.backward(self.dy, self.x, self.weights, self.dx, self.dprobs, self.main_grads)

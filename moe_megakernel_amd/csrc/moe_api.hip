@@ -1,0 +1,522 @@
+// Host side of the C ABI declared in include/moe.h: argument validation, the
+// layout of the caller-owned `saved` and workspace buffers, and the launch
+// sequence on the caller's stream.  Nothing here allocates device memory or
+// synchronises with the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "common.hpp"
+#include "gemm.hpp"
+#include "routing.hpp"
+#include "rowwise.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Dims {
+  int64_t T, H, I, E, K;
+  int64_t SM;        // T*K: slot capacity of the routed buffers
+  int64_t R;         // SM + T: routed rows then shared rows
+  int64_t nchunks;
+  bool mx;
+};
+
+Dims dims_of(const moe_problem* p) {
+  Dims d;
+  d.T = p->tokens; d.H = p->hidden; d.I = p->intermediate; d.E = p->experts; d.K = p->topk;
+  d.SM = d.T * d.K;
+  d.R = d.SM + d.T;
+  d.nchunks = (d.T + kRouteChunk - 1) / kRouteChunk;
+  d.mx = p->routed_dtype == MOE_MXFP8_E4M3;
+  return d;
+}
+
+// Byte offsets inside `saved`.
+struct SavedLayout {
+  size_t top, rw, counts, offsets, slot_of, slot_token, status, slot_w, tile_prefix, chunk_base,
+      chunk_counts, chunk_status, xp, ab, h, y, total;
+};
+
+SavedLayout saved_layout(const Dims& d) {
+  SavedLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  L.top = take(4 * d.T * d.K);
+  L.rw = take(4 * d.T * d.K);
+  L.counts = take(4 * d.E);
+  L.offsets = take(4 * (d.E + 1));
+  L.slot_of = take(4 * d.T * d.K);
+  L.slot_token = take(4 * d.SM);
+  L.status = take(4);
+  L.slot_w = take(4 * d.SM);
+  L.tile_prefix = take(4 * (d.E + 2));
+  L.chunk_base = take(4 * d.nchunks * d.E);
+  L.chunk_counts = take(4 * d.nchunks * d.E);
+  L.chunk_status = take(4 * d.nchunks);
+  L.xp = take(2 * d.SM * d.H);
+  L.ab = take(2 * d.R * 2 * d.I);
+  L.h = take(2 * d.R * d.I);
+  L.y = take(2 * d.R * d.H);
+  L.total = o;
+  return L;
+}
+
+struct BwdLayout {
+  size_t dyw, dfc1, dxp, total;
+};
+
+BwdLayout bwd_layout(const Dims& d) {
+  BwdLayout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  L.dyw = take(2 * d.SM * d.H);
+  L.dfc1 = take(2 * d.R * 2 * d.I);
+  L.dxp = take(2 * d.R * d.H);
+  L.total = o;
+  return L;
+}
+
+size_t fwd_workspace(const Dims&) { return kAlign; }
+
+// ---------------------------------------------------------------- validation
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status check_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->tokens < 0 || p->hidden <= 0 || p->intermediate <= 0) return MOE_ERR_SHAPE;
+  if (p->hidden % 128 || p->intermediate % 128) return MOE_ERR_SHAPE;
+  if (p->experts < 1 || p->experts > kMaxExperts) return MOE_ERR_SHAPE;
+  if (p->topk < 1 || p->topk > kMaxTopk || p->topk > p->experts) return MOE_ERR_SHAPE;
+  if (p->tokens * (int64_t)p->topk > (int64_t)1 << 30) return MOE_ERR_SHAPE;
+  if (p->hidden > (1 << 20) || p->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
+  if (!(p->flags & MOE_FLAG_HAS_SHARED)) return MOE_ERR_UNSUPPORTED;
+  if (p->swiglu_limit != 0.0f) return MOE_ERR_UNSUPPORTED;
+  if (p->routed_dtype != MOE_BF16 && p->routed_dtype != MOE_MXFP8_E4M3) return MOE_ERR_DTYPE;
+  if (p->routed_dtype == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;  // not built yet
+  return MOE_OK;
+}
+
+moe_status check_mat(const moe_mat& m, int64_t cols, bool routed, int elem_bytes) {
+  const bool hb = m.base != nullptr, ht = m.table != nullptr;
+  if (!hb && !ht) return MOE_ERR_NULL;
+  if (hb && ht) return MOE_ERR_LAYOUT;
+  if (!routed && ht) return MOE_ERR_LAYOUT;
+  if (m.ld < cols) return MOE_ERR_LAYOUT;
+  if ((m.ld * elem_bytes) % 16) return MOE_ERR_LAYOUT;
+  if (hb && !aligned16(m.base)) return MOE_ERR_LAYOUT;
+  if (hb && routed && (m.expert_stride < 0 || (m.expert_stride * elem_bytes) % 16)) return MOE_ERR_LAYOUT;
+  return MOE_OK;
+}
+
+moe_status check_weight(const moe_weight& w, int64_t rows, int64_t cols, bool routed, int32_t dtype) {
+  if (w.dtype != dtype) return MOE_ERR_DTYPE;
+  if (w.rows != rows || w.cols != cols) return MOE_ERR_SHAPE;
+  if (w.row_offset < 0) return MOE_ERR_LAYOUT;
+  return check_mat(w.data, cols, routed, 2);
+}
+
+moe_status check_weights(const moe_problem* p, const moe_weights* w) {
+  if (!w) return MOE_ERR_NULL;
+  const int64_t H = p->hidden, I = p->intermediate;
+  moe_status s;
+  // shared expert parameters must be BF16
+  if ((s = check_weight(w->shared_gate, I, H, false, MOE_BF16)) != MOE_OK) return s;
+  if ((s = check_weight(w->shared_up, I, H, false, MOE_BF16)) != MOE_OK) return s;
+  if ((s = check_weight(w->shared_down, H, I, false, MOE_BF16)) != MOE_OK) return s;
+  if ((s = check_weight(w->routed_gate, I, H, true, p->routed_dtype)) != MOE_OK) return s;
+  if ((s = check_weight(w->routed_up, I, H, true, p->routed_dtype)) != MOE_OK) return s;
+  if ((s = check_weight(w->routed_down, H, I, true, p->routed_dtype)) != MOE_OK) return s;
+  return MOE_OK;
+}
+
+moe_status check_grad(const moe_grad& g, int64_t cols, bool routed) {
+  const bool hb = g.base != nullptr, ht = g.table != nullptr;
+  if (!hb && !ht) return MOE_ERR_NULL;
+  if (hb && ht) return MOE_ERR_LAYOUT;
+  if (!routed && ht) return MOE_ERR_LAYOUT;
+  if (g.ld < cols || g.row_offset < 0) return MOE_ERR_LAYOUT;
+  return MOE_OK;
+}
+
+moe_status check_grads(const moe_problem* p, const moe_main_grads* g) {
+  if (!g) return MOE_ERR_NULL;
+  const int64_t H = p->hidden, I = p->intermediate;
+  moe_status s;
+  if ((s = check_grad(g->shared_gate, H, false)) != MOE_OK) return s;
+  if ((s = check_grad(g->shared_up, H, false)) != MOE_OK) return s;
+  if ((s = check_grad(g->shared_down, I, false)) != MOE_OK) return s;
+  if ((s = check_grad(g->routed_gate, H, true)) != MOE_OK) return s;
+  if ((s = check_grad(g->routed_up, H, true)) != MOE_OK) return s;
+  if ((s = check_grad(g->routed_down, I, true)) != MOE_OK) return s;
+  return MOE_OK;
+}
+
+MatRef matref(const moe_weight& w, const moe_mat& m, int elem_bytes) {
+  MatRef r;
+  r.base = static_cast<const uint8_t*>(m.base);
+  r.table = reinterpret_cast<const uint8_t* const*>(m.table);
+  r.estride_bytes = m.expert_stride * elem_bytes;
+  r.ld_bytes = m.ld * elem_bytes;
+  r.row_offset = w.row_offset;
+  return r;
+}
+
+GradRef gradref(const moe_grad& g) {
+  GradRef r;
+  r.base = g.base;
+  r.table = g.table;
+  r.estride = g.expert_stride;
+  r.ld = g.ld;
+  r.row_offset = g.row_offset;
+  return r;
+}
+
+// ---------------------------------------------------------------- kernel timer
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct Timer {
+  bool on = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::string> names;
+  std::vector<int> counts;
+  std::vector<double> ms;
+  std::mutex mu;
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Timer g_timer;
+
+template <class F>
+moe_status launch(const char* name, hipStream_t st, F&& f) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_timer.on) {
+    a = g_timer.get();
+    b = g_timer.get();
+    if (a) (void)hipEventRecord(a, st);
+  }
+  f();
+  const hipError_t err = hipGetLastError();
+  if (g_timer.on && a && b) {
+    (void)hipEventRecord(b, st);
+    g_timer.pending.push_back({name, a, b});
+  }
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+#define MOE_TRY(x)                        \
+  do {                                    \
+    const moe_status _s = (x);            \
+    if (_s != MOE_OK) return _s;          \
+  } while (0)
+
+int64_t max_mtiles(const Dims& d) {
+  return (d.SM + gemm::BM - 1) / gemm::BM + d.E + (d.T + gemm::BM - 1) / gemm::BM;
+}
+unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
+
+}  // namespace
+
+// ================================================================== C ABI
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or not a supported multiple";
+    case MOE_ERR_DTYPE: return "unsupported element type";
+    case MOE_ERR_LAYOUT: return "inconsistent layout (strides, alignment, base/table)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "saved or workspace buffer missing or too small";
+    case MOE_ERR_ROUTE_OVERFLOW: return "a routing-map row has more than topk routes";
+    case MOE_ERR_HIP: return "a HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t moe_saved_bytes(const moe_problem* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return saved_layout(dims_of(p)).total;
+}
+
+size_t moe_workspace_bytes(const moe_problem* p, int for_backward) {
+  if (check_problem(p) != MOE_OK) return 0;
+  const Dims d = dims_of(p);
+  return for_backward ? bwd_layout(d).total : fwd_workspace(d);
+}
+
+moe_status moe_saved_view(const moe_problem* p, moe_saved_layout* out) {
+  MOE_TRY(check_problem(p));
+  if (!out) return MOE_ERR_NULL;
+  const SavedLayout L = saved_layout(dims_of(p));
+  out->top_experts = L.top;
+  out->router_weights = L.rw;
+  out->counts = L.counts;
+  out->offsets = L.offsets;
+  out->slot_of = L.slot_of;
+  out->slot_token = L.slot_token;
+  out->status_word = L.status;
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_problem* p, const void* hidden, const float* probs,
+                       const uint8_t* routing_map, const moe_weights* w, void* out, void* saved,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_problem(p));
+  MOE_TRY(check_weights(p, w));
+  const Dims d = dims_of(p);
+  if (d.T > 0 && (!hidden || !probs || !routing_map || !out)) return MOE_ERR_NULL;
+  if (!saved) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < fwd_workspace(d) || !workspace) return MOE_ERR_WORKSPACE;
+  if ((hidden && !aligned16(hidden)) || (out && !aligned16(out)) || !aligned16(saved))
+    return MOE_ERR_LAYOUT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(d);
+  uint8_t* S = static_cast<uint8_t*>(saved);
+  auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(S + off); };
+  auto F32 = [&](size_t off) { return reinterpret_cast<float*>(S + off); };
+  auto U16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(S + off); };
+
+  const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
+  const int nch = (int)d.nchunks;
+
+  // F1 compaction, F2 histogram + scan + stable rank
+  MOE_TRY(launch("route_compact", st, [&] {
+    if (nch > 0)
+      hipLaunchKernelGGL(k_route_compact, dim3(nch), dim3(256), 0, st, routing_map, probs, T, E, K,
+                         I32(L.top), F32(L.rw), I32(L.chunk_counts), I32(L.chunk_status));
+  }));
+  MOE_TRY(launch("route_scan", st, [&] {
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, st, I32(L.chunk_counts), nch, E, T, 1,
+                       gemm::BM, I32(L.chunk_base), I32(L.counts), I32(L.offsets), I32(L.tile_prefix),
+                       I32(L.chunk_status), I32(L.status));
+  }));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(launch("route_rank", st, [&] {
+    hipLaunchKernelGGL(k_route_rank, dim3(nch), dim3(256), 0, st, I32(L.top), F32(L.rw), T, E, K,
+                       I32(L.chunk_base), I32(L.offsets), I32(L.slot_of), I32(L.slot_token), F32(L.slot_w));
+  }));
+  // F3 dispatch gather
+  MOE_TRY(launch("gather_x", st, [&] {
+    hipLaunchKernelGGL(k_gather_rows, dim3(T), dim3(kRowThreads), 0, st,
+                       static_cast<const uint16_t*>(hidden), H, K, I32(L.slot_of), U16(L.xp));
+  }));
+
+  gemm::TokArgs ta;
+  ta.counts = I32(L.counts);
+  ta.offsets = I32(L.offsets);
+  ta.tile_prefix = I32(L.tile_prefix);
+  ta.T = T; ta.E = E; ta.groups = E + 1;
+  ta.shared_row0 = d.SM;
+  const int64_t mt = max_mtiles(d);
+
+  // F4 + F6: routed and shared FC1 with the SwiGLU epilogue, one launch
+  gemm::Fc1Args a1;
+  a1.t = ta;
+  a1.xp = U16(L.xp);
+  a1.x = static_cast<const uint16_t*>(hidden);
+  a1.wg = matref(w->routed_gate, w->routed_gate.data, 2);
+  a1.wu = matref(w->routed_up, w->routed_up.data, 2);
+  a1.sg = matref(w->shared_gate, w->shared_gate.data, 2);
+  a1.su = matref(w->shared_up, w->shared_up.data, 2);
+  a1.ab = U16(L.ab);
+  a1.h = U16(L.h);
+  a1.H = H; a1.I = I;
+  MOE_TRY(launch("fc1_swiglu", st, [&] {
+    hipLaunchKernelGGL(gemm::k_fc1_swiglu, dim3(grid8(mt * (I / 64))), dim3(gemm::NT), 0, st, a1);
+  }));
+
+  // F5 + F6: routed and shared FC2 -> y (unweighted)
+  gemm::PlainArgs a2;
+  a2.t = ta;
+  a2.a_r = U16(L.h);
+  a2.a_s = U16(L.h);
+  a2.a_s_row0 = d.SM;
+  a2.w0 = matref(w->routed_down, w->routed_down.data, 2);
+  a2.w1 = a2.w0;
+  a2.s0 = matref(w->shared_down, w->shared_down.data, 2);
+  a2.s1 = a2.s0;
+  a2.ksplit = I;
+  a2.c = U16(L.y);
+  a2.N = H; a2.K = I;
+  MOE_TRY(launch("fc2", st, [&] {
+    hipLaunchKernelGGL(gemm::k_gemm_plain<true>, dim3(grid8(mt * (H / gemm::BN))), dim3(gemm::NT), 0, st, a2);
+  }));
+
+  // F7 combine
+  MOE_TRY(launch("combine", st, [&] {
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kRowThreads), 0, st, U16(L.y), d.SM, H, K,
+                       I32(L.slot_of), F32(L.rw), static_cast<uint16_t*>(out));
+  }));
+  return MOE_OK;
+}
+
+moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* hidden,
+                        const moe_weights* w, const void* saved, void* grad_hidden, float* grad_probs,
+                        const moe_main_grads* mg, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_problem(p));
+  MOE_TRY(check_weights(p, w));
+  MOE_TRY(check_grads(p, mg));
+  const Dims d = dims_of(p);
+  if (d.T > 0 && (!grad_out || !hidden || !grad_hidden || !grad_probs)) return MOE_ERR_NULL;
+  if (!saved) return MOE_ERR_WORKSPACE;
+  const BwdLayout B = bwd_layout(d);
+  if (!workspace || workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
+  if ((grad_out && !aligned16(grad_out)) || (hidden && !aligned16(hidden)) ||
+      (grad_hidden && !aligned16(grad_hidden)) || !aligned16(saved) || !aligned16(workspace))
+    return MOE_ERR_LAYOUT;
+  if (d.T == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SavedLayout L = saved_layout(d);
+  const uint8_t* S = static_cast<const uint8_t*>(saved);
+  uint8_t* W = static_cast<uint8_t*>(workspace);
+  auto I32 = [&](size_t off) { return reinterpret_cast<const int32_t*>(S + off); };
+  auto F32 = [&](size_t off) { return reinterpret_cast<const float*>(S + off); };
+  auto U16 = [&](size_t off) { return reinterpret_cast<const uint16_t*>(S + off); };
+  auto WU16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(W + off); };
+  const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
+  const uint16_t* dy = static_cast<const uint16_t*>(grad_out);
+  const uint16_t* x = static_cast<const uint16_t*>(hidden);
+
+  // B1 weighted dy gather + B8 router-probability gradient (dense row, zeros off the map)
+  MOE_TRY(launch("gather_dy_dprob", st, [&] {
+    hipLaunchKernelGGL(k_gather_dy_dprob, dim3(T), dim3(kRowThreads), 0, st, dy, U16(L.y), H, E, K,
+                       I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs);
+  }));
+
+  gemm::TokArgs ta;
+  ta.counts = I32(L.counts);
+  ta.offsets = I32(L.offsets);
+  ta.tile_prefix = I32(L.tile_prefix);
+  ta.T = T; ta.E = E; ta.groups = E + 1;
+  ta.shared_row0 = d.SM;
+  const int64_t mt = max_mtiles(d);
+
+  // B2 (+B6): FC2 data gradient with the SwiGLU backward epilogue -> dfc1
+  gemm::DgradSwigluArgs a3;
+  a3.t = ta;
+  a3.a_r = WU16(B.dyw);
+  a3.a_s = dy;
+  a3.wd = matref(w->routed_down, w->routed_down.data, 2);
+  a3.sd = matref(w->shared_down, w->shared_down.data, 2);
+  a3.ab = U16(L.ab);
+  a3.dfc1 = WU16(B.dfc1);
+  a3.H = H; a3.I = I;
+  MOE_TRY(launch("dgrad_fc2_swiglu", st, [&] {
+    hipLaunchKernelGGL(gemm::k_dgrad_swiglu, dim3(grid8(mt * (I / gemm::BN))), dim3(gemm::NT), 0, st, a3);
+  }));
+
+  // B3 (+B6): FC1 data gradient -> dxp (routed rows) and the shared rows
+  gemm::PlainArgs a4;
+  a4.t = ta;
+  a4.a_r = WU16(B.dfc1);
+  a4.a_s = WU16(B.dfc1);
+  a4.a_s_row0 = d.SM;
+  a4.w0 = matref(w->routed_gate, w->routed_gate.data, 2);
+  a4.w1 = matref(w->routed_up, w->routed_up.data, 2);
+  a4.s0 = matref(w->shared_gate, w->shared_gate.data, 2);
+  a4.s1 = matref(w->shared_up, w->shared_up.data, 2);
+  a4.ksplit = I;
+  a4.c = WU16(B.dxp);
+  a4.N = H; a4.K = 2 * I;
+  MOE_TRY(launch("dgrad_fc1", st, [&] {
+    hipLaunchKernelGGL(gemm::k_gemm_plain<false>, dim3(grid8(mt * (H / gemm::BN))), dim3(gemm::NT), 0, st, a4);
+  }));
+
+  // B7 dx combine
+  MOE_TRY(launch("dx_combine", st, [&] {
+    hipLaunchKernelGGL(k_dx_combine, dim3(T), dim3(kRowThreads), 0, st, WU16(B.dxp), d.SM, H, K,
+                       I32(L.slot_of), static_cast<uint16_t*>(grad_hidden));
+  }));
+
+  // B4 (+B6): FC2 weight gradient: main_grad_down[e] += dyw^T h
+  gemm::WgradArgs a5;
+  a5.counts = I32(L.counts);
+  a5.offsets = I32(L.offsets);
+  a5.T = T; a5.E = E; a5.has_shared = 1;
+  a5.a_r = WU16(B.dyw); a5.a_s = dy; a5.lda = H; a5.a_s_row0 = 0;
+  a5.b_r = U16(L.h); a5.b_s = U16(L.h); a5.ldb = I; a5.b_s_row0 = d.SM;
+  a5.g_lo = gradref(mg->routed_down); a5.g_hi = a5.g_lo;
+  a5.s_lo = gradref(mg->shared_down); a5.s_hi = a5.s_lo;
+  a5.msplit = H;
+  a5.M = H; a5.N = I;
+  {
+    const int per = (H / gemm::BM) * (I / gemm::BN);
+    MOE_TRY(launch("wgrad_fc2", st, [&] {
+      hipLaunchKernelGGL(gemm::k_wgrad, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a5);
+    }));
+  }
+
+  // B5 (+B6): FC1 weight gradient: main_grad_{gate,up}[e] += dfc1^T xp
+  gemm::WgradArgs a6;
+  a6.counts = I32(L.counts);
+  a6.offsets = I32(L.offsets);
+  a6.T = T; a6.E = E; a6.has_shared = 1;
+  a6.a_r = WU16(B.dfc1); a6.a_s = WU16(B.dfc1); a6.lda = 2 * (int64_t)I; a6.a_s_row0 = d.SM;
+  a6.b_r = U16(L.xp); a6.b_s = x; a6.ldb = H; a6.b_s_row0 = 0;
+  a6.g_lo = gradref(mg->routed_gate); a6.g_hi = gradref(mg->routed_up);
+  a6.s_lo = gradref(mg->shared_gate); a6.s_hi = gradref(mg->shared_up);
+  a6.msplit = I;
+  a6.M = 2 * I; a6.N = H;
+  {
+    const int per = (2 * I / gemm::BM) * (H / gemm::BN);
+    MOE_TRY(launch("wgrad_fc1", st, [&] {
+      hipLaunchKernelGGL(gemm::k_wgrad, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a6);
+    }));
+  }
+  return MOE_OK;
+}
+
+void moe_kernel_timer_enable(int on) { g_timer.on = on != 0; }
+
+int moe_kernel_timer_read(const char** names, int* launches, double* total_ms, int cap) {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  for (auto& tl : g_timer.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(tl.b) == hipSuccess && hipEventElapsedTime(&ms, tl.a, tl.b) == hipSuccess) {
+      size_t i = 0;
+      for (; i < g_timer.names.size(); ++i)
+        if (g_timer.names[i] == tl.name) break;
+      if (i == g_timer.names.size()) {
+        g_timer.names.emplace_back(tl.name);
+        g_timer.counts.push_back(0);
+        g_timer.ms.push_back(0.0);
+      }
+      g_timer.counts[i] += 1;
+      g_timer.ms[i] += ms;
+    }
+    g_timer.pool.push_back(tl.a);
+    g_timer.pool.push_back(tl.b);
+  }
+  g_timer.pending.clear();
+  const int n = (int)g_timer.names.size();
+  for (int i = 0; i < n && i < cap; ++i) {
+    if (names) names[i] = g_timer.names[i].c_str();
+    if (launches) launches[i] = g_timer.counts[i];
+    if (total_ms) total_ms[i] = g_timer.ms[i];
+  }
+  for (int i = 0; i < n; ++i) {   // the totals restart; the name strings stay valid until the next read
+    g_timer.counts[i] = 0;
+    g_timer.ms[i] = 0.0;
+  }
+  return n;
+}
+
+}  // extern "C"

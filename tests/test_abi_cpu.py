@@ -1,0 +1,140 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every symbol
+include/moe.h declares, and rejects invalid arguments on the host before any
+HIP call (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_megakernel_amd as mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("moe_forward", "moe_backward", "moe_saved_bytes", "moe_workspace_bytes",
+              "moe_saved_view", "moe_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mk.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", mk.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(moe_\w+)", out))
+    for n in _declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(mk.EXPORTED) == set(_declared_functions())
+
+
+def test_status_strings():
+    for s in range(9):
+        assert mk.moe_status_str(s) and mk.moe_status_str(s) != "unknown status"
+    assert mk.moe_status_str(99) == "unknown status"
+
+
+def _ok_problem(**kw):
+    d = dict(tokens=64, hidden=256, inter=128, experts=8, topk=2)
+    d.update(kw)
+    return mk.problem(d["tokens"], d["hidden"], d["inter"], d["experts"], d["topk"])
+
+
+def test_sizes_are_positive_and_monotone():
+    small = mk.moe_saved_bytes(_ok_problem())
+    big = mk.moe_saved_bytes(_ok_problem(tokens=128))
+    assert 0 < small < big
+    assert mk.moe_workspace_bytes(_ok_problem(), True) > 0
+    assert mk.moe_workspace_bytes(_ok_problem(), False) > 0
+    lay = mk.moe_saved_view(_ok_problem())
+    offs = [lay.top_experts, lay.router_weights, lay.counts, lay.offsets, lay.slot_of,
+            lay.slot_token, lay.status_word]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=100), mk.MOE_ERR_SHAPE),
+    (dict(inter=64), mk.MOE_ERR_SHAPE),
+    (dict(experts=0), mk.MOE_ERR_SHAPE),
+    (dict(experts=256), mk.MOE_ERR_SHAPE),
+    (dict(topk=9), mk.MOE_ERR_SHAPE),
+    (dict(topk=3, experts=2), mk.MOE_ERR_SHAPE),
+    (dict(tokens=-1), mk.MOE_ERR_SHAPE),
+])
+def test_invalid_problem_is_rejected(kw, status):
+    p = _ok_problem(**kw)
+    assert mk.moe_saved_bytes(p) == 0
+    st = mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0)
+    assert st == status
+
+
+def test_unsupported_configurations_are_rejected():
+    p = _ok_problem()
+    p.flags = 0                                   # no shared expert
+    assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_UNSUPPORTED
+    p = _ok_problem()
+    p.swiglu_limit = 7.0                          # clamp not supported
+    assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_UNSUPPORTED
+    p = _ok_problem()
+    p.routed_dtype = 2                            # fp32 routed weights
+    assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_DTYPE
+
+
+def _fake_weights(p, shared_dtype=mk.MOE_BF16, routed_table=False, ld_pad=0):
+    """Descriptors over fake (never dereferenced) 256-byte aligned addresses."""
+    H, I = p.hidden, p.intermediate
+    base = 1 << 40
+    m = lambda ld: mk.moe_mat(base, 0, 0, ld + ld_pad)
+    r = lambda ld: mk.moe_mat(0 if routed_table else base, H * I * 2, base if routed_table else 0, ld + ld_pad)
+    z = mk.moe_mat(0, 0, 0, 0)
+    W = mk.moe_weight
+    return mk.moe_weights(W(shared_dtype, I, H, 0, m(H), z, z, z), W(shared_dtype, I, H, I, m(H), z, z, z),
+                          W(shared_dtype, H, I, 0, m(I), z, z, z), W(p.routed_dtype, I, H, 0, r(H), z, z, z),
+                          W(p.routed_dtype, I, H, I, r(H), z, z, z), W(p.routed_dtype, H, I, 0, r(I), z, z, z))
+
+
+def test_weight_validation_errors():
+    p = _ok_problem()
+    args = (1 << 41, 1 << 41, 1 << 41)
+    # shared expert must be BF16
+    w = _fake_weights(p, shared_dtype=mk.MOE_MXFP8_E4M3)
+    assert mk.moe_forward(p, *args, w, 1 << 41, 0, 0, 0, 0) == mk.MOE_ERR_DTYPE
+    # both base and table set
+    w = _fake_weights(p)
+    w.routed_gate.data.table = 1 << 40
+    assert mk.moe_forward(p, *args, w, 1 << 41, 0, 0, 0, 0) == mk.MOE_ERR_LAYOUT
+    # wrong logical shape
+    w = _fake_weights(p)
+    w.routed_down.rows = 128
+    assert mk.moe_forward(p, *args, w, 1 << 41, 0, 0, 0, 0) == mk.MOE_ERR_SHAPE
+    # row stride not a multiple of 16 bytes
+    w = _fake_weights(p, ld_pad=3)
+    assert mk.moe_forward(p, *args, w, 1 << 41, 0, 0, 0, 0) == mk.MOE_ERR_LAYOUT
+    # missing saved buffer / workspace
+    w = _fake_weights(p)
+    assert mk.moe_forward(p, *args, w, 1 << 41, 0, 1 << 41, 1 << 20, 0) == mk.MOE_ERR_WORKSPACE
+    assert mk.moe_forward(p, *args, w, 1 << 41, 1 << 41, 1 << 41, 0, 0) == mk.MOE_ERR_WORKSPACE
+    # missing input pointer
+    assert mk.moe_forward(p, 0, 1 << 41, 1 << 41, w, 1 << 41, 1 << 41, 1 << 41, 1 << 20, 0) == mk.MOE_ERR_NULL
+
+
+def test_backward_validation_errors():
+    p = _ok_problem()
+    w = _fake_weights(p)
+    g = mk.moe_main_grads()
+    a = 1 << 41
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 1 << 30, 0) == mk.MOE_ERR_NULL
+    H, I = p.hidden, p.intermediate
+    G = lambda ld, ro=0: mk.moe_grad(a, 0, 0, ld, ro)
+    g = mk.moe_main_grads(G(H), G(H, I), G(I), G(H), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 16, 0) == mk.MOE_ERR_WORKSPACE
+    g.shared_down.ld = I - 1
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 1 << 30, 0) == mk.MOE_ERR_LAYOUT

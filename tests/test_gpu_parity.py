@@ -1,0 +1,184 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on
+the same seeded bits.  Integer routing state is compared bit-exact; floating
+results by max|gpu - ref| / max|ref| <= 2e-2 (BF16 routed experts)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as gen
+from oracle import moe_oracle as O
+from tests.gpu_parity_util import (BF16_TOL, check_routing_state, oracle_weights, rel_err,
+                                   sample_tokens, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _dp(cfg, **kw):
+    from moe_inputs.device import DeviceProblem
+    print(f"[case] {cfg.name} T={cfg.tokens} H={cfg.hidden} E={cfg.experts} K={cfg.topk} I={cfg.inter}",
+          flush=True)
+    return DeviceProblem(cfg, **kw)
+
+
+def _check_forward(dp, W, tokens=None, tol=BF16_TOL):
+    cfg = dp.cfg
+    ref = O.moe_forward(dp.np_x, dp.np_probs, dp.np_rmap, cfg.topk, W, tokens=tokens)
+    got = to_f64(dp.out) if tokens is None else to_f64(dp.out[torch.as_tensor(tokens, device=dp.out.device)])
+    err = rel_err(got, ref)
+    assert np.isfinite(got).all()
+    assert err <= tol, f"out rel err {err:.3e}"
+    return err
+
+
+def _check_backward(dp, W, tokens=None, experts=None, tol=BF16_TOL):
+    cfg = dp.cfg
+    I = cfg.inter
+    g = O.moe_backward(dp.np_dy, dp.np_x, dp.np_probs, dp.np_rmap, cfg.topk, W, tokens=tokens,
+                       experts=experts)
+    sel = slice(None) if tokens is None else torch.as_tensor(tokens, device=dp.dx.device)
+    dx = to_f64(dp.dx[sel])
+    dpr = dp.dprobs[sel].cpu().numpy().astype(np.float64)
+    errs = {"dx": rel_err(dx, g["dx"]), "dprobs": rel_err(dpr, g["dprobs"])}
+    rm = dp.np_rmap if tokens is None else dp.np_rmap[tokens]
+    assert np.all(dpr[rm == 0] == 0), "dprobs must be exactly zero off the routing map"
+    for e in (range(cfg.experts) if experts is None else experts):
+        d1 = to_f64(dp.mg_r1_list[e]) - dp.main_grad_start((2 * I, cfg.hidden), e)
+        d2 = to_f64(dp.mg_r2_list[e]) - dp.main_grad_start((cfg.hidden, I), e)
+        dg, du, dd = g["dW"][e]
+        errs[f"gate{e}"] = rel_err(d1[:I], dg) if np.abs(dg).max() > 0 else float(np.abs(d1[:I]).max())
+        errs[f"up{e}"] = rel_err(d1[I:], du) if np.abs(du).max() > 0 else float(np.abs(d1[I:]).max())
+        errs[f"down{e}"] = rel_err(d2, dd) if np.abs(dd).max() > 0 else float(np.abs(d2).max())
+    s1 = to_f64(dp.mg_s1) - dp.main_grad_start((2 * I, cfg.hidden), 0)
+    s2 = to_f64(dp.mg_s2) - dp.main_grad_start((cfg.hidden, I), 0)
+    dg, du, dd = g["dW"]["shared"]
+    errs["shared_gate"] = rel_err(s1[:I], dg)
+    errs["shared_up"] = rel_err(s1[I:], du)
+    errs["shared_down"] = rel_err(s2, dd)
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    assert not bad, f"over tolerance {tol}: {bad}"
+    return errs
+
+
+def test_config0_forward_matches_oracle(gpu_lib):
+    dp = _dp(gen.config(0))
+    dp.forward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    _check_forward(dp, oracle_weights(dp))
+
+
+def test_config1_forward_backward_matches_oracle(gpu_lib):
+    dp = _dp(gen.config(1))
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    _check_forward(dp, W)
+    _check_backward(dp, W)
+
+
+@pytest.mark.parametrize("shape", [
+    (300, 256, 5, 3, 128),     # ragged token count, uneven experts, short rows
+    (1, 128, 3, 2, 128),       # a single token
+    (777, 384, 13, 4, 256),    # several tiles and ragged tails everywhere
+])
+def test_ragged_shapes_forward_backward(gpu_lib, shape):
+    T, H, E, K, I = shape
+    cfg = gen.custom(T, H, E, K, I, short_frac=0.1, short_max=max(1, K - 1), idx=200 + T)
+    dp = _dp(cfg)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    _check_forward(dp, W)
+    _check_backward(dp, W)
+
+
+def test_empty_routing_map_gives_shared_expert_only(gpu_lib):
+    cfg = gen.custom(200, 256, 6, 2, 128, idx=301)
+    probs = np.zeros((200, 6), np.float32)
+    rmap = np.zeros((200, 6), np.uint8)
+    dp = _dp(cfg, routing=(probs, rmap))
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    st = dp.layer.routing_state()
+    assert int(st["counts"].sum()) == 0 and bool((st["top_experts"] == -1).all())
+    W = oracle_weights(dp)
+    _check_forward(dp, W)
+    errs = _check_backward(dp, W)
+    assert all(errs[f"down{e}"] == 0 for e in range(6))     # routed main_grad untouched
+    assert float(dp.dprobs.abs().max()) == 0.0
+
+
+def test_all_tokens_on_one_expert(gpu_lib):
+    # one expert receives every token (many row tiles), the others none
+    T, E = 640, 4
+    cfg = gen.custom(T, 256, E, 1, 128, idx=302)
+    rmap = np.zeros((T, E), np.uint8)
+    rmap[:, 2] = 1
+    probs = rmap.astype(np.float32) * np.float32(0.75)
+    dp = _dp(cfg, routing=(probs, rmap))
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    _check_forward(dp, W)
+    _check_backward(dp, W)
+
+
+def test_route_overflow_sets_status_word(gpu_lib):
+    T, E, K = 64, 8, 2
+    cfg = gen.custom(T, 128, E, K, 128, idx=303)
+    probs, rmap = gen.routing(cfg)
+    rmap[5, :] = 1                        # 8 routes on a top-2 row: invalid input
+    probs[5, :] = 0.125
+    dp = _dp(cfg, routing=(probs, rmap), backward=False)
+    dp.forward()
+    torch.cuda.synchronize()
+    assert int(dp.layer.routing_state()["status_word"][0]) == 7   # MOE_ERR_ROUTE_OVERFLOW
+
+
+def test_forward_backward_bitwise_deterministic(gpu_lib):
+    dp = _dp(gen.config(1))
+    outs = []
+    for _ in range(2):
+        dp.reset_main_grads()
+        dp.forward()
+        dp.backward()
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (dp.out, dp.dx, dp.dprobs, dp.mg_r1, dp.mg_r2, dp.mg_s1, dp.mg_s2)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a, b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_zero_tokens_is_a_no_op(gpu_lib):
+    import moe_megakernel_amd as mk
+    p = mk.problem(0, 256, 128, 4, 2)
+    layer = mk.Layer(p)
+    dp = _dp(gen.custom(4, 256, 4, 2, 128, idx=304), backward=True)
+    empty = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+    layer.forward(empty, torch.empty(0, 4, device="cuda"), torch.empty(0, 4, dtype=torch.uint8, device="cuda"),
+                  dp.weights, empty)
+    layer.backward(empty, empty, dp.weights, empty, torch.empty(0, 4, device="cuda"), dp.main_grads)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("idx", [2])
+def test_full_size_bf16_config_sampled(gpu_lib, idx):
+    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024: the benchmark's launch
+    configuration.  Routing state in full; out / dx / dprobs on sampled tokens; main_grad
+    deltas of sampled experts and of the shared expert."""
+    cfg = gen.config(idx)
+    dp = _dp(cfg)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    top, offsets = check_routing_state(dp)
+    W = oracle_weights(dp)
+    toks = sample_tokens(cfg.tokens, 48, seed=idx)
+    _check_forward(dp, W, tokens=toks)
+    _check_backward(dp, W, tokens=toks, experts=[0, 37, cfg.experts - 1])
