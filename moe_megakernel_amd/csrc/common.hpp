@@ -30,6 +30,46 @@ __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 
 
 __device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
 
+// ----------------------------------------------------------------------------- MXFP8
+// Block exponent of a 32-element MX block: the smallest e in [-127, 127] with
+// amax * 2^-e <= 448 (E4M3's largest finite magnitude), taken from the float's bits:
+// amax = (1 + m / 2^23) 2^(b - 127) gives e = b - 135, plus one when the significand
+// exceeds 1.75 (= 448 / 2^8).  amax == 0 (or subnormal) -> -127.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int b = (int)((u >> 23) & 0xffu);
+  if (b == 0) return -127;
+  const int e = b - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four floats (already scaled into [-448, 448]) -> four E4M3 codes (round to nearest even).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// 32 floats of one block -> 32 E4M3 codes (two uint4) and the E8M0 scale byte.
+__device__ __forceinline__ uint32_t mx_quantize32(const float (&v)[32], uint4& q0, uint4& q1) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mx_block_exp(amax);
+  const float inv = ldexpf(1.0f, -e);
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = pack_e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+  q0 = make_uint4(w[0], w[1], w[2], w[3]);
+  q1 = make_uint4(w[4], w[5], w[6], w[7]);
+  return (uint32_t)(e + 127);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
+  f[0] = lo_bf(v.x); f[1] = hi_bf(v.x); f[2] = lo_bf(v.y); f[3] = hi_bf(v.y);
+  f[4] = lo_bf(v.z); f[5] = hi_bf(v.z); f[6] = lo_bf(v.w); f[7] = hi_bf(v.w);
+}
+
 // Per-expert matrix addressing: single grouped tensor or a device pointer table.
 struct MatRef {
   const uint8_t* base;     // bytes
@@ -41,6 +81,12 @@ struct MatRef {
     const uint8_t* b = table ? table[e] : base + (int64_t)e * estride_bytes;
     return b + (row_offset + r) * ld_bytes;
   }
+};
+
+// MXFP8 operand of a routed weight: payload rows and their E8M0 scale rows.
+struct MxRef {
+  MatRef data;    // E4M3 payload (bytes)
+  MatRef scale;   // E8M0 bytes; for a columnwise copy its rows are blocks of 32 weight rows
 };
 
 struct GradRef {

@@ -72,7 +72,7 @@ SavedLayout saved_layout(const Dims& d) {
 }
 
 struct BwdLayout {
-  size_t dyw, dfc1, dxp, total;
+  size_t dyw, dfc1, dxp, dyq, dys, dfq, dfs, total;
 };
 
 BwdLayout bwd_layout(const Dims& d) {
@@ -82,11 +82,37 @@ BwdLayout bwd_layout(const Dims& d) {
   L.dyw = take(2 * d.SM * d.H);
   L.dfc1 = take(2 * d.R * 2 * d.I);
   L.dxp = take(2 * d.R * d.H);
+  L.dyq = L.dys = L.dfq = L.dfs = 0;
+  if (d.mx) {   // MXFP8 codes + scales of the routed data-gradient GEMM inputs
+    L.dyq = take(d.SM * d.H);
+    L.dys = take(d.SM * d.H / 32);
+    L.dfq = take(d.SM * 2 * d.I);
+    L.dfs = take(d.SM * 2 * d.I / 32);
+  }
   L.total = o;
   return L;
 }
 
-size_t fwd_workspace(const Dims&) { return kAlign; }
+// Forward workspace: MXFP8 codes + scales of the routed FC1 input (x) and FC2 input (h).
+struct FwdLayout {
+  size_t xq, xs, hq, hs, total;
+};
+
+FwdLayout fwd_layout(const Dims& d) {
+  FwdLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  if (d.mx) {
+    L.xq = take(d.SM * d.H);
+    L.xs = take(d.SM * d.H / 32);
+    L.hq = take(d.SM * d.I);
+    L.hs = take(d.SM * d.I / 32);
+  }
+  L.total = o > kAlign ? o : kAlign;
+  return L;
+}
+
+size_t fwd_workspace(const Dims& d) { return fwd_layout(d).total; }
 
 // ---------------------------------------------------------------- validation
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -102,7 +128,6 @@ moe_status check_problem(const moe_problem* p) {
   if (!(p->flags & MOE_FLAG_HAS_SHARED)) return MOE_ERR_UNSUPPORTED;
   if (p->swiglu_limit != 0.0f) return MOE_ERR_UNSUPPORTED;
   if (p->routed_dtype != MOE_BF16 && p->routed_dtype != MOE_MXFP8_E4M3) return MOE_ERR_DTYPE;
-  if (p->routed_dtype == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;  // not built yet
   return MOE_OK;
 }
 
@@ -118,14 +143,37 @@ moe_status check_mat(const moe_mat& m, int64_t cols, bool routed, int elem_bytes
   return MOE_OK;
 }
 
-moe_status check_weight(const moe_weight& w, int64_t rows, int64_t cols, bool routed, int32_t dtype) {
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// E8M0 scale matrices are read 4 bytes at a time: row stride and base 4-byte aligned.
+moe_status check_scale(const moe_mat& m, int64_t cols) {
+  const bool hb = m.base != nullptr, ht = m.table != nullptr;
+  if (!hb && !ht) return MOE_ERR_NULL;
+  if (hb && ht) return MOE_ERR_LAYOUT;
+  if (m.ld < cols || m.ld % 4) return MOE_ERR_LAYOUT;
+  if (hb && (!aligned4(m.base) || m.expert_stride < 0 || m.expert_stride % 4)) return MOE_ERR_LAYOUT;
+  return MOE_OK;
+}
+
+// need_col: the columnwise MXFP8 copy is required (backward).
+moe_status check_weight(const moe_weight& w, int64_t rows, int64_t cols, bool routed, int32_t dtype,
+                        bool need_col = false) {
   if (w.dtype != dtype) return MOE_ERR_DTYPE;
   if (w.rows != rows || w.cols != cols) return MOE_ERR_SHAPE;
   if (w.row_offset < 0) return MOE_ERR_LAYOUT;
-  return check_mat(w.data, cols, routed, 2);
+  if (dtype != MOE_MXFP8_E4M3) return check_mat(w.data, cols, routed, 2);
+  moe_status s;
+  if (w.row_offset % 32 || rows % 32 || cols % 32) return MOE_ERR_LAYOUT;
+  if ((s = check_mat(w.data, cols, routed, 1)) != MOE_OK) return s;
+  if ((s = check_scale(w.scale, cols / 32)) != MOE_OK) return s;
+  if (need_col) {
+    if ((s = check_mat(w.col_data, cols, routed, 1)) != MOE_OK) return s;
+    if ((s = check_scale(w.col_scale, cols)) != MOE_OK) return s;
+  }
+  return MOE_OK;
 }
 
-moe_status check_weights(const moe_problem* p, const moe_weights* w) {
+moe_status check_weights(const moe_problem* p, const moe_weights* w, bool backward = false) {
   if (!w) return MOE_ERR_NULL;
   const int64_t H = p->hidden, I = p->intermediate;
   moe_status s;
@@ -133,9 +181,9 @@ moe_status check_weights(const moe_problem* p, const moe_weights* w) {
   if ((s = check_weight(w->shared_gate, I, H, false, MOE_BF16)) != MOE_OK) return s;
   if ((s = check_weight(w->shared_up, I, H, false, MOE_BF16)) != MOE_OK) return s;
   if ((s = check_weight(w->shared_down, H, I, false, MOE_BF16)) != MOE_OK) return s;
-  if ((s = check_weight(w->routed_gate, I, H, true, p->routed_dtype)) != MOE_OK) return s;
-  if ((s = check_weight(w->routed_up, I, H, true, p->routed_dtype)) != MOE_OK) return s;
-  if ((s = check_weight(w->routed_down, H, I, true, p->routed_dtype)) != MOE_OK) return s;
+  if ((s = check_weight(w->routed_gate, I, H, true, p->routed_dtype, backward)) != MOE_OK) return s;
+  if ((s = check_weight(w->routed_up, I, H, true, p->routed_dtype, backward)) != MOE_OK) return s;
+  if ((s = check_weight(w->routed_down, H, I, true, p->routed_dtype, backward)) != MOE_OK) return s;
   return MOE_OK;
 }
 
@@ -168,6 +216,21 @@ MatRef matref(const moe_weight& w, const moe_mat& m, int elem_bytes) {
   r.estride_bytes = m.expert_stride * elem_bytes;
   r.ld_bytes = m.ld * elem_bytes;
   r.row_offset = w.row_offset;
+  return r;
+}
+
+// MXFP8 weight views: the rowwise copy (forward) or the columnwise copy (data gradient);
+// a columnwise scale row covers 32 weight rows, so its row offset is row_offset / 32.
+MxRef mxref(const moe_weight& w, bool columnwise) {
+  MxRef r;
+  if (!columnwise) {
+    r.data = matref(w, w.data, 1);
+    r.scale = matref(w, w.scale, 1);
+  } else {
+    r.data = matref(w, w.col_data, 1);
+    r.scale = matref(w, w.col_scale, 1);
+    r.scale.row_offset = w.row_offset / 32;
+  }
   return r;
 }
 
@@ -284,9 +347,12 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   const Dims d = dims_of(p);
   if (d.T > 0 && (!hidden || !probs || !routing_map || !out)) return MOE_ERR_NULL;
   if (!saved) return MOE_ERR_WORKSPACE;
-  if (workspace_bytes < fwd_workspace(d) || !workspace) return MOE_ERR_WORKSPACE;
-  if ((hidden && !aligned16(hidden)) || (out && !aligned16(out)) || !aligned16(saved))
+  const FwdLayout F = fwd_layout(d);
+  if (workspace_bytes < F.total || !workspace) return MOE_ERR_WORKSPACE;
+  if ((hidden && !aligned16(hidden)) || (out && !aligned16(out)) || !aligned16(saved) ||
+      !aligned16(workspace))
     return MOE_ERR_LAYOUT;
+  uint8_t* WS = static_cast<uint8_t*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const SavedLayout L = saved_layout(d);
   uint8_t* S = static_cast<uint8_t*>(saved);
@@ -313,10 +379,15 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
     hipLaunchKernelGGL(k_route_rank, dim3(nch), dim3(256), 0, st, I32(L.top), F32(L.rw), T, E, K,
                        I32(L.chunk_base), I32(L.offsets), I32(L.slot_of), I32(L.slot_token), F32(L.slot_w));
   }));
-  // F3 dispatch gather
+  // F3 dispatch gather (+ Q: MXFP8 codes of the routed FC1 input)
   MOE_TRY(launch("gather_x", st, [&] {
-    hipLaunchKernelGGL(k_gather_rows, dim3(T), dim3(kRowThreads), 0, st,
-                       static_cast<const uint16_t*>(hidden), H, K, I32(L.slot_of), U16(L.xp));
+    if (d.mx)
+      hipLaunchKernelGGL(k_gather_rows<true>, dim3(T), dim3(kRowThreads), 0, st,
+                         static_cast<const uint16_t*>(hidden), H, K, I32(L.slot_of), U16(L.xp), WS + F.xq, WS + F.xs);
+    else
+      hipLaunchKernelGGL(k_gather_rows<false>, dim3(T), dim3(kRowThreads), 0, st,
+                         static_cast<const uint16_t*>(hidden), H, K, I32(L.slot_of), U16(L.xp),
+                         (uint8_t*)nullptr, (uint8_t*)nullptr);
   }));
 
   gemm::TokArgs ta;
@@ -339,9 +410,24 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   a1.ab = U16(L.ab);
   a1.h = U16(L.h);
   a1.H = H; a1.I = I;
+  a1.mx = gemm::MxOperands{};
+  if (d.mx) {
+    a1.mx.aq = WS + F.xq;
+    a1.mx.as = WS + F.xs;
+    a1.mx.b0 = mxref(w->routed_gate, false);
+    a1.mx.b1 = mxref(w->routed_up, false);
+  }
   MOE_TRY(launch("fc1_swiglu", st, [&] {
-    hipLaunchKernelGGL(gemm::k_fc1_swiglu, dim3(grid8(mt * (I / 64))), dim3(gemm::NT), 0, st, a1);
+    const dim3 g(grid8(mt * (I / 64)));
+    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, g, dim3(gemm::NT), 0, st, a1);
+    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, g, dim3(gemm::NT), 0, st, a1);
   }));
+  if (d.mx) {   // Q: MXFP8 codes of the routed FC2 input h
+    MOE_TRY(launch("quantize_h", st, [&] {
+      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, U16(L.h), d.SM, I,
+                         I32(L.offsets) + E, WS + F.hq, WS + F.hs);
+    }));
+  }
 
   // F5 + F6: routed and shared FC2 -> y (unweighted)
   gemm::PlainArgs a2;
@@ -356,8 +442,17 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   a2.ksplit = I;
   a2.c = U16(L.y);
   a2.N = H; a2.K = I;
+  a2.mx = gemm::MxOperands{};
+  if (d.mx) {
+    a2.mx.aq = WS + F.hq;
+    a2.mx.as = WS + F.hs;
+    a2.mx.b0 = mxref(w->routed_down, false);
+    a2.mx.b1 = a2.mx.b0;
+  }
   MOE_TRY(launch("fc2", st, [&] {
-    hipLaunchKernelGGL(gemm::k_gemm_plain<true>, dim3(grid8(mt * (H / gemm::BN))), dim3(gemm::NT), 0, st, a2);
+    const dim3 g(grid8(mt * (H / gemm::BN)));
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<true, true>), g, dim3(gemm::NT), 0, st, a2);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<true, false>), g, dim3(gemm::NT), 0, st, a2);
   }));
 
   // F7 combine
@@ -372,7 +467,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
                         const moe_weights* w, const void* saved, void* grad_hidden, float* grad_probs,
                         const moe_main_grads* mg, void* workspace, size_t workspace_bytes, void* stream) {
   MOE_TRY(check_problem(p));
-  MOE_TRY(check_weights(p, w));
+  MOE_TRY(check_weights(p, w, true));
   MOE_TRY(check_grads(p, mg));
   const Dims d = dims_of(p);
   if (d.T > 0 && (!grad_out || !hidden || !grad_hidden || !grad_probs)) return MOE_ERR_NULL;
@@ -395,10 +490,15 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   const uint16_t* dy = static_cast<const uint16_t*>(grad_out);
   const uint16_t* x = static_cast<const uint16_t*>(hidden);
 
-  // B1 weighted dy gather + B8 router-probability gradient (dense row, zeros off the map)
+  // B1 weighted dy gather (+ Q) + B8 router-probability gradient (dense row, zeros off the map)
   MOE_TRY(launch("gather_dy_dprob", st, [&] {
-    hipLaunchKernelGGL(k_gather_dy_dprob, dim3(T), dim3(kRowThreads), 0, st, dy, U16(L.y), H, E, K,
-                       I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs);
+    if (d.mx)
+      hipLaunchKernelGGL(k_gather_dy_dprob<true>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(L.y), H, E, K,
+                         I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, W + B.dyq, W + B.dys);
+    else
+      hipLaunchKernelGGL(k_gather_dy_dprob<false>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(L.y), H, E, K,
+                         I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, (uint8_t*)nullptr,
+                         (uint8_t*)nullptr);
   }));
 
   gemm::TokArgs ta;
@@ -419,9 +519,24 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a3.ab = U16(L.ab);
   a3.dfc1 = WU16(B.dfc1);
   a3.H = H; a3.I = I;
+  a3.mx = gemm::MxOperands{};
+  if (d.mx) {
+    a3.mx.aq = W + B.dyq;
+    a3.mx.as = W + B.dys;
+    a3.mx.b0 = mxref(w->routed_down, true);
+    a3.mx.b1 = a3.mx.b0;
+  }
   MOE_TRY(launch("dgrad_fc2_swiglu", st, [&] {
-    hipLaunchKernelGGL(gemm::k_dgrad_swiglu, dim3(grid8(mt * (I / gemm::BN))), dim3(gemm::NT), 0, st, a3);
+    const dim3 g(grid8(mt * (I / gemm::BN)));
+    if (d.mx) hipLaunchKernelGGL(gemm::k_dgrad_swiglu<true>, g, dim3(gemm::NT), 0, st, a3);
+    else hipLaunchKernelGGL(gemm::k_dgrad_swiglu<false>, g, dim3(gemm::NT), 0, st, a3);
   }));
+  if (d.mx) {   // Q: MXFP8 codes of the routed FC1 data-gradient input dfc1
+    MOE_TRY(launch("quantize_dfc1", st, [&] {
+      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, WU16(B.dfc1), d.SM, 2 * I,
+                         I32(L.offsets) + E, W + B.dfq, W + B.dfs);
+    }));
+  }
 
   // B3 (+B6): FC1 data gradient -> dxp (routed rows) and the shared rows
   gemm::PlainArgs a4;
@@ -436,8 +551,17 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a4.ksplit = I;
   a4.c = WU16(B.dxp);
   a4.N = H; a4.K = 2 * I;
+  a4.mx = gemm::MxOperands{};
+  if (d.mx) {
+    a4.mx.aq = W + B.dfq;
+    a4.mx.as = W + B.dfs;
+    a4.mx.b0 = mxref(w->routed_gate, true);
+    a4.mx.b1 = mxref(w->routed_up, true);
+  }
   MOE_TRY(launch("dgrad_fc1", st, [&] {
-    hipLaunchKernelGGL(gemm::k_gemm_plain<false>, dim3(grid8(mt * (H / gemm::BN))), dim3(gemm::NT), 0, st, a4);
+    const dim3 g(grid8(mt * (H / gemm::BN)));
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<false, true>), g, dim3(gemm::NT), 0, st, a4);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<false, false>), g, dim3(gemm::NT), 0, st, a4);
   }));
 
   // B7 dx combine

@@ -16,18 +16,66 @@ __device__ __forceinline__ void load_slots(const int32_t* __restrict__ slot_of, 
 }
 
 // xp[slot_of[t,k]] = x[t] for every valid route (dispatch into expert-contiguous rows).
+// With Q, the row is also quantised to MXFP8 along H (one E8M0 scale per 32 elements)
+// into xq / xs, the A operand of the scaled-FP8 FC1.  One thread per 32-element block.
+template <bool Q>
 __global__ __launch_bounds__(kRowThreads) void k_gather_rows(
     const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ slot_of,
-    uint16_t* __restrict__ xp) {
+    uint16_t* __restrict__ xp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
   const int t = blockIdx.x;
   int s[kMaxTopk];
   load_slots(slot_of, t, K, s);
   const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
-  for (int c = threadIdx.x; c < H / 8; c += kRowThreads) {
-    const uint4 v = src[c];
+  for (int c = threadIdx.x; c < H / 32; c += kRowThreads) {
+    uint4 v[4];
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k)
-      if (s[k] >= 0) reinterpret_cast<uint4*>(xp + (int64_t)s[k] * H)[c] = v;
+    for (int q = 0; q < 4; ++q) v[q] = src[4 * c + q];
+    uint4 q0, q1;
+    uint32_t sc = 0;
+    if constexpr (Q) {
+      float f[32];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) unpack_bf16x8(v[q], f + 8 * q);
+      sc = mx_quantize32(f, q0, q1);
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) {
+      if (s[k] < 0) continue;
+      uint4* dst = reinterpret_cast<uint4*>(xp + (int64_t)s[k] * H) + 4 * c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = v[q];
+      if constexpr (Q) {
+        uint4* dq = reinterpret_cast<uint4*>(xq + (int64_t)s[k] * H) + 2 * c;
+        dq[0] = q0;
+        dq[1] = q1;
+        xs[(int64_t)s[k] * (H / 32) + c] = (uint8_t)sc;
+      }
+    }
+  }
+}
+
+// MXFP8 quantisation of bf16 rows along their length: payload [rows][cols] E4M3 and
+// scales [rows][cols/32] E8M0.  Rows at or beyond *row_limit (when given) are skipped:
+// the routed buffers hold offsets[E] valid rows.  One thread per 32-element block.
+__global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
+    const uint16_t* __restrict__ in, int64_t rows, int cols, const int32_t* __restrict__ row_limit,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  const int64_t nb = (int64_t)cols / 32;
+  const int64_t lim = row_limit ? (int64_t)*row_limit : rows;
+  const int64_t total = (lim < rows ? lim : rows) * nb;
+  for (int64_t b = (int64_t)blockIdx.x * kRowThreads + threadIdx.x; b < total;
+       b += (int64_t)gridDim.x * kRowThreads) {
+    const int64_t r = b / nb, c = b - r * nb;
+    const uint4* src = reinterpret_cast<const uint4*>(in + r * cols) + 4 * c;
+    float f[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) unpack_bf16x8(src[i], f + 8 * i);
+    uint4 q0, q1;
+    const uint32_t s = mx_quantize32(f, q0, q1);
+    uint4* dq = reinterpret_cast<uint4*>(q + r * cols) + 2 * c;
+    dq[0] = q0;
+    dq[1] = q1;
+    sc[r * nb + c] = (uint8_t)s;
   }
 }
 
@@ -67,11 +115,15 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
 // routed expert's upstream gradient), and the router-probability gradient
 // dprobs[t, e_tk] = dy[t] . y[slot] (y is the unweighted expert output), written
 // into the dense [T][E] row with zeros off the map.  The dot products are
-// reduced per thread in a fixed order and then by a fixed LDS tree.
+// reduced per thread in a fixed order and then by a fixed LDS tree.  With Q,
+// w_tk * dy[t] is also quantised to MXFP8 along H (the A operand of the
+// scaled-FP8 data-gradient GEMM).  One thread per 32-element block.
+template <bool Q>
 __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y, int H, int E, int K,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ top,
-    const float* __restrict__ rw, uint16_t* __restrict__ dyw, float* __restrict__ dprobs) {
+    const float* __restrict__ rw, uint16_t* __restrict__ dyw, float* __restrict__ dprobs,
+    uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys) {
   __shared__ float red[kMaxTopk][kRowThreads];
   const int t = blockIdx.x;
   int s[kMaxTopk];
@@ -83,24 +135,39 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     part[k] = 0.0f;
   }
   const uint4* src = reinterpret_cast<const uint4*>(dy + (int64_t)t * H);
-  for (int c = threadIdx.x; c < H / 8; c += kRowThreads) {
-    const uint4 v = src[c];
-    const float g[8] = {lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y),
-                        lo_bf(v.z), hi_bf(v.z), lo_bf(v.w), hi_bf(v.w)};
+  for (int c = threadIdx.x; c < H / 32; c += kRowThreads) {
+    float g[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) unpack_bf16x8(src[4 * c + q], g + 8 * q);
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) {
       if (s[k] < 0) continue;
-      const uint4 r = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H)[c];
-      const float yv[8] = {lo_bf(r.x), hi_bf(r.x), lo_bf(r.y), hi_bf(r.y),
-                           lo_bf(r.z), hi_bf(r.z), lo_bf(r.w), hi_bf(r.w)};
+      const uint4* yr = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H) + 4 * c;
       float d = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) d += g[q] * yv[q];
+      for (int q = 0; q < 4; ++q) {
+        float yv[8];
+        unpack_bf16x8(yr[q], yv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d += g[8 * q + i] * yv[i];
+      }
       part[k] += d;
-      uint4 o;
-      o.x = pack_bf2(w[k] * g[0], w[k] * g[1]); o.y = pack_bf2(w[k] * g[2], w[k] * g[3]);
-      o.z = pack_bf2(w[k] * g[4], w[k] * g[5]); o.w = pack_bf2(w[k] * g[6], w[k] * g[7]);
-      reinterpret_cast<uint4*>(dyw + (int64_t)s[k] * H)[c] = o;
+      float wg[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) wg[i] = w[k] * g[i];
+      uint4* dst = reinterpret_cast<uint4*>(dyw + (int64_t)s[k] * H) + 4 * c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dst[q] = make_uint4(pack_bf2(wg[8 * q], wg[8 * q + 1]), pack_bf2(wg[8 * q + 2], wg[8 * q + 3]),
+                            pack_bf2(wg[8 * q + 4], wg[8 * q + 5]), pack_bf2(wg[8 * q + 6], wg[8 * q + 7]));
+      if constexpr (Q) {
+        uint4 q0, q1;
+        const uint32_t sc = mx_quantize32(wg, q0, q1);
+        uint4* dq = reinterpret_cast<uint4*>(dyq + (int64_t)s[k] * H) + 2 * c;
+        dq[0] = q0;
+        dq[1] = q1;
+        dys[(int64_t)s[k] * (H / 32) + c] = (uint8_t)sc;
+      }
     }
   }
 #pragma unroll

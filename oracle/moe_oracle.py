@@ -80,11 +80,17 @@ def e8m0_decode(codes: np.ndarray) -> np.ndarray:
     return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
 
 
+_E4M3_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))   # the closed form above, tabulated
+_E8M0_TABLE = e8m0_decode(np.arange(256, dtype=np.uint8))
+
+
 def mxfp8_decode_rowwise(payload: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """W[r, c] = E4M3(payload[r, c]) * E8M0(scale[r, c // 32])."""
     R, C = payload.shape
     assert scale.shape == (R, C // 32), (scale.shape, (R, C // 32))
-    return e4m3_decode(payload) * np.repeat(e8m0_decode(scale), 32, axis=1)
+    out = _E4M3_TABLE[payload].reshape(R, C // 32, 32)
+    out *= _E8M0_TABLE[scale][:, :, None]
+    return out.reshape(R, C)
 
 
 def mxfp8_decode_colwise(payload: np.ndarray, colscale: np.ndarray) -> np.ndarray:
@@ -93,7 +99,9 @@ def mxfp8_decode_colwise(payload: np.ndarray, colscale: np.ndarray) -> np.ndarra
     on the per-expert MXFP8 scale conversion)."""
     R, C = payload.shape
     assert colscale.shape == (R // 32, C), (colscale.shape, (R // 32, C))
-    return e4m3_decode(payload) * np.repeat(e8m0_decode(colscale), 32, axis=0)
+    out = _E4M3_TABLE[payload].reshape(R // 32, 32, C)
+    out *= _E8M0_TABLE[colscale][:, None, :]
+    return out.reshape(R, C)
 
 
 # ----------------------------------------------------------------------------------

@@ -7,8 +7,8 @@ import torch
 
 import moe_inputs as gen
 from oracle import moe_oracle as O
-from tests.gpu_parity_util import (BF16_TOL, check_routing_state, oracle_weights, rel_err,
-                                   sample_tokens, to_f64)
+from tests.gpu_parity_util import (BF16_TOL, MXFP8_TOL, check_routing_state, oracle_weights,
+                                   rel_err, sample_tokens, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +25,7 @@ def _check_forward(dp, W, tokens=None, tol=BF16_TOL):
     ref = O.moe_forward(dp.np_x, dp.np_probs, dp.np_rmap, cfg.topk, W, tokens=tokens)
     got = to_f64(dp.out) if tokens is None else to_f64(dp.out[torch.as_tensor(tokens, device=dp.out.device)])
     err = rel_err(got, ref)
+    print(f"[parity] out rel err {err:.3e} (tol {tol})", flush=True)
     assert np.isfinite(got).all()
     assert err <= tol, f"out rel err {err:.3e}"
     return err
@@ -54,6 +55,9 @@ def _check_backward(dp, W, tokens=None, experts=None, tol=BF16_TOL):
     errs["shared_gate"] = rel_err(s1[:I], dg)
     errs["shared_up"] = rel_err(s1[I:], du)
     errs["shared_down"] = rel_err(s2, dd)
+    worst = max(errs, key=lambda k: errs[k])
+    print(f"[parity] dx {errs['dx']:.3e} dprobs {errs['dprobs']:.3e} worst {worst} {errs[worst]:.3e} "
+          f"(tol {tol})", flush=True)
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     assert not bad, f"over tolerance {tol}: {bad}"
     return errs
@@ -182,3 +186,44 @@ def test_full_size_bf16_config_sampled(gpu_lib, idx):
     toks = sample_tokens(cfg.tokens, 48, seed=idx)
     _check_forward(dp, W, tokens=toks)
     _check_backward(dp, W, tokens=toks, experts=[0, 37, cfg.experts - 1])
+
+
+# ----------------------------------------------------------------------------------
+# MXFP8 routed experts (E4M3 payload + E8M0 scale per 32 along K; shared stays BF16)
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("layout,shape", [
+    ("table", (300, 256, 6, 3, 128)),
+    ("single", (520, 384, 9, 2, 256)),
+])
+def test_mxfp8_forward_backward_matches_oracle(gpu_lib, layout, shape):
+    T, H, E, K, I = shape
+    cfg = gen.custom(T, H, E, K, I, routed="mxfp8", layout=layout, short_frac=0.05, short_max=max(1, K - 1),
+                     idx=400 + T)
+    dp = _dp(cfg)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    _check_forward(dp, W, tol=MXFP8_TOL)
+    _check_backward(dp, W, tol=MXFP8_TOL)
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_full_size_mxfp8_config_sampled(gpu_lib, idx):
+    """3: 4096 tokens, 96 experts, top-4, skewed softmax routing, per-expert allocations
+    through device pointer tables.  4: 8192 tokens, hidden 7168, 64 experts, top-6,
+    inter 2048, 2% of tokens with fewer than 6 routes.  Routing state in full; sampled
+    tokens and experts otherwise."""
+    cfg = gen.config(idx)
+    dp = _dp(cfg, threads=16)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    toks = sample_tokens(cfg.tokens, 24, seed=idx)
+    _check_forward(dp, W, tokens=toks, tol=MXFP8_TOL)
+    counts = np.asarray(dp.layer.routing_state()["counts"].cpu())
+    busiest = int(np.argmax(counts))
+    _check_backward(dp, W, tokens=toks, experts=sorted({0, busiest, cfg.experts - 1}), tol=MXFP8_TOL)
