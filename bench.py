@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (2: 4096-token BF16 layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy before the steps (a known-size "
+                         "reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -118,6 +121,13 @@ def main():
     dp = DeviceProblem(cfg, backward=True)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s: {cfg.name}", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         dp.forward()

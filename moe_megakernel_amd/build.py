@@ -21,9 +21,10 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile the library to `out`; `defines` are extra -D options (tile variants)."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,8 +34,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

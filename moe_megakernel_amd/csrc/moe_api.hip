@@ -451,8 +451,8 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   }
   MOE_TRY(launch("fc2", st, [&] {
     const dim3 g(grid8(mt * (H / gemm::BN)));
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<true, true>), g, dim3(gemm::NT), 0, st, a2);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<true, false>), g, dim3(gemm::NT), 0, st, a2);
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), g, dim3(gemm::NT), 0, st, a2);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), g, dim3(gemm::NT), 0, st, a2);
   }));
 
   // F7 combine
@@ -560,8 +560,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   }
   MOE_TRY(launch("dgrad_fc1", st, [&] {
     const dim3 g(grid8(mt * (H / gemm::BN)));
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<false, true>), g, dim3(gemm::NT), 0, st, a4);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<false, false>), g, dim3(gemm::NT), 0, st, a4);
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, true>), g, dim3(gemm::NT), 0, st, a4);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, false>), g, dim3(gemm::NT), 0, st, a4);
   }));
 
   // B7 dx combine
@@ -579,12 +579,12 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a5.b_r = U16(L.h); a5.b_s = U16(L.h); a5.ldb = I; a5.b_s_row0 = d.SM;
   a5.g_lo = gradref(mg->routed_down); a5.g_hi = a5.g_lo;
   a5.s_lo = gradref(mg->shared_down); a5.s_hi = a5.s_lo;
-  a5.msplit = H;
-  a5.M = H; a5.N = I;
+  a5.parts = 1; a5.mpart = H;
+  a5.N = I;
   {
-    const int per = (H / gemm::BM) * (I / gemm::BN);
+    const int per = gemm::wgrad_tiles_per_group(1, H, I);
     MOE_TRY(launch("wgrad_fc2", st, [&] {
-      hipLaunchKernelGGL(gemm::k_wgrad, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a5);
+      hipLaunchKernelGGL(gemm::k_wgrad<2>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a5);
     }));
   }
 
@@ -597,12 +597,12 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a6.b_r = U16(L.xp); a6.b_s = x; a6.ldb = H; a6.b_s_row0 = 0;
   a6.g_lo = gradref(mg->routed_gate); a6.g_hi = gradref(mg->routed_up);
   a6.s_lo = gradref(mg->shared_gate); a6.s_hi = gradref(mg->shared_up);
-  a6.msplit = I;
-  a6.M = 2 * I; a6.N = H;
+  a6.parts = 2; a6.mpart = I;
+  a6.N = H;
   {
-    const int per = (2 * I / gemm::BM) * (H / gemm::BN);
+    const int per = gemm::wgrad_tiles_per_group(2, I, H);
     MOE_TRY(launch("wgrad_fc1", st, [&] {
-      hipLaunchKernelGGL(gemm::k_wgrad, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a6);
+      hipLaunchKernelGGL(gemm::k_wgrad<1>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a6);
     }));
   }
   return MOE_OK;

@@ -39,13 +39,23 @@ __global__ __launch_bounds__(256) void k_route_compact(
       }
       ++n;
     };
-    if ((E & 3) == 0 && ((reinterpret_cast<uintptr_t>(row) & 3) == 0)) {
-      const uint32_t* r4 = reinterpret_cast<const uint32_t*>(row);
-      for (int q = 0; q < (E >> 2); ++q) {
-        uint32_t v = r4[q];
-        if (!v) continue;
-        for (int b = 0; b < 4; ++b)
-          if ((v >> (8 * b)) & 0xffu) take(4 * q + b);
+    if ((E & 15) == 0 && ((reinterpret_cast<uintptr_t>(row) & 15) == 0)) {
+      // the whole row (E <= 256 bytes) is loaded with independent 16-byte loads first
+      uint4 r16[16];
+      const uint4* src = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) r16[q] = (q < (E >> 4)) ? src[q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t w4[4] = {r16[q].x, r16[q].y, r16[q].z, r16[q].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t v = w4[d];
+          if (!v) continue;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if ((v >> (8 * b)) & 0xffu) take(16 * q + 4 * d + b);
+        }
       }
     } else {
       for (int e = 0; e < E; ++e)
