@@ -735,7 +735,14 @@ __global__ __launch_bounds__(NT, MINB_W) void k_wgrad(WgradArgs p) {
   if (kdim == 0) return;
   const int part = tile / (mtp * ntn);
   const int rem = tile - part * mtp * ntn;
-  const int m0 = (rem / ntn) * BMW, n0 = (rem % ntn) * BN;
+  // Supertile order: blocks of sm x sn tiles run consecutively, so the sm A-row slices and
+  // sn B-column slices they share are re-read from L2 while the main_grad stream flows past.
+  const int sm = (mtp % 4 == 0) ? 4 : ((mtp % 2 == 0) ? 2 : 1);
+  const int sn = (ntn % 8 == 0) ? 8 : ((ntn % 4 == 0) ? 4 : ((ntn % 2 == 0) ? 2 : 1));
+  const int sblk = rem / (sm * sn), sin = rem - sblk * sm * sn;
+  const int sbn = ntn / sn;
+  const int mt = (sblk / sbn) * sm + sin / sn, nt = (sblk % sbn) * sn + sin % sn;
+  const int m0 = mt * BMW, n0 = nt * BN;
   const int mrows = min(BMW, p.mpart - m0);
   const int64_t ar0 = shared ? p.a_s_row0 : (int64_t)p.offsets[g];
   const int64_t br0 = shared ? p.b_s_row0 : (int64_t)p.offsets[g];
