@@ -1,413 +1,465 @@
 // Grouped GEMMs of the MoE layer on gfx950 matrix cores.  One launch covers
 // every routed expert's row group plus the shared expert's group.
 //
-// Tile: TM (M) x 128 (N) per workgroup of 256 threads = 4 waves in a WM x WN
-// grid, each wave a block of MI x NJ MFMA 32x32 accumulators (fp32).  Several
-// workgroups share a CU, so one workgroup's global loads overlap another's
-// MFMAs; a wave whose rows are all past the group's last row skips its MFMAs.
+// Tile: TM (M) x TN (N) per workgroup of NWM x NWN waves, each wave a block of
+// MI x NJ MFMA 32x32 accumulators (fp32).  A wave whose rows all lie past the
+// group's last row skips its MFMAs.
 //
-// K is staged 64 bytes at a time (32 bf16 or 64 E4M3 codes) through two LDS
-// stages with 80-byte padded rows ([row][k], so every fragment read is one
-// 16-byte ds_read), with PFD register stages of global loads in flight.
-// Operands whose source is K-contiguous are copied as 16-byte chunks; operands
-// whose source is contiguous along M / N (weights in the data-gradient GEMMs,
-// activations in the weight-gradient GEMMs) are loaded as 4 x 8 (bf16) or
-// 4 x 16 (bytes) blocks and transposed in registers on the way into LDS.
+// Operand movement: every K stage (128 bytes of K per row: 64 bf16 or 128 E4M3)
+// is copied global -> LDS by the load unit itself (global_load_lds_dwordx4: one
+// wave instruction moves 64 x 16 bytes into 1 KB of LDS), so no registers hold
+// staged data and NS stages can be in flight.  LDS tiles are unpadded; 16-byte
+// chunks are XOR-swizzled by row so that both the DMA writes and the fragment
+// reads are free of bank conflicts.  An operand is stored as it lies in memory:
+//   K-contiguous ("KC", rows of a [rows][K] matrix): tile [rows][128 B],
+//       fragments read with ds_read_b128;
+//   row-contiguous ("RC", k-th row holds the tile's M / N run): tile
+//       [k][T * elem bytes], fragments read transposed with ds_read_b64_tr_b16
+//       (bf16) or ds_read_b64_tr_b8 (E4M3).
+// Row-contiguous k rows past the end of K are loaded from a zero page, so the
+// weight-gradient token tail contributes exactly zero.  With PF > 0 every wave also
+// touches each 128-byte line of the stage PF steps past the newest DMA'd one with a
+// 4-byte LDS DMA into a scratch word, pulling the lines into L2 ahead of their DMA
+// (nothing lands in registers, so a late return cannot clobber one).
 //
 // BF16: v_mfma_f32_32x32x16_bf16.  MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4
 // with one E8M0 scale per lane (row or column, 32-code K block).
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
 namespace gemm {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 
-#ifndef MOE_TILE_BM
-#define MOE_TILE_BM 128
-#endif
-#ifndef MOE_TILE_BMW
-#define MOE_TILE_BMW 128
-#endif
-#ifndef MOE_TILE_WM
-#define MOE_TILE_WM 2
-#endif
-#ifndef MOE_TILE_PFD
-#define MOE_TILE_PFD 1
-#endif
-#ifndef MOE_TILE_MINB
-#define MOE_TILE_MINB 2
-#endif
-#ifndef MOE_TILE_MINB_DG
-#define MOE_TILE_MINB_DG 3
-#endif
-#ifndef MOE_TILE_MINB_W
-#define MOE_TILE_MINB_W MOE_TILE_MINB
-#endif
-#ifndef MOE_TILE_KBYTES
-#define MOE_TILE_KBYTES 128
-#endif
-constexpr int BN = 128, NT = 256;
-constexpr int BM = MOE_TILE_BM;                 // token rows per tile (token-dim GEMMs)
-constexpr int BMW = MOE_TILE_BMW;               // weight rows per tile (weight gradients)
-constexpr int WM = MOE_TILE_WM;                 // waves along M (WN = 4 / WM along N)
-constexpr int PFD = MOE_TILE_PFD;               // register stages of prefetch
-constexpr int MINB = MOE_TILE_MINB;             // workgroups per CU the register budget targets:
-constexpr int MINB_DG = MOE_TILE_MINB_DG;       //   forward, data-gradient and weight-gradient GEMMs
-constexpr int MINB_W = MOE_TILE_MINB_W;
-constexpr int KBYTES = MOE_TILE_KBYTES;         // K bytes per stage (64 or 128)
-constexpr int ROW = KBYTES + 16;                // LDS row stride (bytes): 80 or 144
-constexpr int CPR = KBYTES / 16;                // 16-byte chunks per row per stage
-constexpr int SBK = KBYTES / 32;                // E8M0 blocks per row per MXFP8 stage
-#ifndef MOE_TILE_RK
-#define MOE_TILE_RK 4
-#endif
-constexpr int RK = MOE_TILE_RK;                 // k rows per row-contiguous bf16 block (4 or 8)
 
-template <int TM>
-struct Cfg {
-  static constexpr int WN = 4 / WM;
-  static constexpr int B_OFF = TM * ROW;                 // B tile offset inside a stage
-  static constexpr int STAGE = (TM + BN) * ROW;
-  static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int SC_B = TM * SBK;                  // scale tile: A [TM][SBK] then B [128][SBK]
-  static constexpr int SC_STAGE = (TM + BN) * SBK;
-  static constexpr int WMR = TM / WM;                    // rows per wave
-  static constexpr int WNC = BN / WN;                    // columns per wave
+template <int TM_, int TN_, int NWM_, int NWN_, int NS_, int MINB_, int PF_ = 0, int KB_ = 128>
+struct Tile {
+  static constexpr int TM = TM_, TN = TN_, NWM = NWM_, NWN = NWN_, NS = NS_, MINB = MINB_;
+  static constexpr int PF = PF_;   // L2 prefetch distance in stages past the newest DMA stage (0: off)
+  static constexpr int KB = KB_;   // K bytes per row per stage: 128, or 64 (BF16 only)
+  static constexpr int NW = NWM * NWN, NTH = 64 * NW;
+  static constexpr int WMR = TM / NWM, WNC = TN / NWN;   // rows / columns per wave
   static constexpr int MI = WMR / 32, NJ = WNC / 32;     // 32x32 blocks per wave
-  static constexpr int AKC = TM * CPR / 256;             // A K-contiguous chunks per thread
-  static constexpr int BKC = BN * CPR / 256;             // B K-contiguous chunks per thread
-  static constexpr int KG16 = KBYTES / 2 / RK;           // RK-element k groups per stage (bf16)
-  static constexpr int NA_RC = KG16 * (TM / 8);          // A row-contiguous blocks (bf16)
-  static constexpr int NB_RC = KG16 * (BN / 8);          // B row-contiguous blocks (bf16)
-  static constexpr int KG8 = KBYTES / 4;                 // 4-code k groups per stage (bytes)
-  static constexpr int NB_RC8 = KG8 * (BN / 16);         // B row-contiguous blocks (bytes)
+  static constexpr int A_BYTES = TM * KB, B_BYTES = TN * KB, STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_DMA = A_BYTES / 1024 / NW;      // 1 KB DMA instructions per wave per stage
+  static constexpr int B_DMA = B_BYTES / 1024 / NW;
+  // MXFP8 scales of one stage (4 blocks of 32 codes): A [TM][4], B [TN][4] or [4][TN]
+  static constexpr int SC_A = TM * 4, SC_B = TN * 4, SC_STAGE = SC_A + SC_B;
+  static constexpr int SC_REAL = SC_STAGE / 256;         // 256-byte dword DMA instructions
+  static constexpr int SC_DMA = (SC_REAL + NW - 1) / NW; // per wave (the extra ones are dummies)
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int SC_LDS = NS * SC_STAGE + 256;     // + the dummies' target
+  // L2 prefetch: one dword per 128-byte line of a stage (TM + TN lines), PF_N per wave
+  static constexpr int PF_N = PF ? (TM + TN + NTH - 1) / NTH : 0;
+  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
+  static_assert(WMR % 32 == 0 && WNC % 32 == 0 && NS >= 2, "tile shape");
+  static_assert(KB == 128 || (KB == 64 && PF == 0), "64-byte stages take no L2 prefetch");
 };
 
-template <int TM>
-using Acc = f32x16_t[Cfg<TM>::MI][Cfg<TM>::NJ];
+template <class TL>
+using Acc = f32x16_t[TL::MI][TL::NJ];
 
-// 4 x 4 byte transpose: b_j = [a0.byte j, a1.byte j, a2.byte j, a3.byte j].
-__device__ __forceinline__ void tr4x4_bytes(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                            uint32_t& b0, uint32_t& b1, uint32_t& b2, uint32_t& b3) {
-  const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a00 a10 a01 a11
-  const uint32_t t1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a02 a12 a03 a13
-  const uint32_t t2 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);   // a20 a30 a21 a31
-  const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);   // a22 a32 a23 a33
-  b0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  b1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  b2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  b3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+// Zero page: the source of row-contiguous k rows past the end of K.
+__device__ __align__(16) uint4 g_zero_page[64];
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
 
-// RK rows (k) x 8 bf16 (r) -> LDS rows r0 + i, 2 RK bytes (RK k values) at byte offset kb.
-template <int NK>
-__device__ __forceinline__ void store_tr_bf16(uint8_t* tile, int r0, int kb, const u32x4_t (&v)[NK]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int wi = i >> 1, sh = (i & 1) * 16;
-    uint32_t o[NK / 2];
-#pragma unroll
-    for (int q = 0; q < NK / 2; ++q)
-      o[q] = ((v[2 * q][wi] >> sh) & 0xffffu) | (((v[2 * q + 1][wi] >> sh) & 0xffffu) << 16);
-    if constexpr (NK == 8)
-      *reinterpret_cast<u32x4_t*>(tile + (r0 + i) * ROW + kb) = u32x4_t{o[0], o[1], o[2], o[3]};
-    else
-      *reinterpret_cast<uint2*>(tile + (r0 + i) * ROW + kb) = make_uint2(o[0], o[1]);
-  }
+// LDS DMA: lane l's 16 (or 4) bytes at gptr land at LDS byte m0v + 16 l (or 4 l); m0v
+// is the same for the whole wave.  The asm keeps the compiler from inserting its own
+// full vmcnt waits before every LDS read; the pipeline below waits on exact counts.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t m0v) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(m0v);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(m)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t m0v) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(m0v);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(m)
+               : "memory", "m0");
 }
 
-// 4 rows (k) x 16 codes (r) -> LDS rows r0 + 0..15, 4 bytes (4 k) at byte offset kb.
-__device__ __forceinline__ void store_tr_u8(uint8_t* tile, int r0, int kb, const u32x4_t (&v)[4]) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t b[4];
-    tr4x4_bytes(v[0][w], v[1][w], v[2][w], v[3][w], b[0], b[1], b[2], b[3]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(tile + (r0 + 4 * w + j) * ROW + kb) = b[j];
-  }
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// ---------------------------------------------------------------------------------
-// Operand descriptions handed to the tile loop.
-//  KC (K-contiguous): fa / fb(r) -> pointer to tile row r at K = 0 (callers clamp rows
-//                     past the end to a valid row; result rows they feed are never stored).
-//  RC (row-contiguous): fa / fb(k) -> pointer to element (k, tile row 0); only called for
-//                     k < kdim (for bf16), rows k >= kdim are zero-filled (the token tail
-//                     of the weight gradients).
-//  Scales (MXFP8): fas / fbs(r) -> E8M0 row of tile row r (K-contiguous operand), or for a
-//                  row-contiguous B: fbs(kb) -> E8M0 byte of (K block kb, tile column 0).
-// ---------------------------------------------------------------------------------
+// Swizzles (16-byte chunk index XOR a function of the row), chosen so that the 16 or
+// 32 lanes one LDS cycle serves touch 64 distinct banks:
+//  KC, rows of KB = 128 or 64 bytes: ds_read_b128 of 16 consecutive rows, same chunk.
+template <int KB>
+__device__ __forceinline__ int swz_kc(int r) { return KB == 128 ? (r >> 1) & 7 : (r >> 2) & 3; }
+//  RC bf16 (rows of 256 or 512 bytes): tr16 reads 4 k rows x 4 chunks.
+__device__ __forceinline__ int swz_rc16(int k) { return (k & 3) << 2; }
+//  RC E4M3 (rows of RB = 128 or 256 bytes): tr8 reads 8 k rows x 2 chunks.
+template <int RB>
+__device__ __forceinline__ int swz_rc8(int k) { return RB == 128 ? ((k >> 1) & 3) << 1 : (k & 7) << 1; }
+
 enum Mode { KC = 0, RC = 1 };
-
-// Global loads of one K stage held in registers until they are written to LDS.
-// Thread mapping.  KC: chunk t % CPR of rows t / CPR + (256 / CPR) i.  RC bf16: block
-// (kg = t % KG16, rg = t / KG16) of 4 k x 8 rows, on threads [0, NA_RC) for A and
-// [256 - NB_RC, 256) for B.  RC bytes (B): block (kg = u % KG8, rg = u / KG8) of 4 k x 16.
-template <int TM>
-struct Staged {
-  u32x4_t ka[Cfg<TM>::AKC];  // A KC chunks
-  u32x4_t kb[Cfg<TM>::BKC];  // B KC chunks
-  u32x4_t ra[RK];            // A RC block (RK k rows)
-  u32x4_t rb[RK];            // B RC block (RK k rows of bf16; 4 of codes)
-  uint32_t sa, sb;           // MXFP8 scale bytes (SBK per row; B RC: 4 columns of one block)
-};
-
-// acc[i][j] (wave rows wm*WMR + 32 i, columns wn*WNC + 32 j) += A[TM x K] * B[128 x K]^T.
-// arows: for a row-contiguous A, the tile rows that exist (a multiple of 8); the 8-row
-// blocks past it are zero-filled instead of loaded.
-template <int TM, int AM, int BMODE, bool FP8, class FA, class FB, class FAS, class FBS>
-__device__ __forceinline__ void tile_mma(Acc<TM>& acc, int kdim, const FA& fa, const FB& fb, const FAS& fas,
-                                         const FBS& fbs, uint8_t* lds, uint8_t* sc, bool wave_active,
-                                         int arows = TM) {
-  using C = Cfg<TM>;
-  static_assert(!(FP8 && AM == RC), "MXFP8 A operands are K-contiguous");
-  static_assert(TM == 128 || TM == 256, "tile rows");
-  static_assert(AM == KC || C::NA_RC <= NT, "row-contiguous A blocks must fit the workgroup");
-  static_assert(BMODE == KC || (FP8 ? C::NB_RC8 : C::NB_RC) <= NT, "row-contiguous B blocks must fit");
-  const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6, wm = w / C::WN, wn = w % C::WN;
-  constexpr int EB = FP8 ? 1 : 2;                 // bytes per element
-  constexpr int KST = KBYTES / EB;                // K elements per stage
-
-  constexpr int RSTEP = NT / CPR;                 // rows between a thread's KC chunks
-  const int kc = t % CPR, kr = t / CPR;           // KC chunk and first row
-  const uint8_t* rpa[C::AKC];
-  const uint8_t* rpb[C::BKC];
-  const uint8_t* spa = nullptr;      // A scale row of tile row t (t < TM)
-  const uint8_t* spb = nullptr;      // B scale row of tile row t (t < 128, KC B)
-#pragma unroll
-  for (int i = 0; i < C::AKC; ++i) rpa[i] = nullptr;
-#pragma unroll
-  for (int i = 0; i < C::BKC; ++i) rpb[i] = nullptr;
-  if constexpr (AM == KC) {
-#pragma unroll
-    for (int i = 0; i < C::AKC; ++i) rpa[i] = reinterpret_cast<const uint8_t*>(fa(kr + RSTEP * i));
-    if constexpr (FP8) spa = (t < TM) ? fas(t) : nullptr;
-  }
-  if constexpr (BMODE == KC) {
-#pragma unroll
-    for (int i = 0; i < C::BKC; ++i) rpb[i] = reinterpret_cast<const uint8_t*>(fb(kr + RSTEP * i));
-    if constexpr (FP8) spb = (t < BN) ? fbs(t) : nullptr;
-  }
-  // A RC blocks on threads [0, NA_RC); blocks past arows are zero-filled.
-  const int akg = t % C::KG16, arg = t / C::KG16;
-  const bool rcA = (AM == RC) && t < C::NA_RC && arg * 8 < arows;
-  const bool rcAz = (AM == RC) && t < C::NA_RC && !rcA;
-  // B RC blocks on the last NB_RC (bf16) or NB_RC8 (bytes) threads.
-  const int u = t - (NT - (FP8 ? C::NB_RC8 : C::NB_RC));
-  const bool rcB = (BMODE == RC) && u >= 0;
-  const int bkg = FP8 ? u % C::KG8 : u % C::KG16, brg = FP8 ? u / C::KG8 : u / C::KG16;
-
-  auto gload = [&](int k0, Staged<TM>& g) __attribute__((always_inline)) {   // k0 in elements
-    const int kbyte = k0 * EB;
-    if constexpr (AM == KC) {
-#pragma unroll
-      for (int i = 0; i < C::AKC; ++i) g.ka[i] = *reinterpret_cast<const u32x4_t*>(rpa[i] + kbyte + kc * 16);
-      if constexpr (FP8) {
-        if (t < TM) {
-          if constexpr (SBK == 2) g.sa = *reinterpret_cast<const uint16_t*>(spa + k0 / 32);
-          else g.sa = *reinterpret_cast<const uint32_t*>(spa + k0 / 32);
-        }
-      }
-    } else {
-      if (rcA) {
-        const int kb = k0 + akg * RK, m8 = arg * 8;
-#pragma unroll
-        for (int q = 0; q < RK; ++q)
-          g.ra[q] = (kb + q < kdim)
-                        ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(fa(kb + q)) + m8 * EB)
-                        : u32x4_t{0, 0, 0, 0};
-      }
-    }
-    if constexpr (BMODE == KC) {
-#pragma unroll
-      for (int i = 0; i < C::BKC; ++i) g.kb[i] = *reinterpret_cast<const u32x4_t*>(rpb[i] + kbyte + kc * 16);
-      if constexpr (FP8) {
-        if (t < BN) {
-          if constexpr (SBK == 2) g.sb = *reinterpret_cast<const uint16_t*>(spb + k0 / 32);
-          else g.sb = *reinterpret_cast<const uint32_t*>(spb + k0 / 32);
-        }
-      }
-    } else {
-      if (rcB) {
-        if constexpr (FP8) {
-          const int kb = k0 + bkg * 4, n16 = brg * 16;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            g.rb[q] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(fb(kb + q)) + n16);
-          // column scales: SBK blocks x 128 columns, 4 columns per thread on the first 32*SBK threads
-          if (u < 32 * SBK)
-            g.sb = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(fbs(k0 / 32 + (u >> 5))) +
-                                                      (u & 31) * 4);
-        } else {
-          const int kb = k0 + bkg * RK, n8 = brg * 8;
-#pragma unroll
-          for (int q = 0; q < RK; ++q)
-            g.rb[q] = (kb + q < kdim)
-                          ? *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(fb(kb + q)) + n8 * 2)
-                          : u32x4_t{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-  auto sstore = [&](int s, const Staged<TM>& g) __attribute__((always_inline)) {
-    uint8_t* As = lds + s * C::STAGE;
-    uint8_t* Bs = As + C::B_OFF;
-    if constexpr (AM == KC) {
-#pragma unroll
-      for (int i = 0; i < C::AKC; ++i)
-        *reinterpret_cast<u32x4_t*>(As + (kr + RSTEP * i) * ROW + kc * 16) = g.ka[i];
-      if constexpr (FP8) {
-        if (t < TM) {
-          if constexpr (SBK == 2) *reinterpret_cast<uint16_t*>(sc + s * C::SC_STAGE + t * SBK) = (uint16_t)g.sa;
-          else *reinterpret_cast<uint32_t*>(sc + s * C::SC_STAGE + t * SBK) = g.sa;
-        }
-      }
-    } else {
-      if (rcA) {
-        store_tr_bf16<RK>(As, arg * 8, akg * 2 * RK, g.ra);
-      } else if (rcAz) {
-        u32x4_t z[RK];
-#pragma unroll
-        for (int q = 0; q < RK; ++q) z[q] = u32x4_t{0, 0, 0, 0};
-        store_tr_bf16<RK>(As, arg * 8, akg * 2 * RK, z);
-      }
-    }
-    if constexpr (BMODE == KC) {
-#pragma unroll
-      for (int i = 0; i < C::BKC; ++i) *reinterpret_cast<u32x4_t*>(Bs + (kr + RSTEP * i) * ROW + kc * 16) = g.kb[i];
-      if constexpr (FP8) {
-        if (t < BN) {
-          if constexpr (SBK == 2) *reinterpret_cast<uint16_t*>(sc + s * C::SC_STAGE + C::SC_B + t * SBK) = (uint16_t)g.sb;
-          else *reinterpret_cast<uint32_t*>(sc + s * C::SC_STAGE + C::SC_B + t * SBK) = g.sb;
-        }
-      }
-    } else {
-      if (rcB) {
-        if constexpr (FP8) {
-          const u32x4_t r4[4] = {g.rb[0], g.rb[1], g.rb[2], g.rb[3]};
-          store_tr_u8(Bs, brg * 16, bkg * 4, r4);
-          if (u < 32 * SBK) {
-            const int kb = u >> 5, n4 = (u & 31) * 4;
-            uint8_t* sB = sc + s * C::SC_STAGE + C::SC_B;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sB[(n4 + j) * SBK + kb] = (uint8_t)(g.sb >> (8 * j));
-          }
-        } else {
-          store_tr_bf16<RK>(Bs, brg * 8, bkg * 2 * RK, g.rb);
-        }
-      }
-    }
-  };
-  auto compute = [&](int s) __attribute__((always_inline)) {
-    if (!wave_active) return;
-    const uint8_t* As = lds + s * C::STAGE;
-    const uint8_t* Bs = As + C::B_OFF;
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int ks = 0; ks < KBYTES / 32; ++ks) {
-        bf16x8_t a[C::MI], b[C::NJ];
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-          a[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * C::WMR + i * 32 + (lane & 31)) * ROW + ks * 32 +
-                                                    (lane >> 5) * 16);
-#pragma unroll
-        for (int j = 0; j < C::NJ; ++j)
-          b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * C::WNC + j * 32 + (lane & 31)) * ROW + ks * 32 +
-                                                    (lane >> 5) * 16);
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-          for (int j = 0; j < C::NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // Per 64-code K step, lane (r, g) holds codes 16g..16g+15 and 32+16g..32+16g+15 and
-      // carries the scale of 32-code block g (the scaled MFMA's measured lane layout).
-      const uint8_t* sA = sc + s * C::SC_STAGE;
-      const uint8_t* sB = sA + C::SC_B;
-#pragma unroll
-      for (int ks = 0; ks < KBYTES / 64; ++ks) {
-        i32x8_t a[C::MI], b[C::NJ];
-        int sa[C::MI], sb[C::NJ];
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i) {
-          const int r = wm * C::WMR + i * 32 + (lane & 31);
-          const uint8_t* p = As + r * ROW + ks * 64 + (lane >> 5) * 16;
-          const u32x4_t u0 = *reinterpret_cast<const u32x4_t*>(p);
-          const u32x4_t u1 = *reinterpret_cast<const u32x4_t*>(p + 32);
-          a[i] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-          sa[i] = sA[r * SBK + ks * 2 + (lane >> 5)];
-        }
-#pragma unroll
-        for (int j = 0; j < C::NJ; ++j) {
-          const int c = wn * C::WNC + j * 32 + (lane & 31);
-          const uint8_t* p = Bs + c * ROW + ks * 64 + (lane >> 5) * 16;
-          const u32x4_t u0 = *reinterpret_cast<const u32x4_t*>(p);
-          const u32x4_t u1 = *reinterpret_cast<const u32x4_t*>(p + 32);
-          b[j] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-          sb[j] = sB[c * SBK + ks * 2 + (lane >> 5)];
-        }
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-          for (int j = 0; j < C::NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
-      }
-    }
-  };
-
-  const int nk = (kdim + KST - 1) / KST;
-  if (nk <= 0) return;
-  Staged<TM> buf[PFD];
-#pragma unroll
-  for (int q = 0; q < PFD; ++q)
-    if (q < nk) gload(q * KST, buf[q]);
-  sstore(0, buf[0]);
-  __syncthreads();
-  for (int k0 = 0; k0 < nk; k0 += PFD) {
-#pragma unroll
-    for (int q = 0; q < PFD; ++q) {
-      const int kt = k0 + q;          // buf[q] held stage kt, already in LDS: reuse it for kt + PFD
-      if (kt < nk) {
-        if (kt + PFD < nk) gload((kt + PFD) * KST, buf[q]);
-        compute(kt & 1);
-        if (kt + 1 < nk) sstore((kt + 1) & 1, buf[(q + 1) % PFD]);
-        __syncthreads();
-      }
-    }
-  }
-}
-
-// Accumulator element r of block (i, j): 32x32 MFMA result layout, lane holds column
-// lane % 32 and rows 8 (r / 4) + 4 (lane / 32) + r % 4 of its block.
-template <int TM>
-__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * Cfg<TM>::WMR + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-}
-template <int TM>
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
-  return wn * Cfg<TM>::WNC + j * 32 + (lane & 31);
-}
-
-template <int TM>
-__device__ __forceinline__ void zero_acc(Acc<TM>& acc) {
-#pragma unroll
-  for (int i = 0; i < Cfg<TM>::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg<TM>::NJ; ++j) acc[i][j] = f32x16_t{};
-}
 
 struct NoScale {
   __device__ const uint8_t* operator()(int) const { return nullptr; }
 };
 
 // ---------------------------------------------------------------------------------
+// acc[i][j] (wave rows wm*WMR + 32 i, columns wn*WNC + 32 j) += A[TM x K] * B[TN x K]^T.
+//  KC operand: fa(r) / fb(r) -> bytes of tile row r at K = 0 (callers clamp rows past
+//              the end to a valid row; the result rows they feed are never stored).
+//  RC operand: fa(k) / fb(k) -> bytes of element (k, tile row 0); called for k < kdim.
+//              acols / bcols: tile rows of a row-contiguous A / B that exist (a multiple
+//              of 8); the 16-byte pieces past them come from the zero page instead.
+//  MXFP8 scales: fas(r) / fbs(r) -> E8M0 row of tile row r (KC operand), or for a
+//              row-contiguous B, fbs(kb) -> E8M0 byte of (K block kb, tile column 0).
+// ---------------------------------------------------------------------------------
+template <class TL, int AM, int BMODE, bool FP8, class FA, class FB, class FAS, class FBS>
+__device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, const FB& fb, const FAS& fas,
+                                         const FBS& fbs, uint8_t* lds, uint8_t* sc, bool wave_active,
+                                         int acols = TL::TM, uint8_t* pf_lds = nullptr, int bcols = TL::TN) {
+  static_assert(!(FP8 && AM == RC), "MXFP8 A operands are K-contiguous");
+  static_assert(!FP8 || TL::KB == 128, "MXFP8 stages are 128 codes (4 scale blocks)");
+  constexpr int KB = TL::KB;
+  constexpr int EB = FP8 ? 1 : 2;        // bytes per element
+  constexpr int KST = KB / EB;           // K elements per stage
+  constexpr int RBA = TL::TM * EB, RBB = TL::TN * EB;   // RC row bytes
+  constexpr int LPS = TL::A_DMA + TL::B_DMA + (FP8 ? TL::SC_DMA : 0) + TL::PF_N;   // loads per stage per wave
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / TL::NWN, wn = w % TL::NWN;
+  const uint32_t lds0 = lds_off(lds);
+  const uint32_t sc0 = FP8 ? lds_off(sc) : 0u;
+  const uint8_t* zp = reinterpret_cast<const uint8_t*>(g_zero_page) + 16 * lane;
+  const int nk = (kdim + KST - 1) / KST;
+
+  // ---- per-lane DMA sources.  Slot i of this wave fills 1 KB block w * X_DMA + i.
+  const uint8_t* pa[TL::A_DMA];
+  const uint8_t* pb[TL::B_DMA];
+  int ka[TL::A_DMA], kb[TL::B_DMA];       // RC: k row within the stage
+  int ca[TL::A_DMA], cb[TL::B_DMA];       // RC: byte offset inside the tile row
+#pragma unroll
+  for (int i = 0; i < TL::A_DMA; ++i) {
+    const int off = (w * TL::A_DMA + i) * 1024 + 16 * lane;
+    if constexpr (AM == KC) {
+      const int r = off / KB, c = ((off % KB) >> 4) ^ swz_kc<KB>(r);
+      pa[i] = reinterpret_cast<const uint8_t*>(fa(r)) + 16 * c;
+      ka[i] = ca[i] = 0;
+    } else {
+      const int k = off / RBA, c = ((off % RBA) >> 4) ^ swz_rc16(k);
+      pa[i] = nullptr;
+      ka[i] = 16 * c < acols * EB ? k : (1 << 30);   // columns past acols: never loaded
+      ca[i] = 16 * c;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TL::B_DMA; ++i) {
+    const int off = (w * TL::B_DMA + i) * 1024 + 16 * lane;
+    if constexpr (BMODE == KC) {
+      const int r = off / KB, c = ((off % KB) >> 4) ^ swz_kc<KB>(r);
+      pb[i] = reinterpret_cast<const uint8_t*>(fb(r)) + 16 * c;
+      kb[i] = cb[i] = 0;
+    } else {
+      const int k = off / RBB;
+      const int c = ((off % RBB) >> 4) ^ (FP8 ? swz_rc8<RBB>(k) : swz_rc16(k));
+      pb[i] = nullptr;
+      kb[i] = 16 * c < bcols * EB ? k : (1 << 30);   // columns past bcols: never loaded
+      cb[i] = 16 * c;
+    }
+  }
+  // MXFP8 scale DMA sources (dword per lane): instruction q < SC_A/256 covers A rows
+  // 64q.., the next ones B (KC rows, or RC [4 blocks][TN] bytes), the rest are dummies.
+  const uint8_t* ps[TL::SC_DMA];
+  int qs[TL::SC_DMA];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < TL::SC_DMA; ++i) {
+      const int q = w * TL::SC_DMA + i;
+      qs[i] = q;
+      ps[i] = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
+      if (q < TL::SC_A / 256) {
+        ps[i] = fas(q * 64 + lane);
+      } else if (q < TL::SC_REAL) {
+        const int idx = (q - TL::SC_A / 256) * 64 + lane;
+        if constexpr (BMODE == KC) ps[i] = fbs(idx);
+      }
+    }
+  }
+
+  // L2 prefetch sources: line p * NTH + 64 w + lane of a stage; lines < TM belong to A.
+  const uint32_t pfm0 = TL::PF ? lds_off(pf_lds) : 0u;
+  auto pf_issue = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < TL::PF_N; ++p) {
+      const int line = p * TL::NTH + 64 * w + lane;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
+      if (line < TL::TM) {
+        if constexpr (AM == KC) {
+          src = reinterpret_cast<const uint8_t*>(fa(line)) + kt * 128;
+        } else {
+          const int k = kt * KST + line / (RBA / 128);
+          if (k < kdim && 128 * (line % (RBA / 128)) < acols * EB)
+            src = reinterpret_cast<const uint8_t*>(fa(k)) + 128 * (line % (RBA / 128));
+        }
+      } else if (line < TL::TM + TL::TN) {
+        const int lb = line - TL::TM;
+        if constexpr (BMODE == KC) {
+          src = reinterpret_cast<const uint8_t*>(fb(lb)) + kt * 128;
+        } else {
+          const int k = kt * KST + lb / (RBB / 128);
+          if (k < kdim && 128 * (lb % (RBB / 128)) < bcols * EB)
+            src = reinterpret_cast<const uint8_t*>(fb(k)) + 128 * (lb % (RBB / 128));
+        }
+      }
+      dma4(src, pfm0);
+    }
+  };
+
+  auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
+    const uint32_t sa = lds0 + slot * TL::STAGE, sb = sa + TL::A_BYTES;
+    const int k0 = kt * KST;
+#pragma unroll
+    for (int i = 0; i < TL::A_DMA; ++i) {
+      const uint32_t m0v = sa + (w * TL::A_DMA + i) * 1024;
+      if constexpr (AM == KC) {
+        dma16(pa[i] + kt * KB, m0v);
+      } else {
+        const int k = k0 + ka[i];
+        dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fa(k)) + ca[i] : zp, m0v);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TL::B_DMA; ++i) {
+      const uint32_t m0v = sb + (w * TL::B_DMA + i) * 1024;
+      if constexpr (BMODE == KC) {
+        dma16(pb[i] + kt * KB, m0v);
+      } else {
+        const int k = k0 + kb[i];
+        dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fb(k)) + cb[i] : zp, m0v);
+      }
+    }
+    if constexpr (FP8) {
+#pragma unroll
+      for (int i = 0; i < TL::SC_DMA; ++i) {
+        const int q = qs[i];
+        if (q < TL::SC_A / 256) {
+          dma4(ps[i] + kt * 4, sc0 + slot * TL::SC_STAGE + q * 256);
+        } else if (q < TL::SC_REAL) {
+          const uint32_t m0v = sc0 + slot * TL::SC_STAGE + q * 256;
+          if constexpr (BMODE == KC) {
+            dma4(ps[i] + kt * 4, m0v);
+          } else {
+            const int idx = (q - TL::SC_A / 256) * 64 + lane;   // [kb][TN] bytes 4 idx .. 4 idx + 3
+            const int kblk = (4 * idx) / TL::TN, col = (4 * idx) % TL::TN;
+            dma4(col < bcols ? reinterpret_cast<const uint8_t*>(fbs(kt * 4 + kblk)) + col
+                             : reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane,
+                 m0v);
+          }
+        } else {
+          dma4(ps[i], sc0 + TL::NS * TL::SC_STAGE);
+        }
+      }
+    }
+    if constexpr (TL::PF > 0) pf_issue(min(kt + TL::PF, nk - 1));
+  };
+
+  // ---- fragment reads and MFMAs of one stage
+  auto compute = [&](int slot) __attribute__((always_inline)) {
+    const uint8_t* As = lds + slot * TL::STAGE;
+    const uint8_t* Bs = As + TL::A_BYTES;
+    const int g = lane >> 5, grp = lane >> 4, j16 = lane & 15;
+    // Small wave tiles read all fragments of the stage first, so the LDS reads of later K
+    // steps overlap the MFMAs of earlier ones; large ones (whose fragments would not fit
+    // in registers beside the accumulators) read and multiply one K step at a time.
+    if constexpr (!FP8) {
+      constexpr int NKS = KB / 32;   // 16-element K steps per stage
+      constexpr bool PRE = NKS * (TL::MI + TL::NJ) * 4 <= 64;
+      bf16x8_t a[NKS][TL::MI], b[NKS][TL::NJ];
+      auto load = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i) {
+          if constexpr (AM == KC) {
+            const int r = wm * TL::WMR + i * 32 + (lane & 31);
+            a[ks][i] = *reinterpret_cast<const bf16x8_t*>(As + r * KB + (((2 * ks + g) ^ swz_kc<KB>(r)) << 4));
+          } else {
+            const int m0 = wm * TL::WMR + i * 32 + 16 * (grp & 1);
+            i16x4_t h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int k = 16 * ks + 8 * (grp >> 1) + 4 * hh + (j16 >> 2);
+              const int byte = 2 * (m0 + 4 * (j16 & 3));
+              h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)((lds_u8*)As + k * RBA + ((((byte >> 4) ^ swz_rc16(k)) << 4) | (byte & 15))));
+            }
+            a[ks][i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TL::NJ; ++j) {
+          if constexpr (BMODE == KC) {
+            const int r = wn * TL::WNC + j * 32 + (lane & 31);
+            b[ks][j] = *reinterpret_cast<const bf16x8_t*>(Bs + r * KB + (((2 * ks + g) ^ swz_kc<KB>(r)) << 4));
+          } else {
+            const int n0 = wn * TL::WNC + j * 32 + 16 * (grp & 1);
+            i16x4_t h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int k = 16 * ks + 8 * (grp >> 1) + 4 * hh + (j16 >> 2);
+              const int byte = 2 * (n0 + 4 * (j16 & 3));
+              h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_i16x4*)((lds_u8*)Bs + k * RBB + ((((byte >> 4) ^ swz_rc16(k)) << 4) | (byte & 15))));
+            }
+            b[ks][j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        }
+      };
+      auto mma = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < TL::NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+      };
+      if constexpr (PRE) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) load(ks);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) mma(ks);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          load(ks);
+          mma(ks);
+        }
+      }
+    } else {
+      // Per 64-code K step, lane (r, g) holds codes 16g..16g+15 and 32+16g..32+16g+15 and
+      // carries the scale of 32-code block g (the scaled MFMA's measured lane layout).
+      const uint8_t* sA = sc + slot * TL::SC_STAGE;
+      const uint8_t* sB = sA + TL::SC_A;
+      constexpr bool PRE = 2 * (TL::MI + TL::NJ) * 8 <= 64;
+      i32x8_t a[2][TL::MI], b[2][TL::NJ];
+      int sa[2][TL::MI], sb[2][TL::NJ];
+      auto load = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i) {
+          const int r = wm * TL::WMR + i * 32 + (lane & 31);
+          const uint8_t* p = As + r * KB;
+          const u32x4_t u0 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g) ^ swz_kc<KB>(r)) << 4));
+          const u32x4_t u1 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g + 2) ^ swz_kc<KB>(r)) << 4));
+          a[ks][i] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+          sa[ks][i] = sA[r * 4 + 2 * ks + g];
+        }
+#pragma unroll
+        for (int j = 0; j < TL::NJ; ++j) {
+          const int c = wn * TL::WNC + j * 32 + (lane & 31);
+          if constexpr (BMODE == KC) {
+            const uint8_t* p = Bs + c * KB;
+            const u32x4_t u0 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g) ^ swz_kc<KB>(c)) << 4));
+            const u32x4_t u1 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g + 2) ^ swz_kc<KB>(c)) << 4));
+            b[ks][j] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+            sb[ks][j] = sB[c * 4 + 2 * ks + g];
+          } else {
+            const int n0 = wn * TL::WNC + j * 32 + 16 * (grp & 1);
+            i32x2_t q[4];
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+              const int k = 64 * ks + 16 * g + 8 * (hh & 1) + 32 * (hh >> 1) + (j16 >> 1);
+              const int byte = n0 + 8 * (j16 & 1);
+              q[hh] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                  (lds_i32x2*)((lds_u8*)Bs + k * RBB + ((((byte >> 4) ^ swz_rc8<RBB>(k)) << 4) | (byte & 15))));
+            }
+            b[ks][j] = i32x8_t{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
+            sb[ks][j] = sB[(2 * ks + g) * TL::TN + c];
+          }
+        }
+      };
+      auto mma = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < TL::NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0,
+                                                                         sa[ks][i], 0, sb[ks][j]);
+      };
+      if constexpr (PRE) {
+        load(0);
+        load(1);
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
+        mma(0);
+        mma(1);
+      } else {
+        load(0);
+        mma(0);
+        load(1);
+        mma(1);
+      }
+    }
+  };
+
+  // ---- NS-stage pipeline, one barrier per stage.  At the top of step kt the wave's
+  // DMAs of stage kt must have landed; those of the up to NS - 2 later stages may fly
+  // (with PF, each stage's group of loads ends with its prefetch, which may fly too).
+#pragma unroll
+  for (int s = 0; s < TL::NS - 1; ++s)
+    if (s < nk) issue(s, s);
+  // Two copies of the loop, so that skipping the MFMAs of an idle wave is not a branch
+  // inside it (a conditional update would make the accumulators flow through a join
+  // and cost a copy of every accumulator register per stage).
+  auto run = [&](auto act) __attribute__((always_inline)) {
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ahead = min(TL::NS - 2, nk - 1 - kt);
+      constexpr int TAIL = TL::PF_N;   // the prefetch that follows stage kt's DMAs
+      if constexpr (TL::NS >= 4) {
+        if (ahead >= 2) wait_vm<2 * LPS + TAIL>();
+        else if (ahead == 1) wait_vm<LPS + TAIL>();
+        else wait_vm<TAIL>();
+      } else if constexpr (TL::NS == 3) {
+        if (ahead >= 1) wait_vm<LPS + TAIL>();
+        else wait_vm<TAIL>();
+      } else {
+        wait_vm<TAIL>();
+      }
+      __syncthreads();
+      if (kt + TL::NS - 1 < nk) issue(kt + TL::NS - 1, (kt + TL::NS - 1) % TL::NS);
+      if constexpr (decltype(act)::value) compute(kt % TL::NS);
+    }
+  };
+  if (wave_active) run(std::true_type{});
+  else run(std::false_type{});
+}
+
+// Accumulator element r of block (i, j): 32x32 MFMA result layout, lane holds column
+// lane % 32 and rows 8 (r / 4) + 4 (lane / 32) + r % 4 of its block.
+template <class TL>
+__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
+  return wm * TL::WMR + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+template <class TL>
+__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
+  return wn * TL::WNC + j * 32 + (lane & 31);
+}
+
+template <class TL>
+__device__ __forceinline__ void zero_acc(Acc<TL>& acc) {
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::NJ; ++j) acc[i][j] = f32x16_t{};
+}
+
+// ---------------------------------------------------------------------------------
 // Token-dimension grouped tiles: group g < E is routed expert g with counts[g] rows
 // starting at offsets[g] of the permuted buffers; group E is the shared expert with
-// T rows.  tile_prefix[g] = sum of ceil(rows / BM) over groups before g.  Linear
+// T rows.  tile_prefix[g] = sum of ceil(rows / BMT) over groups before g.  Linear
 // tiles (m-tile major, n-tile minor) are split into 8 contiguous chunks, chunk x
 // run by the blocks with blockIdx % 8 == x (the blocks one XCD receives), so the
 // n-tiles that share an A row panel run on one L2.
@@ -417,9 +469,10 @@ struct TokTile {
   bool ok;
 };
 
+template <int BMT>
 __device__ __forceinline__ TokTile map_tok_tile(const int32_t* __restrict__ tile_prefix, int groups, int ntn,
                                                 int E, const int32_t* __restrict__ counts, int T, int* sp) {
-  for (int i = threadIdx.x; i <= groups; i += NT) sp[i] = tile_prefix[i];
+  for (int i = threadIdx.x; i <= groups; i += blockDim.x) sp[i] = tile_prefix[i];
   __syncthreads();
   TokTile tt;
   const int total = sp[groups] * ntn;
@@ -436,9 +489,9 @@ __device__ __forceinline__ TokTile map_tok_tile(const int32_t* __restrict__ tile
     if (sp[mid] <= mt) lo = mid; else hi = mid - 1;
   }
   tt.g = lo;
-  tt.m0 = (mt - sp[lo]) * BM;
+  tt.m0 = (mt - sp[lo]) * BMT;
   const int n = (lo < E) ? counts[lo] : T;
-  tt.rows = min(BM, n - tt.m0);
+  tt.rows = min(BMT, n - tt.m0);
   return tt;
 }
 
@@ -457,7 +510,59 @@ struct MxOperands {
   MxRef b0, b1;          // routed B: rowwise (forward) or columnwise (data gradient) copies
 };
 
-using TC = Cfg<BM>;
+// Tile shapes per kernel: TM, TN, waves along M, waves along N, LDS stages, the
+// workgroups per CU the register budget targets, L2 prefetch distance, K bytes per
+// stage.  BF16 and MXFP8 routed weights take separate shapes; within one of the two,
+// every token-dimension GEMM has the same M tile (the routing scan builds one tile
+// prefix for it).
+#ifndef MOE_TL_FC1
+#define MOE_TL_FC1 128, 256, 2, 2, 3, 2, 0, 64
+#endif
+#ifndef MOE_TL_FC2
+#define MOE_TL_FC2 128, 256, 2, 2, 3, 2, 0, 64
+#endif
+#ifndef MOE_TL_DG2
+#define MOE_TL_DG2 128, 256, 2, 2, 3, 2, 0, 64
+#endif
+#ifndef MOE_TL_DG1
+#define MOE_TL_DG1 128, 256, 2, 2, 3, 2, 0, 64
+#endif
+#ifndef MOE_TL_FC1_MX
+#define MOE_TL_FC1_MX 256, 256, 2, 4, 2, 1
+#endif
+#ifndef MOE_TL_FC2_MX
+#define MOE_TL_FC2_MX 256, 256, 2, 4, 2, 1
+#endif
+#ifndef MOE_TL_DG2_MX
+#define MOE_TL_DG2_MX 256, 256, 2, 4, 2, 1, 2
+#endif
+#ifndef MOE_TL_DG1_MX
+#define MOE_TL_DG1_MX 256, 256, 2, 4, 2, 1, 2
+#endif
+#ifndef MOE_TL_WG
+#define MOE_TL_WG 128, 128, 2, 2, 2, 2
+#endif
+template <bool MX> struct Shapes;
+template <> struct Shapes<false> {
+  using FC1 = Tile<MOE_TL_FC1>; using FC2 = Tile<MOE_TL_FC2>;
+  using DG2 = Tile<MOE_TL_DG2>; using DG1 = Tile<MOE_TL_DG1>;
+};
+template <> struct Shapes<true> {
+  using FC1 = Tile<MOE_TL_FC1_MX>; using FC2 = Tile<MOE_TL_FC2_MX>;
+  using DG2 = Tile<MOE_TL_DG2_MX>; using DG1 = Tile<MOE_TL_DG1_MX>;
+};
+using TL_WG = Tile<MOE_TL_WG>;
+template <bool MX>
+constexpr int bm_of() { return Shapes<MX>::FC1::TM; }
+static_assert(Shapes<false>::FC2::TM == bm_of<false>() && Shapes<false>::DG2::TM == bm_of<false>() &&
+              Shapes<false>::DG1::TM == bm_of<false>(), "BF16 token-dimension tiles share their M tile");
+static_assert(Shapes<true>::FC2::TM == bm_of<true>() && Shapes<true>::DG2::TM == bm_of<true>() &&
+              Shapes<true>::DG1::TM == bm_of<true>(), "MXFP8 token-dimension tiles share their M tile");
+
+template <class TL>
+__device__ __forceinline__ int wave_m() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / TL::NWN; }
+template <class TL>
+__device__ __forceinline__ int wave_n() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % TL::NWN; }
 
 // FC1 + SwiGLU: [a | b] = A W1^T with gate rows -> a, up rows -> b; writes a, b
 // (bf16, [rows][2I]: a at column j, b at I + j) and h = silu(a) * b (bf16, [rows][I]).
@@ -476,28 +581,36 @@ struct Fc1Args {
 };
 
 template <bool MX>
-__global__ __launch_bounds__(NT, MINB) void k_fc1_swiglu(Fc1Args p) {
-  __shared__ __align__(16) uint8_t lds[TC::LDS_BYTES];
-  __shared__ __align__(16) uint8_t sc[MX ? 2 * TC::SC_STAGE : 16];
+__global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k_fc1_swiglu(Fc1Args p) {
+  using TL = typename Shapes<MX>::FC1;
+  static_assert(TL::WNC % 64 == 0 && TL::TN <= 256, "gate/up pairs per wave; 2I is a multiple of TN");
+  __shared__ __align__(16) uint8_t lds[TL::LDS];
+  __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
+  __shared__ __align__(16) uint8_t sc[MX ? TL::SC_LDS : 16];
   __shared__ int sp[kMaxExperts + 2];
-  const TokTile tt = map_tok_tile(p.t.tile_prefix, p.t.groups, p.I / 64, p.t.E, p.t.counts, p.t.T, sp);
+  const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, 2 * p.I / TL::TN, p.t.E, p.t.counts, p.t.T, sp);
   if (!tt.ok) return;
   const bool shared = tt.g == p.t.E;
   const int e = shared ? 0 : tt.g;
   const int64_t arow0 = shared ? tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int H = p.H, last = tt.rows - 1;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / TC::WN, wn = w % TC::WN;
-  auto brow = [&](int rr) { return tt.nt * 64 + (rr >> 6) * 32 + (rr & 31); };   // logical column
-  Acc<BM> acc;
-  zero_acc<BM>(acc);
-  const bool active = wm * TC::WMR < tt.rows;
-  if (MX && !shared) {
-    auto fa = [&](int r) { return p.mx.aq + (arow0 + min(r, last)) * H; };
-    auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (H / 32); };
-    auto fb = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).data.row(e, brow(rr)); };
-    auto fbs = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).scale.row(e, brow(rr)); };
-    tile_mma<BM, KC, KC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active);
-  } else {
+  const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  auto brow = [&](int rr) { return tt.nt * (TL::TN / 2) + (rr >> 6) * 32 + (rr & 31); };   // logical column
+  Acc<TL> acc;
+  zero_acc<TL>(acc);
+  const bool active = wm * TL::WMR < tt.rows;
+  bool done = false;
+  if constexpr (MX) {
+    if (!shared) {
+      auto fa = [&](int r) { return p.mx.aq + (arow0 + min(r, last)) * H; };
+      auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (H / 32); };
+      auto fb = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).data.row(e, brow(rr)); };
+      auto fbs = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).scale.row(e, brow(rr)); };
+      tile_mma<TL, KC, KC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb);
+      done = true;
+    }
+  }
+  if (!done) {
     const uint16_t* abase = shared ? p.x : p.xp;
     auto fa = [&](int r) { return abase + (arow0 + min(r, last)) * H; };
     const uint8_t* gb = shared ? p.sg.row(0, 0) : p.wg.row(e, 0);
@@ -508,19 +621,19 @@ __global__ __launch_bounds__(NT, MINB) void k_fc1_swiglu(Fc1Args p) {
       const int jj = brow(rr);
       return ((rr >> 5) & 1) ? ub + (int64_t)jj * uld : gb + (int64_t)jj * gld;
     };
-    tile_mma<BM, KC, KC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active);
+    tile_mma<TL, KC, KC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb);
   }
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int I = p.I;
 #pragma unroll
-  for (int jp = 0; jp < TC::NJ / 2; ++jp) {
-    const int jj = tt.nt * 64 + (wn * TC::NJ / 2 + jp) * 32 + (lane & 31);
+  for (int jp = 0; jp < TL::NJ / 2; ++jp) {
+    const int jj = tt.nt * (TL::TN / 2) + (wn * TL::NJ / 2 + jp) * 32 + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < TC::MI; ++i)
+    for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<BM>(wm, i, r, lane);
+        const int row = acc_row<TL>(wm, i, r, lane);
         if (row >= tt.rows) continue;
         const float a = acc[i][2 * jp][r], b = acc[i][2 * jp + 1][r];
         const int64_t R = crow0 + row;
@@ -543,44 +656,55 @@ struct PlainArgs {
   int64_t a_s_row0;      // first shared row inside a_s
   MatRef w0, w1, s0, s1; // weights: KC: w0 rows; RC: k < ksplit from w0, else w1
   MxOperands mx;
-  int ksplit;
+  int ksplit;            // a multiple of 128, so no K stage straddles the two parts
   uint16_t* c;           // [rows][N] (routed rows at offsets, shared at shared_row0)
   int N, K;
 };
 
 template <int BMODE, bool MX>
-__global__ __launch_bounds__(NT, BMODE == KC ? MINB : MINB_DG) void k_gemm_plain(PlainArgs p) {
-  __shared__ __align__(16) uint8_t lds[TC::LDS_BYTES];
-  __shared__ __align__(16) uint8_t sc[MX ? 2 * TC::SC_STAGE : 16];
+using TL_PLAIN = typename std::conditional<BMODE == KC, typename Shapes<MX>::FC2, typename Shapes<MX>::DG1>::type;
+
+template <int BMODE, bool MX>
+__global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::MINB)) void k_gemm_plain(PlainArgs p) {
+  using TL = TL_PLAIN<BMODE, MX>;
+  __shared__ __align__(16) uint8_t lds[TL::LDS];
+  __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
+  __shared__ __align__(16) uint8_t sc[MX ? TL::SC_LDS : 16];
   __shared__ int sp[kMaxExperts + 2];
-  const TokTile tt = map_tok_tile(p.t.tile_prefix, p.t.groups, p.N / BN, p.t.E, p.t.counts, p.t.T, sp);
+  const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, (p.N + TL::TN - 1) / TL::TN, p.t.E, p.t.counts,
+                                          p.t.T, sp);
   if (!tt.ok) return;
   const bool shared = tt.g == p.t.E;
   const int e = shared ? 0 : tt.g;
   const int64_t arow0 = shared ? p.a_s_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int K = p.K, last = tt.rows - 1;
-  const int n0 = tt.nt * BN;
+  const int n0 = tt.nt * TL::TN;
+  const int ncols = min(TL::TN, p.N - n0);   // the last N tile may be partial (a multiple of 128)
+  const int nlast = ncols - 1;
   const int ksplit = p.ksplit;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / TC::WN, wn = w % TC::WN;
-  Acc<BM> acc;
-  zero_acc<BM>(acc);
-  const bool active = wm * TC::WMR < tt.rows;
-  if (MX && !shared) {
+  const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  Acc<TL> acc;
+  zero_acc<TL>(acc);
+  const bool active = wm * TL::WMR < tt.rows;
+  bool done = false;
+  if constexpr (MX) if (!shared) {
+    done = true;
     auto fa = [&](int r) { return p.mx.aq + (arow0 + min(r, last)) * K; };
     auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (K / 32); };
     if constexpr (BMODE == KC) {
-      auto fb = [&](int r) { return p.mx.b0.data.row(e, n0 + r); };
-      auto fbs = [&](int r) { return p.mx.b0.scale.row(e, n0 + r); };
-      tile_mma<BM, KC, KC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active);
+      auto fb = [&](int r) { return p.mx.b0.data.row(e, n0 + min(r, nlast)); };
+      auto fbs = [&](int r) { return p.mx.b0.scale.row(e, n0 + min(r, nlast)); };
+      tile_mma<TL, KC, KC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb);
     } else {
       const int kbsplit = ksplit / 32;
       auto fb = [&](int q) { return (q < ksplit ? p.mx.b0.data.row(e, q) : p.mx.b1.data.row(e, q - ksplit)) + n0; };
       auto fbs = [&](int kb) {
         return (kb < kbsplit ? p.mx.b0.scale.row(e, kb) : p.mx.b1.scale.row(e, kb - kbsplit)) + n0;
       };
-      tile_mma<BM, KC, RC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active);
+      tile_mma<TL, KC, RC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb, ncols);
     }
-  } else {
+  }
+  if (!done) {
     const uint16_t* abase = shared ? p.a_s : p.a_r;
     auto fa = [&](int r) { return abase + (arow0 + min(r, last)) * K; };
     // per-tile base rows of the two weight parts, so the loaders only add row offsets
@@ -589,27 +713,28 @@ __global__ __launch_bounds__(NT, BMODE == KC ? MINB : MINB_DG) void k_gemm_plain
     const int64_t ld0 = shared ? p.s0.ld_bytes : p.w0.ld_bytes;
     const int64_t ld1 = shared ? p.s1.ld_bytes : p.w1.ld_bytes;
     if constexpr (BMODE == KC) {
-      auto fb = [&](int q) { return b0 + (int64_t)(n0 + q) * ld0; };
-      tile_mma<BM, KC, KC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active);
+      auto fb = [&](int q) { return b0 + (int64_t)(n0 + min(q, nlast)) * ld0; };
+      tile_mma<TL, KC, KC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb);
     } else {
       auto fb = [&](int q) {
         return ((q < ksplit) ? b0 + (int64_t)q * ld0 : b1 + (int64_t)(q - ksplit) * ld1) + 2 * n0;
       };
-      tile_mma<BM, KC, RC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active);
+      tile_mma<TL, KC, RC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb, ncols);
     }
   }
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int N = p.N;
+  if (wn * TL::WNC >= ncols) return;
 #pragma unroll
-  for (int i = 0; i < TC::MI; ++i)
+  for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < TC::NJ; ++j)
+    for (int j = 0; j < TL::NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<BM>(wm, i, r, lane);
-        if (row >= tt.rows) continue;
-        p.c[(crow0 + row) * N + n0 + acc_col<BM>(wn, j, lane)] = (uint16_t)f2bf(acc[i][j][r]);
+        const int row = acc_row<TL>(wm, i, r, lane);
+        if (row >= tt.rows || acc_col<TL>(wn, j, lane) >= ncols) continue;
+        p.c[(crow0 + row) * N + n0 + acc_col<TL>(wn, j, lane)] = (uint16_t)f2bf(acc[i][j][r]);
       }
 }
 
@@ -629,46 +754,54 @@ struct DgradSwigluArgs {
 };
 
 template <bool MX>
-__global__ __launch_bounds__(NT, MINB_DG) void k_dgrad_swiglu(DgradSwigluArgs p) {
-  __shared__ __align__(16) uint8_t lds[TC::LDS_BYTES];
-  __shared__ __align__(16) uint8_t sc[MX ? 2 * TC::SC_STAGE : 16];
+__global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k_dgrad_swiglu(DgradSwigluArgs p) {
+  using TL = typename Shapes<MX>::DG2;
+  __shared__ __align__(16) uint8_t lds[TL::LDS];
+  __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
+  __shared__ __align__(16) uint8_t sc[MX ? TL::SC_LDS : 16];
   __shared__ int sp[kMaxExperts + 2];
-  const TokTile tt = map_tok_tile(p.t.tile_prefix, p.t.groups, p.I / BN, p.t.E, p.t.counts, p.t.T, sp);
+  const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, (p.I + TL::TN - 1) / TL::TN, p.t.E, p.t.counts,
+                                          p.t.T, sp);
   if (!tt.ok) return;
   const bool shared = tt.g == p.t.E;
   const int e = shared ? 0 : tt.g;
   const int64_t arow0 = shared ? tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int H = p.H, I = p.I, last = tt.rows - 1;
-  const int n0 = tt.nt * BN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / TC::WN, wn = w % TC::WN;
-  Acc<BM> acc;
-  zero_acc<BM>(acc);
-  const bool active = wm * TC::WMR < tt.rows;
-  if (MX && !shared) {
+  const int n0 = tt.nt * TL::TN;
+  const int ncols = min(TL::TN, I - n0);   // the last N tile may be partial (a multiple of 128)
+  const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  Acc<TL> acc;
+  zero_acc<TL>(acc);
+  const bool active = wm * TL::WMR < tt.rows;
+  bool done = false;
+  if constexpr (MX) if (!shared) {
+    done = true;
     auto fa = [&](int r) { return p.mx.aq + (arow0 + min(r, last)) * H; };
     auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (H / 32); };
     auto fb = [&](int k) { return p.mx.b0.data.row(e, k) + n0; };
     auto fbs = [&](int kb) { return p.mx.b0.scale.row(e, kb) + n0; };
-    tile_mma<BM, KC, RC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active);
-  } else {
+    tile_mma<TL, KC, RC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb, ncols);
+  }
+  if (!done) {
     const uint16_t* abase = shared ? p.a_s : p.a_r;
     auto fa = [&](int r) { return abase + (arow0 + min(r, last)) * H; };
     const uint8_t* wb = shared ? p.sd.row(0, 0) : p.wd.row(e, 0);
     const int64_t wld = shared ? p.sd.ld_bytes : p.wd.ld_bytes;
     auto fb = [&](int k) { return wb + (int64_t)k * wld + 2 * n0; };
-    tile_mma<BM, KC, RC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active);
+    tile_mma<TL, KC, RC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb, ncols);
   }
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
+  if (wn * TL::WNC >= ncols) return;
 #pragma unroll
-  for (int i = 0; i < TC::MI; ++i)
+  for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < TC::NJ; ++j)
+    for (int j = 0; j < TL::NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<BM>(wm, i, r, lane);
-        if (row >= tt.rows) continue;
-        const int n = n0 + acc_col<BM>(wn, j, lane);
+        const int row = acc_row<TL>(wm, i, r, lane);
+        if (row >= tt.rows || acc_col<TL>(wn, j, lane) >= ncols) continue;
+        const int n = n0 + acc_col<TL>(wn, j, lane);
         const int64_t R = (crow0 + row) * 2 * (int64_t)I;
         const float a = bf2f(p.ab[R + n]);
         const float b = bf2f(p.ab[R + I + n]);
@@ -685,7 +818,7 @@ __global__ __launch_bounds__(NT, MINB_DG) void k_dgrad_swiglu(DgradSwigluArgs p)
 // Weight gradients: main_grad[e] (M x N, FP32) += A^T B over the expert's token rows
 // (both operands row-contiguous along M / N; K = the group's tokens).  M is made of
 // `parts` row ranges of `mpart` rows each (FC1: gate then up, FC2: one part), each
-// tiled by BMW with a masked tail, so no tile straddles two main_grad buffers.  Each
+// tiled by TM with a masked tail, so no tile straddles two main_grad buffers.  Each
 // output tile has exactly one owner: it loads its main_grad tile into the
 // accumulators, runs the full token loop, and stores once (no split-K, no atomics).
 // Shared-expert tiles come first in launch order (their K is all T tokens); routed
@@ -703,16 +836,16 @@ struct WgradArgs {
 };
 
 __host__ __device__ inline int wgrad_tiles_per_group(int parts, int mpart, int N) {
-  return parts * ((mpart + BMW - 1) / BMW) * (N / BN);
+  return parts * ((mpart + TL_WG::TM - 1) / TL_WG::TM) * (N / TL_WG::TN);
 }
-
-using WC = Cfg<BMW>;
 
 // FC is 1 or 2 (which projection's gradient); it only names the kernel symbol apart.
 template <int FC>
-__global__ __launch_bounds__(NT, MINB_W) void k_wgrad(WgradArgs p) {
-  __shared__ __align__(16) uint8_t lds[WC::LDS_BYTES];
-  const int mtp = (p.mpart + BMW - 1) / BMW, ntn = p.N / BN;
+__global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) {
+  using TL = TL_WG;
+  __shared__ __align__(16) uint8_t lds[TL::LDS];
+  __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
+  const int mtp = (p.mpart + TL::TM - 1) / TL::TM, ntn = p.N / TL::TN;
   const int per = p.parts * mtp * ntn;
   const int nshared = p.has_shared ? per : 0;
   int g, tile;
@@ -742,8 +875,8 @@ __global__ __launch_bounds__(NT, MINB_W) void k_wgrad(WgradArgs p) {
   const int sblk = rem / (sm * sn), sin = rem - sblk * sm * sn;
   const int sbn = ntn / sn;
   const int mt = (sblk / sbn) * sm + sin / sn, nt = (sblk % sbn) * sn + sin % sn;
-  const int m0 = mt * BMW, n0 = nt * BN;
-  const int mrows = min(BMW, p.mpart - m0);
+  const int m0 = mt * TL::TM, n0 = nt * TL::TN;
+  const int mrows = min(TL::TM, p.mpart - m0);
   const int64_t ar0 = shared ? p.a_s_row0 : (int64_t)p.offsets[g];
   const int64_t br0 = shared ? p.b_s_row0 : (int64_t)p.offsets[g];
   const uint16_t* A = (shared ? p.a_s : p.a_r) + (int64_t)part * p.mpart + m0;
@@ -756,49 +889,49 @@ __global__ __launch_bounds__(NT, MINB_W) void k_wgrad(WgradArgs p) {
   float* cb = G.row(e, m0) + n0;
   const int64_t ldc = G.ld;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / WC::WN, wn = w % WC::WN;
-  Acc<BMW> acc;
-  if (mrows == BMW) {   // full tile: unmasked main_grad read-modify-write
+  const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  Acc<TL> acc;
+  if (mrows == TL::TM) {   // full tile: unmasked main_grad read-modify-write
 #pragma unroll
-    for (int i = 0; i < WC::MI; ++i)
+    for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < WC::NJ; ++j)
+      for (int j = 0; j < TL::NJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = cb[acc_row<BMW>(wm, i, r, lane) * ldc + acc_col<BMW>(wn, j, lane)];
-    tile_mma<BMW, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, true, BMW);
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = cb[acc_row<TL>(wm, i, r, lane) * ldc + acc_col<TL>(wn, j, lane)];
+    tile_mma<TL, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, true, TL::TM, pfb);
 #pragma unroll
-    for (int i = 0; i < WC::MI; ++i)
+    for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < WC::NJ; ++j)
+      for (int j = 0; j < TL::NJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cb[acc_row<BMW>(wm, i, r, lane) * ldc + acc_col<BMW>(wn, j, lane)] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r) cb[acc_row<TL>(wm, i, r, lane) * ldc + acc_col<TL>(wn, j, lane)] = acc[i][j][r];
     return;
   }
-  const bool active = wm * WC::WMR < mrows;
-  zero_acc<BMW>(acc);
+  const bool active = wm * TL::WMR < mrows;
+  zero_acc<TL>(acc);
   if (active) {
 #pragma unroll
-    for (int i = 0; i < WC::MI; ++i)
+    for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < WC::NJ; ++j)
+      for (int j = 0; j < TL::NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<BMW>(wm, i, r, lane);
-          if (row < mrows) acc[i][j][r] = cb[row * ldc + acc_col<BMW>(wn, j, lane)];
+          const int row = acc_row<TL>(wm, i, r, lane);
+          if (row < mrows) acc[i][j][r] = cb[row * ldc + acc_col<TL>(wn, j, lane)];
         }
   }
 
-  tile_mma<BMW, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, active, mrows);
+  tile_mma<TL, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, active, mrows, pfb);
 
   if (!active) return;
 #pragma unroll
-  for (int i = 0; i < WC::MI; ++i)
+  for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < WC::NJ; ++j)
+    for (int j = 0; j < TL::NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<BMW>(wm, i, r, lane);
-        if (row < mrows) cb[row * ldc + acc_col<BMW>(wn, j, lane)] = acc[i][j][r];
+        const int row = acc_row<TL>(wm, i, r, lane);
+        if (row < mrows) cb[row * ldc + acc_col<TL>(wn, j, lane)] = acc[i][j][r];
       }
 }
 

@@ -289,8 +289,11 @@ moe_status launch(const char* name, hipStream_t st, F&& f) {
     if (_s != MOE_OK) return _s;          \
   } while (0)
 
+// Token rows per M tile of the token-dimension GEMMs (one value per routed-weight type).
+int64_t tok_bm(const Dims& d) { return d.mx ? gemm::bm_of<true>() : gemm::bm_of<false>(); }
 int64_t max_mtiles(const Dims& d) {
-  return (d.SM + gemm::BM - 1) / gemm::BM + d.E + (d.T + gemm::BM - 1) / gemm::BM;
+  const int64_t bm = tok_bm(d);
+  return (d.SM + bm - 1) / bm + d.E + (d.T + bm - 1) / bm;
 }
 unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
 
@@ -371,7 +374,7 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   }));
   MOE_TRY(launch("route_scan", st, [&] {
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, st, I32(L.chunk_counts), nch, E, T, 1,
-                       gemm::BM, I32(L.chunk_base), I32(L.counts), I32(L.offsets), I32(L.tile_prefix),
+                       (int)tok_bm(d), I32(L.chunk_base), I32(L.counts), I32(L.offsets), I32(L.tile_prefix),
                        I32(L.chunk_status), I32(L.status));
   }));
   if (T == 0) return MOE_OK;
@@ -418,9 +421,10 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
     a1.mx.b1 = mxref(w->routed_up, false);
   }
   MOE_TRY(launch("fc1_swiglu", st, [&] {
-    const dim3 g(grid8(mt * (I / 64)));
-    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, g, dim3(gemm::NT), 0, st, a1);
-    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, g, dim3(gemm::NT), 0, st, a1);
+    using S1 = gemm::Shapes<true>::FC1;
+    using S0 = gemm::Shapes<false>::FC1;
+    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, dim3(grid8(mt * (2 * I / S1::TN))), dim3(S1::NTH), 0, st, a1);
+    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, dim3(grid8(mt * (2 * I / S0::TN))), dim3(S0::NTH), 0, st, a1);
   }));
   if (d.mx) {   // Q: MXFP8 codes of the routed FC2 input h
     MOE_TRY(launch("quantize_h", st, [&] {
@@ -450,9 +454,10 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
     a2.mx.b1 = a2.mx.b0;
   }
   MOE_TRY(launch("fc2", st, [&] {
-    const dim3 g(grid8(mt * (H / gemm::BN)));
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), g, dim3(gemm::NT), 0, st, a2);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), g, dim3(gemm::NT), 0, st, a2);
+    using S1 = gemm::Shapes<true>::FC2;
+    using S0 = gemm::Shapes<false>::FC2;
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), dim3(grid8(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a2);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), dim3(grid8(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a2);
   }));
 
   // F7 combine
@@ -527,9 +532,10 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
     a3.mx.b1 = a3.mx.b0;
   }
   MOE_TRY(launch("dgrad_fc2_swiglu", st, [&] {
-    const dim3 g(grid8(mt * (I / gemm::BN)));
-    if (d.mx) hipLaunchKernelGGL(gemm::k_dgrad_swiglu<true>, g, dim3(gemm::NT), 0, st, a3);
-    else hipLaunchKernelGGL(gemm::k_dgrad_swiglu<false>, g, dim3(gemm::NT), 0, st, a3);
+    using S1 = gemm::Shapes<true>::DG2;
+    using S0 = gemm::Shapes<false>::DG2;
+    if (d.mx) hipLaunchKernelGGL(gemm::k_dgrad_swiglu<true>, dim3(grid8(mt * ((I + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a3);
+    else hipLaunchKernelGGL(gemm::k_dgrad_swiglu<false>, dim3(grid8(mt * ((I + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a3);
   }));
   if (d.mx) {   // Q: MXFP8 codes of the routed FC1 data-gradient input dfc1
     MOE_TRY(launch("quantize_dfc1", st, [&] {
@@ -559,9 +565,10 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
     a4.mx.b1 = mxref(w->routed_up, true);
   }
   MOE_TRY(launch("dgrad_fc1", st, [&] {
-    const dim3 g(grid8(mt * (H / gemm::BN)));
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, true>), g, dim3(gemm::NT), 0, st, a4);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, false>), g, dim3(gemm::NT), 0, st, a4);
+    using S1 = gemm::Shapes<true>::DG1;
+    using S0 = gemm::Shapes<false>::DG1;
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, true>), dim3(grid8(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a4);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, false>), dim3(grid8(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a4);
   }));
 
   // B7 dx combine
@@ -584,7 +591,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   {
     const int per = gemm::wgrad_tiles_per_group(1, H, I);
     MOE_TRY(launch("wgrad_fc2", st, [&] {
-      hipLaunchKernelGGL(gemm::k_wgrad<2>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a5);
+      hipLaunchKernelGGL(gemm::k_wgrad<2>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::TL_WG::NTH), 0, st, a5);
     }));
   }
 
@@ -602,7 +609,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   {
     const int per = gemm::wgrad_tiles_per_group(2, I, H);
     MOE_TRY(launch("wgrad_fc1", st, [&] {
-      hipLaunchKernelGGL(gemm::k_wgrad<1>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::NT), 0, st, a6);
+      hipLaunchKernelGGL(gemm::k_wgrad<1>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::TL_WG::NTH), 0, st, a6);
     }));
   }
   return MOE_OK;
