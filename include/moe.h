@@ -117,7 +117,10 @@ typedef struct {
   moe_weight shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
 } moe_weights;
 
-/* An FP32 main_grad buffer [rows][cols] per expert, same addressing as moe_mat. */
+/* An FP32 main_grad buffer [rows][cols] per expert, same addressing as moe_mat.
+ * Rows are read and written in 16-byte pieces: `base` (or every table entry) must be
+ * 16-byte aligned and `ld` and `expert_stride` multiples of 4 (MOE_ERR_LAYOUT
+ * otherwise; table entries live on the device and are not checked). */
 typedef struct {
   float* base;
   int64_t expert_stride;

@@ -516,16 +516,16 @@ struct MxOperands {
 // every token-dimension GEMM has the same M tile (the routing scan builds one tile
 // prefix for it).
 #ifndef MOE_TL_FC1
-#define MOE_TL_FC1 128, 256, 2, 2, 3, 2, 0, 64
+#define MOE_TL_FC1 256, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_FC2
-#define MOE_TL_FC2 128, 256, 2, 2, 3, 2, 0, 64
+#define MOE_TL_FC2 256, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_DG2
-#define MOE_TL_DG2 128, 256, 2, 2, 3, 2, 0, 64
+#define MOE_TL_DG2 256, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_DG1
-#define MOE_TL_DG1 128, 256, 2, 2, 3, 2, 0, 64
+#define MOE_TL_DG1 256, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_FC1_MX
 #define MOE_TL_FC1_MX 256, 256, 2, 4, 2, 1
@@ -540,7 +540,7 @@ struct MxOperands {
 #define MOE_TL_DG1_MX 256, 256, 2, 4, 2, 1, 2
 #endif
 #ifndef MOE_TL_WG
-#define MOE_TL_WG 128, 128, 2, 2, 2, 2
+#define MOE_TL_WG 128, 128, 2, 2, 2, 4, 0, 64
 #endif
 template <bool MX> struct Shapes;
 template <> struct Shapes<false> {
@@ -819,8 +819,8 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
 // (both operands row-contiguous along M / N; K = the group's tokens).  M is made of
 // `parts` row ranges of `mpart` rows each (FC1: gate then up, FC2: one part), each
 // tiled by TM with a masked tail, so no tile straddles two main_grad buffers.  Each
-// output tile has exactly one owner: it loads its main_grad tile into the
-// accumulators, runs the full token loop, and stores once (no split-K, no atomics).
+// output tile has exactly one owner: it runs the full token loop and then adds its
+// result to main_grad once (no split-K, no atomics).
 // Shared-expert tiles come first in launch order (their K is all T tokens); routed
 // tiles follow, chunked per XCD like the token-dim GEMMs.
 // ---------------------------------------------------------------------------------
@@ -891,48 +891,55 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
 
   const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
   Acc<TL> acc;
-  if (mrows == TL::TM) {   // full tile: unmasked main_grad read-modify-write
-#pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < TL::NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = cb[acc_row<TL>(wm, i, r, lane) * ldc + acc_col<TL>(wn, j, lane)];
-    tile_mma<TL, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, true, TL::TM, pfb);
-#pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < TL::NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cb[acc_row<TL>(wm, i, r, lane) * ldc + acc_col<TL>(wn, j, lane)] = acc[i][j][r];
-    return;
-  }
-  const bool active = wm * TL::WMR < mrows;
   zero_acc<TL>(acc);
-  if (active) {
-#pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < TL::NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<TL>(wm, i, r, lane);
-          if (row < mrows) acc[i][j][r] = cb[row * ldc + acc_col<TL>(wn, j, lane)];
-        }
-  }
-
+  const bool active = wm * TL::WMR < mrows;
   tile_mma<TL, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, active, mrows, pfb);
 
-  if (!active) return;
+  // main_grad += acc, one slice of WMR rows per round: the waves of wave row `rd` park
+  // their accumulators in LDS, then every thread adds 16-byte pieces of whole rows to
+  // main_grad (coalesced row reads and writes).  The main_grad loads of a round are
+  // issued before its LDS traffic.  LDS slice [WMR][TN] fp32; 16-byte chunk c of row r
+  // sits at c ^ 8 ((r >> 2) & 1), so the two row groups a wave writes at once use
+  // disjoint banks.
+  constexpr int CPRW = TL::TN / 4;                       // 16-byte chunks per row
+  constexpr int CPT = TL::WMR * CPRW / TL::NTH;          // chunks per thread per round
+  static_assert(TL::WMR * TL::TN * 4 <= TL::LDS && (TL::WMR * CPRW) % TL::NTH == 0, "epilogue slice");
+  float* ct = reinterpret_cast<float*>(lds);
+  const int t = threadIdx.x;
+  auto sw = [](int r) { return ((r >> 2) & 1) << 3; };
 #pragma unroll
-  for (int i = 0; i < TL::MI; ++i)
+  for (int rd = 0; rd < TL::NWM; ++rd) {
+    f32x4_t mg[CPT];
 #pragma unroll
-    for (int j = 0; j < TL::NJ; ++j)
+    for (int q = 0; q < CPT; ++q) {
+      const int c = q * TL::NTH + t, row = c / CPRW, cc = c % CPRW;
+      const int grow = rd * TL::WMR + row;
+      mg[q] = grow < mrows ? *reinterpret_cast<const f32x4_t*>(cb + grow * ldc + cc * 4) : f32x4_t{};
+    }
+    __syncthreads();   // the LDS slice is free (K loop or previous round done)
+    if (wm == rd) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<TL>(wm, i, r, lane);
-        if (row < mrows) cb[row * ldc + acc_col<TL>(wn, j, lane)] = acc[i][j][r];
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int col = acc_col<TL>(wn, j, lane);
+            ct[row * TL::TN + (((col >> 2) ^ sw(row)) << 2) + (col & 3)] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int c = q * TL::NTH + t, row = c / CPRW, cc = c % CPRW;
+      const int grow = rd * TL::WMR + row;
+      if (grow < mrows) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + row * TL::TN + ((cc ^ sw(row)) << 2));
+        *reinterpret_cast<f32x4_t*>(cb + grow * ldc + cc * 4) = mg[q] + v;
       }
+    }
+  }
 }
 
 }  // namespace gemm

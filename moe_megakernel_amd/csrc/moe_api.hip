@@ -193,6 +193,7 @@ moe_status check_grad(const moe_grad& g, int64_t cols, bool routed) {
   if (hb && ht) return MOE_ERR_LAYOUT;
   if (!routed && ht) return MOE_ERR_LAYOUT;
   if (g.ld < cols || g.row_offset < 0) return MOE_ERR_LAYOUT;
+  if (g.ld % 4 || (hb && (g.expert_stride % 4 || !aligned16(g.base)))) return MOE_ERR_LAYOUT;
   return MOE_OK;
 }
 
