@@ -138,3 +138,19 @@ def test_backward_validation_errors():
     assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 16, 0) == mk.MOE_ERR_WORKSPACE
     g.shared_down.ld = I - 1
     assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 1 << 30, 0) == mk.MOE_ERR_LAYOUT
+
+
+def test_main_grad_rows_must_be_16_byte_aligned():
+    p = _ok_problem()
+    w = _fake_weights(p)
+    a = 1 << 41
+    H, I = p.hidden, p.intermediate
+    G = lambda ld, ro=0, base=a, stride=0: mk.moe_grad(base, stride, 0, ld, ro)
+    ok = mk.moe_main_grads(G(H), G(H, I), G(I), G(H), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, ok, a, 16, 0) == mk.MOE_ERR_WORKSPACE   # layout accepted
+    bad_base = mk.moe_main_grads(G(H), G(H, I), G(I), G(H, 0, a + 4), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, bad_base, a, 1 << 30, 0) == mk.MOE_ERR_LAYOUT
+    bad_ld = mk.moe_main_grads(G(H), G(H, I), G(I + 2), G(H), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, bad_ld, a, 1 << 30, 0) == mk.MOE_ERR_LAYOUT
+    bad_stride = mk.moe_main_grads(G(H), G(H, I), G(I), G(H), G(H, I), G(I, 0, a, I * H + 2))
+    assert mk.moe_backward(p, a, a, w, a, a, a, bad_stride, a, 1 << 30, 0) == mk.MOE_ERR_LAYOUT
