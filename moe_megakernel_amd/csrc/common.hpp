@@ -50,21 +50,6 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)w;
 }
 
-// 32 floats of one block -> 32 E4M3 codes (two uint4) and the E8M0 scale byte.
-__device__ __forceinline__ uint32_t mx_quantize32(const float (&v)[32], uint4& q0, uint4& q1) {
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int e = mx_block_exp(amax);
-  const float inv = ldexpf(1.0f, -e);
-  uint32_t w[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = pack_e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
-  q0 = make_uint4(w[0], w[1], w[2], w[3]);
-  q1 = make_uint4(w[4], w[5], w[6], w[7]);
-  return (uint32_t)(e + 127);
-}
-
 __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
   f[0] = lo_bf(v.x); f[1] = hi_bf(v.x); f[2] = lo_bf(v.y); f[3] = hi_bf(v.y);
   f[4] = lo_bf(v.z); f[5] = hi_bf(v.z); f[6] = lo_bf(v.w); f[7] = hi_bf(v.w);

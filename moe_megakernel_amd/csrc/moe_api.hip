@@ -374,13 +374,13 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
                          I32(L.top), F32(L.rw), I32(L.chunk_counts), I32(L.chunk_status));
   }));
   MOE_TRY(launch("route_scan", st, [&] {
-    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(256), 0, st, I32(L.chunk_counts), nch, E, T, 1,
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, I32(L.chunk_counts), nch, E, T, 1,
                        (int)tok_bm(d), I32(L.chunk_base), I32(L.counts), I32(L.offsets), I32(L.tile_prefix),
                        I32(L.chunk_status), I32(L.status));
   }));
   if (T == 0) return MOE_OK;
   MOE_TRY(launch("route_rank", st, [&] {
-    hipLaunchKernelGGL(k_route_rank, dim3(nch), dim3(256), 0, st, I32(L.top), F32(L.rw), T, E, K,
+    hipLaunchKernelGGL(k_route_rank, dim3(nch), dim3(kRouteChunk * kMaxTopk), 0, st, I32(L.top), F32(L.rw), T, E, K,
                        I32(L.chunk_base), I32(L.offsets), I32(L.slot_of), I32(L.slot_token), F32(L.slot_w));
   }));
   // F3 dispatch gather (+ Q: MXFP8 codes of the routed FC1 input)

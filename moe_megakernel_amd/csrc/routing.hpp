@@ -7,16 +7,23 @@
 // route (0 at -1).  Dispatch on one GPU is a permutation: routes are grouped by
 // expert, and inside an expert's segment ordered by ascending token, which makes
 // the permutation unique.
+//
+// Work is split into chunks of kRouteChunk tokens: compaction writes each chunk's
+// expert histogram, one scan turns the histograms into per-chunk bases and the
+// expert offsets, and ranking places each route at offsets[e] + chunk base + its
+// rank among the chunk's earlier routes to e.
 #pragma once
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kRouteChunk = 256;   // tokens per block (4 waves of 64)
+constexpr int kRouteChunk = 32;       // tokens per chunk (one compaction block)
+constexpr int kRouteTokPerWave = 8;   // compaction: tokens per wave (4 waves per block)
 
-// Kernel 1: one thread per token.  Writes the fixed-width table and the
-// per-chunk expert histogram (integer LDS atomics: the counts do not depend
-// on the order of the additions).
+// Kernel 1: one wave per 8 tokens, a token's row read by the whole wave (lane l looks
+// at experts 4l .. 4l + 3).  Positions in the ascending ID list come from per-byte
+// ballots; the chunk histogram is built with integer LDS atomics (the counts do not
+// depend on the order of the additions).
 __global__ __launch_bounds__(256) void k_route_compact(
     const uint8_t* __restrict__ rmap, const float* __restrict__ probs, int T, int E, int K,
     int32_t* __restrict__ top, float* __restrict__ rw, int32_t* __restrict__ chunk_counts,
@@ -26,144 +33,179 @@ __global__ __launch_bounds__(256) void k_route_compact(
   if (threadIdx.x == 0) overflow = 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  const int t = blockIdx.x * kRouteChunk + threadIdx.x;
-  if (t < T) {
-    const uint8_t* row = rmap + (int64_t)t * E;
-    const float* prow = probs + (int64_t)t * E;
-    int n = 0;
-    auto take = [&](int e) {
-      if (n < K) {
-        top[(int64_t)t * K + n] = e;
-        rw[(int64_t)t * K + n] = prow[e];     // probs are read only where the map is set
-        atomicAdd(&cnt[e], 1);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRouteChunk + w * kRouteTokPerWave;
+  const int e0 = 4 * lane;
+  const bool word = (E & 3) == 0;   // rows are then 4-byte aligned
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // all map words of the wave's tokens first (independent loads)
+  uint32_t m[kRouteTokPerWave];
+#pragma unroll
+  for (int i = 0; i < kRouteTokPerWave; ++i) {
+    const int t = t0 + i;
+    uint32_t bits = 0;
+    if (t < T && e0 < E) {
+      const uint8_t* row = rmap + (int64_t)t * E + e0;
+      if (word) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(row);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bits |= ((v >> (8 * j)) & 0xffu) ? (1u << j) : 0u;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (e0 + j < E && row[j]) bits |= 1u << j;
       }
-      ++n;
-    };
-    if ((E & 15) == 0 && ((reinterpret_cast<uintptr_t>(row) & 15) == 0)) {
-      // the whole row (E <= 256 bytes) is loaded with independent 16-byte loads first
-      uint4 r16[16];
-      const uint4* src = reinterpret_cast<const uint4*>(row);
+    }
+    m[i] = bits;
+  }
+  // positions, then the probability loads of every listed route, then the stores
+  int pos[kRouteTokPerWave], n[kRouteTokPerWave];
+  float pr[kRouteTokPerWave][4];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) r16[q] = (q < (E >> 4)) ? src[q] : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kRouteTokPerWave; ++i) {
+    int before = 0, total = 0;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const uint32_t w4[4] = {r16[q].x, r16[q].y, r16[q].z, r16[q].w};
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t b = __ballot((m[i] >> j) & 1u);
+      before += __popcll(b & lt);
+      total += __popcll(b);
+    }
+    pos[i] = before;
+    n[i] = total;
+    const int t = t0 + i;
+    int p = before;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t v = w4[d];
-          if (!v) continue;
+    for (int j = 0; j < 4; ++j) {
+      pr[i][j] = 0.0f;
+      if ((m[i] >> j) & 1u) {
+        if (p < K) pr[i][j] = probs[(int64_t)t * E + e0 + j];   // read only where the map is set
+        ++p;
+      }
+    }
+  }
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if ((v >> (8 * b)) & 0xffu) take(16 * q + 4 * d + b);
+  for (int i = 0; i < kRouteTokPerWave; ++i) {
+    const int t = t0 + i;
+    if (t >= T) break;
+    int p = pos[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if ((m[i] >> j) & 1u) {
+        if (p < K) {
+          top[(int64_t)t * K + p] = e0 + j;
+          rw[(int64_t)t * K + p] = pr[i][j];
+          atomicAdd(&cnt[e0 + j], 1);
         }
+        ++p;
       }
-    } else {
-      for (int e = 0; e < E; ++e)
-        if (row[e]) take(e);
     }
-    for (int k = n; k < K; ++k) {
-      top[(int64_t)t * K + k] = -1;
-      rw[(int64_t)t * K + k] = 0.0f;
+    if (lane >= n[i] && lane < K) {
+      top[(int64_t)t * K + lane] = -1;
+      rw[(int64_t)t * K + lane] = 0.0f;
     }
-    if (n > K) overflow = 1;     // benign race: every writer stores the same value
+    if (lane == 0 && n[i] > K) overflow = 1;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
   if (threadIdx.x == 0) chunk_status[blockIdx.x] = overflow ? 7 /* MOE_ERR_ROUTE_OVERFLOW */ : 0;
 }
 
-// Kernel 2: one block of 256 threads.  Per expert: running sum over chunks
-// (chunk base offsets) -> counts; exclusive scan over experts -> offsets;
-// and the prefix over groups of ceil(rows / BM) used by the token-dim GEMMs
-// (group E is the shared expert with T rows when present).  Also folds the
-// per-chunk overflow flags into the status word.
-__global__ __launch_bounds__(256) void k_route_scan(
+// Kernel 2: one block of 1024 threads.  Thread (s, e) owns expert e's chunks of segment
+// s (segments of ceil(nchunks / S) consecutive chunks, S = 1024 / 256 = 4 or more): it
+// sums them, the segment sums are scanned in LDS, and a second pass over the segment
+// writes each chunk's base (routes to e in earlier chunks).  Then counts, the exclusive
+// scan over experts (offsets), and the prefix over groups of ceil(rows / BM) used by the
+// token-dimension GEMMs (group E is the shared expert with T rows when present).  Also
+// folds the per-chunk overflow flags into the status word.
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void k_route_scan(
     const int32_t* __restrict__ chunk_counts, int nchunks, int E, int T, int has_shared, int BM,
     int32_t* __restrict__ chunk_base, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_prefix, const int32_t* __restrict__ chunk_status,
     int32_t* __restrict__ status) {
-  __shared__ int s[256];
-  __shared__ int u[256];
+  __shared__ int seg[kScanThreads];
+  __shared__ int s_tot[256];
+  __shared__ int s_til[256];
   __shared__ int flag;
-  const int e = threadIdx.x;
-  if (e == 0) flag = 0;
+  const int tid = threadIdx.x;
+  int ep = 1;
+  while (ep < E) ep <<= 1;                       // experts padded to a power of two (<= 256)
+  const int S = kScanThreads / ep;               // segments per expert
+  const int e = tid % ep, s = tid / ep;
+  const int L = (nchunks + S - 1) / S;
+  const int c0 = s * L, c1 = min(c0 + L, nchunks);
+  if (tid == 0) flag = 0;
   __syncthreads();
-  for (int c = e; c < nchunks; c += 256)
+  for (int c = tid; c < nchunks; c += kScanThreads)
     if (chunk_status[c]) flag = chunk_status[c];
-  int total = 0;
+  int sum = 0;
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_counts[(int64_t)c * E + e];
-      chunk_base[(int64_t)c * E + e] = total;
-      total += v;
-    }
-    counts[e] = total;
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) sum += chunk_counts[(int64_t)c * E + e];
   }
-  const int groups = E + (has_shared ? 1 : 0);
-  int rows = (e < E) ? total : ((e == E && has_shared) ? T : 0);
-  s[e] = (e < E) ? total : 0;
-  u[e] = (e < groups) ? (rows + BM - 1) / BM : 0;
+  seg[tid] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int q = 0; q < s; ++q) run += seg[q * ep + e];
+  if (e < E) {
+    for (int c = c0; c < c1; ++c) {
+      const int v = chunk_counts[(int64_t)c * E + e];
+      chunk_base[(int64_t)c * E + e] = run;
+      run += v;
+    }
+    if (s == S - 1) counts[e] = run;
+  }
+  // totals per expert -> offsets and tile prefix (first 256 threads)
+  if (s == S - 1 && e < E) s_tot[e] = run;
+  __syncthreads();
+  if (tid < 256) {
+    const int groups = E + (has_shared ? 1 : 0);
+    const int total = tid < E ? s_tot[tid] : 0;
+    const int rows = tid < E ? total : ((tid == E && has_shared) ? T : 0);
+    s_tot[tid] = total;
+    s_til[tid] = tid < groups ? (rows + BM - 1) / BM : 0;
+  }
   __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {      // inclusive Hillis-Steele scans
-    const int a = (e >= d) ? s[e - d] : 0;
-    const int b = (e >= d) ? u[e - d] : 0;
+    int a = 0, b = 0;
+    if (tid < 256 && tid >= d) { a = s_tot[tid - d]; b = s_til[tid - d]; }
     __syncthreads();
-    s[e] += a;
-    u[e] += b;
+    if (tid < 256) { s_tot[tid] += a; s_til[tid] += b; }
     __syncthreads();
   }
-  if (e == 0) { offsets[0] = 0; tile_prefix[0] = 0; *status = flag; }
-  if (e < E) offsets[e + 1] = s[e];
-  if (e < groups) tile_prefix[e + 1] = u[e];
+  if (tid == 0) { offsets[0] = 0; tile_prefix[0] = 0; *status = flag; }
+  const int groups = E + (has_shared ? 1 : 0);
+  if (tid < E) offsets[tid + 1] = s_tot[tid];
+  if (tid < groups) tile_prefix[tid + 1] = s_til[tid];
 }
 
-// Kernel 3: one thread per token.  Rank of each route inside its expert's
-// segment = routes of earlier chunks (chunk_base) + earlier waves of this
-// chunk + earlier lanes of this wave (ballot prefix), all by ascending token.
-__global__ __launch_bounds__(256) void k_route_rank(
+// Kernel 3: one block per chunk, thread (i, k) for the chunk's token i and route k.  Its
+// rank inside expert e's segment = chunk base + the routes to e of the chunk's earlier
+// tokens (a token lists an expert at most once), counted against the chunk's table in LDS.
+__global__ __launch_bounds__(kRouteChunk * kMaxTopk) void k_route_rank(
     const int32_t* __restrict__ top, const float* __restrict__ rw, int T, int E, int K,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ slot_of, int32_t* __restrict__ slot_token, float* __restrict__ slot_w) {
-  __shared__ int wcnt[4][kMaxExperts + 1];
-  const int t = blockIdx.x * kRouteChunk + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  int my[kMaxTopk];
-  int pre[kMaxTopk];
-#pragma unroll
-  for (int k = 0; k < kMaxTopk; ++k) {
-    my[k] = (t < T && k < K) ? top[(int64_t)t * K + k] : -1;
-    pre[k] = 0;
-  }
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = 0; e < E; ++e) {
-    bool pred = false;
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) pred |= (my[k] == e);
-    const uint64_t mask = __ballot(pred);
-    const int p = __popcll(mask & lt);
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k)
-      if (my[k] == e) pre[k] = p;
-    if (lane == 0) wcnt[w][e] = __popcll(mask);
-  }
+  __shared__ int tab[kRouteChunk * kMaxTopk];
+  const int tid = threadIdx.x;
+  const int tb = blockIdx.x * kRouteChunk;
+  const int n = min(kRouteChunk, T - tb) * K;   // routes of this chunk
+  const int e = tid < n ? top[(int64_t)tb * K + tid] : -1;
+  tab[tid] = e;
   __syncthreads();
-  if (t >= T) return;
-#pragma unroll
-  for (int k = 0; k < kMaxTopk; ++k) {
-    if (k >= K) break;
-    const int e = my[k];
-    if (e < 0) {
-      slot_of[(int64_t)t * K + k] = -1;
-      continue;
-    }
-    int r = chunk_base[(int64_t)blockIdx.x * E + e] + pre[k];
-    for (int v = 0; v < w; ++v) r += wcnt[v][e];
-    const int s = offsets[e] + r;
-    slot_of[(int64_t)t * K + k] = s;
-    slot_token[s] = t * K + k;
-    slot_w[s] = rw[(int64_t)t * K + k];
+  if (tid >= n) return;
+  const int i = tid / K;
+  if (e < 0) {
+    slot_of[(int64_t)tb * K + tid] = -1;
+    return;
   }
+  int r = chunk_base[(int64_t)blockIdx.x * E + e];
+  for (int q = 0; q < i * K; ++q) r += (tab[q] == e) ? 1 : 0;
+  const int s = offsets[e] + r;
+  slot_of[(int64_t)tb * K + tid] = s;
+  slot_token[s] = tb * K + tid;
+  slot_w[s] = rw[(int64_t)tb * K + tid];
 }
 
 }  // namespace moe

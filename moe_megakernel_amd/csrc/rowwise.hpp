@@ -1,7 +1,11 @@
 // Per-token row kernels: dispatch gather, probability-weighted combine, the
 // backward's weighted gather of dy fused with the router-probability gradient,
-// and the data-gradient combine.  All are HBM-bound row copies/reductions with
-// 16-byte accesses; every sum runs in a fixed order (no float atomics).
+// and the data-gradient combine.  All are HBM-bound row copies/reductions: each
+// thread moves 16-byte pieces (8 bf16) of a row, and the loads of two pieces are in
+// flight together.  Every sum runs in a fixed order (no float atomics).  With MXFP8
+// output, the 4 lanes holding one 32-element block agree on its E8M0 exponent through
+// two cross-lane max steps (a row's piece c sits on lane c % 64 of its wave, and
+// H is a multiple of 32, so a block's 4 pieces are 4 consecutive lanes).
 #pragma once
 #include "common.hpp"
 
@@ -15,9 +19,38 @@ __device__ __forceinline__ void load_slots(const int32_t* __restrict__ slot_of, 
   for (int k = 0; k < kMaxTopk; ++k) s[k] = (k < K) ? slot_of[(int64_t)t * K + k] : -1;
 }
 
+// Max over the 4 lanes 4q .. 4q + 3 (one 32-element MX block).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  return fmaxf(v, __shfl_xor(v, 2));
+}
+
+// 8 floats of a 32-element block whose |max| is amax -> 8 E4M3 codes; returns the E8M0 byte.
+__device__ __forceinline__ uint32_t mx_quantize8(const float (&v)[8], float amax, uint2& q) {
+  const int e = mx_block_exp(amax);
+  const float inv = ldexpf(1.0f, -e);
+  q.x = pack_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  q.y = pack_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  return (uint32_t)(e + 127);
+}
+
+__device__ __forceinline__ float absmax8(const float (&v)[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+__device__ __forceinline__ uint4 pack_bf8(const float (&a)[8]) {
+  uint4 o;
+  o.x = pack_bf2(a[0], a[1]); o.y = pack_bf2(a[2], a[3]);
+  o.z = pack_bf2(a[4], a[5]); o.w = pack_bf2(a[6], a[7]);
+  return o;
+}
+
 // xp[slot_of[t,k]] = x[t] for every valid route (dispatch into expert-contiguous rows).
 // With Q, the row is also quantised to MXFP8 along H (one E8M0 scale per 32 elements)
-// into xq / xs, the A operand of the scaled-FP8 FC1.  One thread per 32-element block.
+// into xq / xs, the A operand of the scaled-FP8 FC1.  One block per token.
 template <bool Q>
 __global__ __launch_bounds__(kRowThreads) void k_gather_rows(
     const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ slot_of,
@@ -26,29 +59,33 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_rows(
   int s[kMaxTopk];
   load_slots(slot_of, t, K, s);
   const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
-  for (int c = threadIdx.x; c < H / 32; c += kRowThreads) {
-    uint4 v[4];
+  const int nc = H / 8;
+  for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
+    uint4 v[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = src[4 * c + q];
-    uint4 q0, q1;
-    uint32_t sc = 0;
-    if constexpr (Q) {
-      float f[32];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) unpack_bf16x8(v[q], f + 8 * q);
-      sc = mx_quantize32(f, q0, q1);
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c < nc) v[u] = src[c];
     }
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-      if (s[k] < 0) continue;
-      uint4* dst = reinterpret_cast<uint4*>(xp + (int64_t)s[k] * H) + 4 * c;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = v[q];
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c >= nc) break;
+      uint2 q = make_uint2(0, 0);
+      uint32_t sc = 0;
       if constexpr (Q) {
-        uint4* dq = reinterpret_cast<uint4*>(xq + (int64_t)s[k] * H) + 2 * c;
-        dq[0] = q0;
-        dq[1] = q1;
-        xs[(int64_t)s[k] * (H / 32) + c] = (uint8_t)sc;
+        float f[8];
+        unpack_bf16x8(v[u], f);
+        sc = mx_quantize8(f, quad_max(absmax8(f)), q);
+      }
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) {
+        if (s[k] < 0) continue;
+        reinterpret_cast<uint4*>(xp + (int64_t)s[k] * H)[c] = v[u];
+        if constexpr (Q) {
+          reinterpret_cast<uint2*>(xq + (int64_t)s[k] * H)[c] = q;
+          if ((c & 3) == 0) xs[(int64_t)s[k] * (H / 32) + (c >> 2)] = (uint8_t)sc;
+        }
       }
     }
   }
@@ -56,26 +93,22 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_rows(
 
 // MXFP8 quantisation of bf16 rows along their length: payload [rows][cols] E4M3 and
 // scales [rows][cols/32] E8M0.  Rows at or beyond *row_limit (when given) are skipped:
-// the routed buffers hold offsets[E] valid rows.  One thread per 32-element block.
+// the routed buffers hold offsets[E] valid rows.  One thread per 16-byte piece.
 __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
     const uint16_t* __restrict__ in, int64_t rows, int cols, const int32_t* __restrict__ row_limit,
     uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
-  const int64_t nb = (int64_t)cols / 32;
+  const int64_t nc = (int64_t)cols / 8;
   const int64_t lim = row_limit ? (int64_t)*row_limit : rows;
-  const int64_t total = (lim < rows ? lim : rows) * nb;
+  const int64_t total = (lim < rows ? lim : rows) * nc;
+  // the stride is a multiple of 4 pieces, so a block's 4 pieces stay on 4 adjacent lanes
   for (int64_t b = (int64_t)blockIdx.x * kRowThreads + threadIdx.x; b < total;
        b += (int64_t)gridDim.x * kRowThreads) {
-    const int64_t r = b / nb, c = b - r * nb;
-    const uint4* src = reinterpret_cast<const uint4*>(in + r * cols) + 4 * c;
-    float f[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) unpack_bf16x8(src[i], f + 8 * i);
-    uint4 q0, q1;
-    const uint32_t s = mx_quantize32(f, q0, q1);
-    uint4* dq = reinterpret_cast<uint4*>(q + r * cols) + 2 * c;
-    dq[0] = q0;
-    dq[1] = q1;
-    sc[r * nb + c] = (uint8_t)s;
+    float f[8];
+    unpack_bf16x8(reinterpret_cast<const uint4*>(in)[b], f);
+    uint2 code;
+    const uint32_t s = mx_quantize8(f, quad_max(absmax8(f)), code);
+    reinterpret_cast<uint2*>(q)[b] = code;
+    if ((b & 3) == 0) sc[b >> 2] = (uint8_t)s;
   }
 }
 
@@ -91,23 +124,34 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
 #pragma unroll
   for (int k = 0; k < kMaxTopk; ++k) w[k] = (s[k] >= 0) ? rw[(int64_t)t * K + k] : 0.0f;
   const uint4* ys = reinterpret_cast<const uint4*>(y + (shared_row0 + t) * (int64_t)H);
-  for (int c = threadIdx.x; c < H / 8; c += kRowThreads) {
-    const uint4 v = ys[c];
-    float a[8] = {lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y),
-                  lo_bf(v.z), hi_bf(v.z), lo_bf(v.w), hi_bf(v.w)};
+  const int nc = H / 8;
+  for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
+    uint4 v[2], r[2][kMaxTopk];
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-      if (s[k] < 0) continue;
-      const uint4 r = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H)[c];
-      a[0] += w[k] * lo_bf(r.x); a[1] += w[k] * hi_bf(r.x);
-      a[2] += w[k] * lo_bf(r.y); a[3] += w[k] * hi_bf(r.y);
-      a[4] += w[k] * lo_bf(r.z); a[5] += w[k] * hi_bf(r.z);
-      a[6] += w[k] * lo_bf(r.w); a[7] += w[k] * hi_bf(r.w);
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c >= nc) break;
+      v[u] = ys[c];
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k)
+        if (s[k] >= 0) r[u][k] = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H)[c];
     }
-    uint4 o;
-    o.x = pack_bf2(a[0], a[1]); o.y = pack_bf2(a[2], a[3]);
-    o.z = pack_bf2(a[4], a[5]); o.w = pack_bf2(a[6], a[7]);
-    reinterpret_cast<uint4*>(out + (int64_t)t * H)[c] = o;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c >= nc) break;
+      float a[8];
+      unpack_bf16x8(v[u], a);
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) {
+        if (s[k] < 0) continue;
+        float b[8];
+        unpack_bf16x8(r[u][k], b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] += w[k] * b[i];
+      }
+      reinterpret_cast<uint4*>(out + (int64_t)t * H)[c] = pack_bf8(a);
+    }
   }
 }
 
@@ -115,17 +159,19 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
 // routed expert's upstream gradient), and the router-probability gradient
 // dprobs[t, e_tk] = dy[t] . y[slot] (y is the unweighted expert output), written
 // into the dense [T][E] row with zeros off the map.  The dot products are
-// reduced per thread in a fixed order and then by a fixed LDS tree.  With Q,
-// w_tk * dy[t] is also quantised to MXFP8 along H (the A operand of the
-// scaled-FP8 data-gradient GEMM).  One thread per 32-element block.
+// reduced per thread in a fixed order, then across each wave by a fixed butterfly,
+// then across the waves in order.  With Q, w_tk * dy[t] is also quantised to MXFP8
+// along H (the A operand of the scaled-FP8 data-gradient GEMM).  One block per token.
 template <bool Q>
 __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y, int H, int E, int K,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ top,
     const float* __restrict__ rw, uint16_t* __restrict__ dyw, float* __restrict__ dprobs,
     uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys) {
-  __shared__ float red[kMaxTopk][kRowThreads];
+  __shared__ float red[kRowThreads / 64][kMaxTopk];
+  __shared__ float dp[kMaxTopk];
   const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int s[kMaxTopk];
   load_slots(slot_of, t, K, s);
   float w[kMaxTopk], part[kMaxTopk];
@@ -135,56 +181,66 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     part[k] = 0.0f;
   }
   const uint4* src = reinterpret_cast<const uint4*>(dy + (int64_t)t * H);
-  for (int c = threadIdx.x; c < H / 32; c += kRowThreads) {
-    float g[32];
+  const int nc = H / 8;
+  for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
+    uint4 g4[2], y4[2][kMaxTopk];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) unpack_bf16x8(src[4 * c + q], g + 8 * q);
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c >= nc) break;
+      g4[u] = src[c];
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-      if (s[k] < 0) continue;
-      const uint4* yr = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H) + 4 * c;
-      float d = 0.0f;
+      for (int k = 0; k < kMaxTopk; ++k)
+        if (s[k] >= 0) y4[u][k] = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H)[c];
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c >= nc) break;
+      float g[8];
+      unpack_bf16x8(g4[u], g);
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) {
+        if (s[k] < 0) continue;
         float yv[8];
-        unpack_bf16x8(yr[q], yv);
+        unpack_bf16x8(y4[u][k], yv);
+        float d = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d += g[8 * q + i] * yv[i];
-      }
-      part[k] += d;
-      float wg[32];
+        for (int i = 0; i < 8; ++i) d += g[i] * yv[i];
+        part[k] += d;
+        float wg[8];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) wg[i] = w[k] * g[i];
-      uint4* dst = reinterpret_cast<uint4*>(dyw + (int64_t)s[k] * H) + 4 * c;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[q] = make_uint4(pack_bf2(wg[8 * q], wg[8 * q + 1]), pack_bf2(wg[8 * q + 2], wg[8 * q + 3]),
-                            pack_bf2(wg[8 * q + 4], wg[8 * q + 5]), pack_bf2(wg[8 * q + 6], wg[8 * q + 7]));
-      if constexpr (Q) {
-        uint4 q0, q1;
-        const uint32_t sc = mx_quantize32(wg, q0, q1);
-        uint4* dq = reinterpret_cast<uint4*>(dyq + (int64_t)s[k] * H) + 2 * c;
-        dq[0] = q0;
-        dq[1] = q1;
-        dys[(int64_t)s[k] * (H / 32) + c] = (uint8_t)sc;
+        for (int i = 0; i < 8; ++i) wg[i] = w[k] * g[i];
+        reinterpret_cast<uint4*>(dyw + (int64_t)s[k] * H)[c] = pack_bf8(wg);
+        if constexpr (Q) {
+          uint2 q;
+          const uint32_t sc = mx_quantize8(wg, quad_max(absmax8(wg)), q);
+          reinterpret_cast<uint2*>(dyq + (int64_t)s[k] * H)[c] = q;
+          if ((c & 3) == 0) dys[(int64_t)s[k] * (H / 32) + (c >> 2)] = (uint8_t)sc;
+        }
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < kMaxTopk; ++k) red[k][threadIdx.x] = part[k];
+  for (int k = 0; k < kMaxTopk; ++k) {
+    float v = part[k];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wv][k] = v;
+  }
   __syncthreads();
-  for (int d = kRowThreads / 2; d > 0; d >>= 1) {
-    if (threadIdx.x < d) {
+  if (threadIdx.x < kMaxTopk) {
+    float v = 0.0f;
 #pragma unroll
-      for (int k = 0; k < kMaxTopk; ++k) red[k][threadIdx.x] += red[k][threadIdx.x + d];
-    }
-    __syncthreads();
+    for (int q = 0; q < kRowThreads / 64; ++q) v += red[q][threadIdx.x];
+    dp[threadIdx.x] = v;
   }
+  __syncthreads();
   for (int e = threadIdx.x; e < E; e += kRowThreads) {
     float v = 0.0f;
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k)
-      if (k < K && s[k] >= 0 && top[(int64_t)t * K + k] == e) v = red[k][0];
+      if (k < K && s[k] >= 0 && top[(int64_t)t * K + k] == e) v = dp[k];
     dprobs[(int64_t)t * E + e] = v;
   }
 }
@@ -197,21 +253,34 @@ __global__ __launch_bounds__(kRowThreads) void k_dx_combine(
   int s[kMaxTopk];
   load_slots(slot_of, t, K, s);
   const uint4* src = reinterpret_cast<const uint4*>(dxp + (shared_row0 + t) * (int64_t)H);
-  for (int c = threadIdx.x; c < H / 8; c += kRowThreads) {
-    const uint4 v = src[c];
-    float a[8] = {lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y),
-                  lo_bf(v.z), hi_bf(v.z), lo_bf(v.w), hi_bf(v.w)};
+  const int nc = H / 8;
+  for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
+    uint4 v[2], r[2][kMaxTopk];
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-      if (s[k] < 0) continue;
-      const uint4 r = reinterpret_cast<const uint4*>(dxp + (int64_t)s[k] * H)[c];
-      a[0] += lo_bf(r.x); a[1] += hi_bf(r.x); a[2] += lo_bf(r.y); a[3] += hi_bf(r.y);
-      a[4] += lo_bf(r.z); a[5] += hi_bf(r.z); a[6] += lo_bf(r.w); a[7] += hi_bf(r.w);
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c >= nc) break;
+      v[u] = src[c];
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k)
+        if (s[k] >= 0) r[u][k] = reinterpret_cast<const uint4*>(dxp + (int64_t)s[k] * H)[c];
     }
-    uint4 o;
-    o.x = pack_bf2(a[0], a[1]); o.y = pack_bf2(a[2], a[3]);
-    o.z = pack_bf2(a[4], a[5]); o.w = pack_bf2(a[6], a[7]);
-    reinterpret_cast<uint4*>(dx + (int64_t)t * H)[c] = o;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u * kRowThreads;
+      if (c >= nc) break;
+      float a[8];
+      unpack_bf16x8(v[u], a);
+#pragma unroll
+      for (int k = 0; k < kMaxTopk; ++k) {
+        if (s[k] < 0) continue;
+        float b[8];
+        unpack_bf16x8(r[u][k], b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] += b[i];
+      }
+      reinterpret_cast<uint4*>(dx + (int64_t)t * H)[c] = pack_bf8(a);
+    }
   }
 }
 
