@@ -115,6 +115,7 @@ struct NoScale {
 // acc[i][j] (wave rows wm*WMR + 32 i, columns wn*WNC + 32 j) += A[TM x K] * B[TN x K]^T.
 //  KC operand: fa(r) / fb(r) -> bytes of tile row r at K = 0 (callers clamp rows past
 //              the end to a valid row; the result rows they feed are never stored).
+//              A rows at or past acols are loaded from the zero page instead.
 //  RC operand: fa(k) / fb(k) -> bytes of element (k, tile row 0); called for k < kdim.
 //              acols / bcols: tile rows of a row-contiguous A / B that exist (a multiple
 //              of 8); the 16-byte pieces past them come from the zero page instead.
@@ -150,7 +151,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     const int off = (w * TL::A_DMA + i) * 1024 + 16 * lane;
     if constexpr (AM == KC) {
       const int r = off / KB, c = ((off % KB) >> 4) ^ swz_kc<KB>(r);
-      pa[i] = reinterpret_cast<const uint8_t*>(fa(r)) + 16 * c;
+      pa[i] = r < acols ? reinterpret_cast<const uint8_t*>(fa(r)) + 16 * c : nullptr;   // nullptr: zero page
       ka[i] = ca[i] = 0;
     } else {
       const int k = off / RBA, c = ((off % RBA) >> 4) ^ swz_rc16(k);
@@ -202,7 +203,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       const uint8_t* src = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
       if (line < TL::TM) {
         if constexpr (AM == KC) {
-          src = reinterpret_cast<const uint8_t*>(fa(line)) + kt * 128;
+          if (line < acols) src = reinterpret_cast<const uint8_t*>(fa(line)) + kt * 128;
         } else {
           const int k = kt * KST + line / (RBA / 128);
           if (k < kdim && 128 * (line % (RBA / 128)) < acols * EB)
@@ -229,7 +230,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     for (int i = 0; i < TL::A_DMA; ++i) {
       const uint32_t m0v = sa + (w * TL::A_DMA + i) * 1024;
       if constexpr (AM == KC) {
-        dma16(pa[i] + kt * KB, m0v);
+        dma16(pa[i] ? pa[i] + kt * KB : zp, m0v);
       } else {
         const int k = k0 + ka[i];
         dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fa(k)) + ca[i] : zp, m0v);
@@ -516,28 +517,28 @@ struct MxOperands {
 // every token-dimension GEMM has the same M tile (the routing scan builds one tile
 // prefix for it).
 #ifndef MOE_TL_FC1
-#define MOE_TL_FC1 256, 256, 2, 4, 2, 1
+#define MOE_TL_FC1 192, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_FC2
-#define MOE_TL_FC2 256, 256, 2, 4, 2, 1
+#define MOE_TL_FC2 192, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_DG2
-#define MOE_TL_DG2 256, 256, 2, 4, 2, 1
+#define MOE_TL_DG2 192, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_DG1
-#define MOE_TL_DG1 256, 256, 2, 4, 2, 1
+#define MOE_TL_DG1 192, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_FC1_MX
-#define MOE_TL_FC1_MX 256, 256, 2, 4, 2, 1
+#define MOE_TL_FC1_MX 192, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_FC2_MX
-#define MOE_TL_FC2_MX 256, 256, 2, 4, 2, 1
+#define MOE_TL_FC2_MX 192, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_DG2_MX
-#define MOE_TL_DG2_MX 256, 256, 2, 4, 2, 1, 2
+#define MOE_TL_DG2_MX 192, 256, 2, 4, 2, 1, 2
 #endif
 #ifndef MOE_TL_DG1_MX
-#define MOE_TL_DG1_MX 256, 256, 2, 4, 2, 1, 2
+#define MOE_TL_DG1_MX 192, 256, 2, 4, 2, 1, 2
 #endif
 #ifndef MOE_TL_WG
 #define MOE_TL_WG 128, 128, 2, 2, 2, 4, 0, 64
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
       auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (H / 32); };
       auto fb = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).data.row(e, brow(rr)); };
       auto fbs = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).scale.row(e, brow(rr)); };
-      tile_mma<TL, KC, KC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb);
+      tile_mma<TL, KC, KC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb);
       done = true;
     }
   }
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
       const int jj = brow(rr);
       return ((rr >> 5) & 1) ? ub + (int64_t)jj * uld : gb + (int64_t)jj * gld;
     };
-    tile_mma<TL, KC, KC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb);
+    tile_mma<TL, KC, KC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active, tt.rows, pfb);
   }
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
@@ -694,14 +695,14 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::M
     if constexpr (BMODE == KC) {
       auto fb = [&](int r) { return p.mx.b0.data.row(e, n0 + min(r, nlast)); };
       auto fbs = [&](int r) { return p.mx.b0.scale.row(e, n0 + min(r, nlast)); };
-      tile_mma<TL, KC, KC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb);
+      tile_mma<TL, KC, KC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb);
     } else {
       const int kbsplit = ksplit / 32;
       auto fb = [&](int q) { return (q < ksplit ? p.mx.b0.data.row(e, q) : p.mx.b1.data.row(e, q - ksplit)) + n0; };
       auto fbs = [&](int kb) {
         return (kb < kbsplit ? p.mx.b0.scale.row(e, kb) : p.mx.b1.scale.row(e, kb - kbsplit)) + n0;
       };
-      tile_mma<TL, KC, RC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb, ncols);
+      tile_mma<TL, KC, RC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb, ncols);
     }
   }
   if (!done) {
@@ -714,12 +715,12 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::M
     const int64_t ld1 = shared ? p.s1.ld_bytes : p.w1.ld_bytes;
     if constexpr (BMODE == KC) {
       auto fb = [&](int q) { return b0 + (int64_t)(n0 + min(q, nlast)) * ld0; };
-      tile_mma<TL, KC, KC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb);
+      tile_mma<TL, KC, KC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active, tt.rows, pfb);
     } else {
       auto fb = [&](int q) {
         return ((q < ksplit) ? b0 + (int64_t)q * ld0 : b1 + (int64_t)(q - ksplit) * ld1) + 2 * n0;
       };
-      tile_mma<TL, KC, RC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb, ncols);
+      tile_mma<TL, KC, RC, false>(acc, K, fa, fb, NoScale{}, NoScale{}, lds, sc, active, tt.rows, pfb, ncols);
     }
   }
 
@@ -780,7 +781,7 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
     auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (H / 32); };
     auto fb = [&](int k) { return p.mx.b0.data.row(e, k) + n0; };
     auto fbs = [&](int kb) { return p.mx.b0.scale.row(e, kb) + n0; };
-    tile_mma<TL, KC, RC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, TL::TM, pfb, ncols);
+    tile_mma<TL, KC, RC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb, ncols);
   }
   if (!done) {
     const uint16_t* abase = shared ? p.a_s : p.a_r;
@@ -788,7 +789,7 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
     const uint8_t* wb = shared ? p.sd.row(0, 0) : p.wd.row(e, 0);
     const int64_t wld = shared ? p.sd.ld_bytes : p.wd.ld_bytes;
     auto fb = [&](int k) { return wb + (int64_t)k * wld + 2 * n0; };
-    tile_mma<TL, KC, RC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active, TL::TM, pfb, ncols);
+    tile_mma<TL, KC, RC, false>(acc, H, fa, fb, NoScale{}, NoScale{}, lds, sc, active, tt.rows, pfb, ncols);
   }
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
