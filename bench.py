@@ -75,6 +75,28 @@ def counter_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def hbm_calibration():
+    """Achievable HBM rates on this GPU with plain streaming kernels (torch's copy and an
+    in-place FP32 add over 1 GiB): context for the roofline's 8 TB/s vendor peak."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    res = {}
+    for name, f, nbytes in (("copy_GBps", lambda: b.copy_(a), 8 * n), ("rmw_GBps", lambda: a.add_(1.0), 8 * n)):
+        for _ in range(3):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(nbytes / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9, 1)
+    del a, b
+    return res
+
+
 def cpu_baseline(cfg, dp, n_tokens):
     """The oracle, as it stands, on the first n_tokens tokens of the same workload
     (forward + backward incl. every routed expert's and the shared expert's weight
@@ -179,6 +201,7 @@ def main():
         "roofline": roofline,
         "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},
     }
+    line["hbm_calibration"] = hbm_calibration()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, dp, args.cpu_sample_tokens)
     print(json.dumps(line), flush=True)

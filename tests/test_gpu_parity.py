@@ -227,3 +227,71 @@ def test_full_size_mxfp8_config_sampled(gpu_lib, idx):
     counts = np.asarray(dp.layer.routing_state()["counts"].cpu())
     busiest = int(np.argmax(counts))
     _check_backward(dp, W, tokens=toks, experts=sorted({0, busiest, cfg.experts - 1}), tol=MXFP8_TOL)
+
+
+# ----------------------------------------------------------------------------------
+# limits and degenerate shapes
+# ----------------------------------------------------------------------------------
+def test_max_experts_and_topk(gpu_lib):
+    """255 experts (a routing row spans all 64 lanes of a wave) and the widest table, K = 8."""
+    cfg = gen.custom(200, 256, 255, 8, 128, short_frac=0.1, short_max=7, idx=501)
+    dp = _dp(cfg)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    _check_forward(dp, W)
+    _check_backward(dp, W, experts=[0, 1, 127, 254])
+
+
+def test_single_expert_top1(gpu_lib):
+    """E = 1, K = 1: every token takes the one routed expert plus the shared expert."""
+    cfg = gen.custom(130, 128, 1, 1, 128, idx=502)
+    dp = _dp(cfg)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    _check_forward(dp, W)
+    _check_backward(dp, W)
+
+
+def test_hip_graph_replay_matches_eager(gpu_lib):
+    """Both calls enqueue only kernels on the caller's stream, so a captured graph of
+    forward + backward replays bit-identically to the eager calls (main_grad reset
+    eagerly between replays, other eager work in between)."""
+    cfg = gen.custom(300, 256, 6, 3, 128, short_frac=0.1, short_max=2, idx=503)
+    dp = _dp(cfg)
+    names = ("out", "dx", "dprobs", "mg_r1", "mg_r2", "mg_s1", "mg_s2")
+    dp.reset_main_grads()
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    eager = {n: getattr(dp, n).clone() for n in names}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capture stream
+        dp.reset_main_grads()
+        dp.forward()
+        dp.backward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dp.forward()
+        dp.backward()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dp.reset_main_grads()
+        dp.out.fill_(float("nan"))
+        dp.dx.fill_(float("nan"))
+        dp.dprobs.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            a, b = getattr(dp, n), eager[n]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, n)
