@@ -37,18 +37,21 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (2: 4096-token BF16 layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--main-grad", choices=("fp32", "bf16"), default="fp32",
+                    help="main_grad dtype (bf16: contribution rounded to BF16 before a BF16 reduction-store)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before the steps (a known-size "
                          "reference for the HBM byte counters)")
     return ap.parse_args()
 
 
-def wgrad_fc1_bytes(cfg, slots):
+def wgrad_fc1_bytes(cfg, slots, mg_bytes=4):
     """Algorithmic HBM bytes of one launch of the FC1 weight-gradient kernel: every routed
-    and shared FC1 main_grad element (2I x H FP32 per expert) read and written once, plus
-    the dfc1 (2I) and input (H) bf16 rows of every routed slot and every token read once."""
+    and shared FC1 main_grad element (2I x H per expert, mg_bytes each) read and written
+    once, plus the dfc1 (2I) and input (H) bf16 rows of every routed slot and every token
+    read once."""
     E, H, I, T = cfg.experts, cfg.hidden, cfg.inter, cfg.tokens
-    return (E + 1) * 2 * I * H * 8 + (slots + T) * (2 * I + H) * 2
+    return (E + 1) * 2 * I * H * 2 * mg_bytes + (slots + T) * (2 * I + H) * 2
 
 
 def kernel_source_hash():
@@ -140,7 +143,7 @@ def main():
     mk.load()
     cfg = gen.config(args.config)
     t0 = time.time()
-    dp = DeviceProblem(cfg, backward=True)
+    dp = DeviceProblem(cfg, backward=True, main_grad_dtype=args.main_grad)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s: {cfg.name}", file=sys.stderr, flush=True)
 
@@ -181,11 +184,12 @@ def main():
     dom = "wgrad_fc1"
     n_l, tot_ms = ktimes.get(dom, (0, 0.0))
     avg_ms = tot_ms / max(n_l, 1)
-    alg_bytes = wgrad_fc1_bytes(cfg, slots)
+    alg_bytes = wgrad_fc1_bytes(cfg, slots, 2 if args.main_grad == "bf16" else 4)
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": counter_traffic(dom), "avg_launch_ms": round(avg_ms, 4),
+                "traffic": counter_traffic(dom) if args.main_grad == "fp32" else None,
+                "avg_launch_ms": round(avg_ms, 4),
                 "alg_bytes_per_launch": alg_bytes}
 
     line = {
@@ -197,7 +201,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden,
                    "experts": cfg.experts, "topk": cfg.topk, "intermediate": cfg.inter,
                    "routed_slots": slots, "routed_weights": cfg.routed, "layout": cfg.layout,
-                   "routing": cfg.routing, "parallelism": "single-gpu"},
+                   "routing": cfg.routing, "main_grad": args.main_grad, "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},
     }

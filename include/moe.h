@@ -117,23 +117,29 @@ typedef struct {
   moe_weight shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
 } moe_weights;
 
-/* An FP32 main_grad buffer [rows][cols] per expert, same addressing as moe_mat.
- * Rows are read and written in 16-byte pieces: `base` (or every table entry) must be
- * 16-byte aligned and `ld` and `expert_stride` multiples of 4 (MOE_ERR_LAYOUT
- * otherwise; table entries live on the device and are not checked). */
+/* A main_grad buffer [rows][cols] per expert, same addressing as moe_mat, in FP32 or
+ * BF16 (`dtype`; 0 means FP32).  All six buffers of a call must share one dtype
+ * (MOE_ERR_DTYPE otherwise).  Rows are read and written in pieces of 4 elements:
+ * `base` (or every table entry) must be 16-byte aligned and `ld` and `expert_stride`
+ * multiples of 4 (MOE_ERR_LAYOUT otherwise; table entries live on the device and are
+ * not checked).  `base` / `table` point at float or bf16 storage as `dtype` says. */
 typedef struct {
-  float* base;
-  int64_t expert_stride;
-  float* const* table;       /* device array of E pointers, or NULL                         */
-  int64_t ld;
+  void* base;
+  int64_t expert_stride;     /* elements                                                     */
+  void* const* table;        /* device array of E pointers, or NULL                         */
+  int64_t ld;                /* elements                                                     */
   int64_t row_offset;
+  int32_t dtype;             /* 0 or MOE_FP32, or MOE_BF16                                   */
 } moe_grad;
 
 /* main_grad buffers in the same six-buffer order (Megatron Core API docs,
- * mok.runtime, _gate_up_main_grad_arguments).  The backward accumulates
- * (+=) in FP32 into all six (PR #6572, Design > Gradient accumulation;
- * PR #8210, review thread on the wgrad accumulation precision: FP32
- * accumulator, FP32 main_grad stays FP32 through the reduction-store). */
+ * mok.runtime, _gate_up_main_grad_arguments).  The backward accumulates into all
+ * six (PR #6572, Design > Gradient accumulation) with an FP32 GEMM accumulator
+ * (PR #8210, review thread on the wgrad accumulation precision): an FP32 main_grad
+ * receives main_grad + contribution in FP32; a BF16 main_grad receives the BF16
+ * rounding (to nearest even) of main_grad + bf16(contribution), i.e. the call's
+ * contribution is rounded to BF16 before a BF16 reduction-store, so the persistent
+ * accumulation is BF16. */
 typedef struct {
   moe_grad shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
 } moe_main_grads;

@@ -38,9 +38,9 @@ def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
 
 class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
-                 routing=None):
+                 routing=None, main_grad_dtype: str = "fp32"):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
-        configuration's router output (edge cases)."""
+        configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16"."""
         self.cfg = cfg
         self.device = device
         T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
@@ -103,18 +103,20 @@ class DeviceProblem:
         if self.backward_enabled:
             self.dx = torch.empty(T, H, dtype=torch.bfloat16, device=device)
             self.dprobs = torch.empty(T, E, dtype=torch.float32, device=device)
-            self.mg_s1 = torch.empty(2 * I, H, dtype=torch.float32, device=device)
-            self.mg_s2 = torch.empty(H, I, dtype=torch.float32, device=device)
+            mgt = {"fp32": torch.float32, "bf16": torch.bfloat16}[main_grad_dtype]
+            mgd = mk.MOE_BF16 if main_grad_dtype == "bf16" else mk.MOE_FP32
+            self.mg_s1 = torch.empty(2 * I, H, dtype=mgt, device=device)
+            self.mg_s2 = torch.empty(H, I, dtype=mgt, device=device)
             if cfg.layout == "single":
-                self.mg_r1 = torch.empty(E, 2 * I, H, dtype=torch.float32, device=device)
-                self.mg_r2 = torch.empty(E, H, I, dtype=torch.float32, device=device)
+                self.mg_r1 = torch.empty(E, 2 * I, H, dtype=mgt, device=device)
+                self.mg_r2 = torch.empty(E, H, I, dtype=mgt, device=device)
                 g1 = dict(base=self.mg_r1, expert_stride=2 * I * H)
                 g2 = dict(base=self.mg_r2, expert_stride=H * I)
                 self.mg_r1_list = [self.mg_r1[e] for e in range(E)]
                 self.mg_r2_list = [self.mg_r2[e] for e in range(E)]
             else:
-                self.mg_r1_list = [torch.empty(2 * I, H, dtype=torch.float32, device=device) for _ in range(E)]
-                self.mg_r2_list = [torch.empty(H, I, dtype=torch.float32, device=device) for _ in range(E)]
+                self.mg_r1_list = [torch.empty(2 * I, H, dtype=mgt, device=device) for _ in range(E)]
+                self.mg_r2_list = [torch.empty(H, I, dtype=mgt, device=device) for _ in range(E)]
                 t1 = torch.tensor([int(t.data_ptr()) for t in self.mg_r1_list], dtype=torch.int64, device=device)
                 t2 = torch.tensor([int(t.data_ptr()) for t in self.mg_r2_list], dtype=torch.int64, device=device)
                 self._keep += [t1, t2]
@@ -122,9 +124,11 @@ class DeviceProblem:
                 g2 = dict(table=t2)
             self.reset_main_grads()
             self.main_grads = mk.moe_main_grads(
-                mk.grad(base=self.mg_s1, ld=H, row_offset=0), mk.grad(base=self.mg_s1, ld=H, row_offset=I),
-                mk.grad(base=self.mg_s2, ld=I),
-                mk.grad(ld=H, row_offset=0, **g1), mk.grad(ld=H, row_offset=I, **g1), mk.grad(ld=I, **g2))
+                mk.grad(base=self.mg_s1, ld=H, row_offset=0, dtype=mgd),
+                mk.grad(base=self.mg_s1, ld=H, row_offset=I, dtype=mgd),
+                mk.grad(base=self.mg_s2, ld=I, dtype=mgd),
+                mk.grad(ld=H, row_offset=0, dtype=mgd, **g1), mk.grad(ld=H, row_offset=I, dtype=mgd, **g1),
+                mk.grad(ld=I, dtype=mgd, **g2))
 
     # ------------------------------------------------------------------
     def reset_main_grads(self):

@@ -49,7 +49,7 @@ class moe_weights(C.Structure):
 
 class moe_grad(C.Structure):
     _fields_ = [("base", C.c_void_p), ("expert_stride", C.c_int64), ("table", C.c_void_p),
-                ("ld", C.c_int64), ("row_offset", C.c_int64)]
+                ("ld", C.c_int64), ("row_offset", C.c_int64), ("dtype", C.c_int32)]
 
 
 class moe_main_grads(C.Structure):
@@ -172,8 +172,16 @@ def weight(dtype, rows, cols, data: moe_mat, row_offset=0, scale=None, col_data=
     return moe_weight(dtype, rows, cols, row_offset, data, scale or z, col_data or z, col_scale or z)
 
 
-def grad(base=None, expert_stride=0, table=None, ld=0, row_offset=0) -> moe_grad:
-    return moe_grad(_ptr(base), int(expert_stride), _ptr(table), int(ld), int(row_offset))
+def grad(base=None, expert_stride=0, table=None, ld=0, row_offset=0, dtype=None) -> moe_grad:
+    """main_grad view; dtype defaults to the tensor's (torch.float32 -> MOE_FP32,
+    torch.bfloat16 -> MOE_BF16), else MOE_FP32."""
+    if dtype is None:
+        dtype = MOE_FP32
+        t = base if base is not None else None
+        if t is not None and hasattr(t, "dtype"):
+            import torch
+            dtype = MOE_BF16 if t.dtype == torch.bfloat16 else MOE_FP32
+    return moe_grad(_ptr(base), int(expert_stride), _ptr(table), int(ld), int(row_offset), int(dtype))
 
 
 def current_stream() -> int:

@@ -74,15 +74,17 @@ struct MxRef {
   MatRef scale;   // E8M0 bytes; for a columnwise copy its rows are blocks of 32 weight rows
 };
 
+// main_grad of one weight: FP32 or BF16 elements (ES = 4 or 2 bytes).
 struct GradRef {
-  float* base;
-  float* const* table;
+  uint8_t* base;
+  uint8_t* const* table;
   int64_t estride;         // elements
   int64_t ld;              // elements
   int64_t row_offset;
-  __device__ __forceinline__ float* row(int e, int64_t r) const {
-    float* b = table ? table[e] : base + (int64_t)e * estride;
-    return b + (row_offset + r) * ld;
+  template <int ES>
+  __device__ __forceinline__ uint8_t* row(int e, int64_t r) const {
+    uint8_t* b = table ? table[e] : base + (int64_t)e * estride * ES;
+    return b + (row_offset + r) * ld * ES;
   }
 };
 

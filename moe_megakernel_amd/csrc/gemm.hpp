@@ -841,7 +841,9 @@ __host__ __device__ inline int wgrad_tiles_per_group(int parts, int mpart, int N
 }
 
 // FC is 1 or 2 (which projection's gradient); it only names the kernel symbol apart.
-template <int FC>
+// MG16: BF16 main_grad (the contribution is rounded to BF16, then added with one BF16
+// rounding), else FP32.
+template <int FC, bool MG16>
 __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) {
   using TL = TL_WG;
   __shared__ __align__(16) uint8_t lds[TL::LDS];
@@ -886,9 +888,10 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
   auto fa = [&](int k) { return A + (ar0 + k) * lda; };
   auto fb = [&](int k) { return B + (br0 + k) * ldb; };
 
+  constexpr int ES = MG16 ? 2 : 4;   // main_grad element bytes
   const GradRef& G = part == 0 ? (shared ? p.s_lo : p.g_lo) : (shared ? p.s_hi : p.g_hi);
-  float* cb = G.row(e, m0) + n0;
-  const int64_t ldc = G.ld;
+  uint8_t* cb = G.row<ES>(e, m0) + (int64_t)n0 * ES;
+  const int64_t ldc = G.ld * ES;   // bytes
 
   const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
   Acc<TL> acc;
@@ -897,8 +900,8 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
   tile_mma<TL, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, active, mrows, pfb);
 
   // main_grad += acc, one slice of WMR rows per round: the waves of wave row `rd` park
-  // their accumulators in LDS, then every thread adds 16-byte pieces of whole rows to
-  // main_grad (coalesced row reads and writes).  The main_grad loads of a round are
+  // their accumulators in LDS, then every thread adds pieces of 4 elements of whole rows
+  // to main_grad (coalesced row reads and writes).  The main_grad loads of a round are
   // issued before its LDS traffic.  LDS slice [WMR][TN] fp32; 16-byte chunk c of row r
   // sits at c ^ 8 ((r >> 2) & 1), so the two row groups a wave writes at once use
   // disjoint banks.
@@ -915,7 +918,13 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
     for (int q = 0; q < CPT; ++q) {
       const int c = q * TL::NTH + t, row = c / CPRW, cc = c % CPRW;
       const int grow = rd * TL::WMR + row;
-      mg[q] = grow < mrows ? *reinterpret_cast<const f32x4_t*>(cb + grow * ldc + cc * 4) : f32x4_t{};
+      const uint8_t* src = cb + grow * ldc + cc * 4 * ES;
+      if constexpr (MG16) {
+        const uint2 v = grow < mrows ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+        mg[q] = f32x4_t{lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y)};
+      } else {
+        mg[q] = grow < mrows ? *reinterpret_cast<const f32x4_t*>(src) : f32x4_t{};
+      }
     }
     __syncthreads();   // the LDS slice is free (K loop or previous round done)
     if (wm == rd) {
@@ -937,7 +946,17 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
       const int grow = rd * TL::WMR + row;
       if (grow < mrows) {
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + row * TL::TN + ((cc ^ sw(row)) << 2));
-        *reinterpret_cast<f32x4_t*>(cb + grow * ldc + cc * 4) = mg[q] + v;
+        uint8_t* dst = cb + grow * ldc + cc * 4 * ES;
+        if constexpr (MG16) {
+          // contribution rounded to BF16, then main_grad + it rounded to BF16 (the float
+          // sum of two BF16 values rounds to the same BF16 as their exact sum)
+          f32x4_t r;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) r[u] = mg[q][u] + bf2f(f2bf(v[u]));
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3]));
+        } else {
+          *reinterpret_cast<f32x4_t*>(dst) = mg[q] + v;
+        }
       }
     }
   }

@@ -197,8 +197,17 @@ moe_status check_grad(const moe_grad& g, int64_t cols, bool routed) {
   return MOE_OK;
 }
 
+bool grad_bf16(const moe_grad& g) { return g.dtype == MOE_BF16; }
+
 moe_status check_grads(const moe_problem* p, const moe_main_grads* g) {
   if (!g) return MOE_ERR_NULL;
+  // one dtype for all six buffers: FP32 (0 or MOE_FP32) or BF16
+  const moe_grad* all[6] = {&g->shared_gate, &g->shared_up, &g->shared_down,
+                            &g->routed_gate, &g->routed_up, &g->routed_down};
+  for (const moe_grad* x : all)
+    if (x->dtype != 0 && x->dtype != MOE_FP32 && x->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  for (const moe_grad* x : all)
+    if (grad_bf16(*x) != grad_bf16(g->shared_gate)) return MOE_ERR_DTYPE;
   const int64_t H = p->hidden, I = p->intermediate;
   moe_status s;
   if ((s = check_grad(g->shared_gate, H, false)) != MOE_OK) return s;
@@ -237,8 +246,8 @@ MxRef mxref(const moe_weight& w, bool columnwise) {
 
 GradRef gradref(const moe_grad& g) {
   GradRef r;
-  r.base = g.base;
-  r.table = g.table;
+  r.base = static_cast<uint8_t*>(g.base);
+  r.table = reinterpret_cast<uint8_t* const*>(g.table);
   r.estride = g.expert_stride;
   r.ld = g.ld;
   r.row_offset = g.row_offset;
@@ -592,7 +601,9 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   {
     const int per = gemm::wgrad_tiles_per_group(1, H, I);
     MOE_TRY(launch("wgrad_fc2", st, [&] {
-      hipLaunchKernelGGL(gemm::k_wgrad<2>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::TL_WG::NTH), 0, st, a5);
+      const dim3 g(per + grid8((int64_t)E * per));
+      if (grad_bf16(mg->shared_gate)) hipLaunchKernelGGL((gemm::k_wgrad<2, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a5);
+      else hipLaunchKernelGGL((gemm::k_wgrad<2, false>), g, dim3(gemm::TL_WG::NTH), 0, st, a5);
     }));
   }
 
@@ -610,7 +621,9 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   {
     const int per = gemm::wgrad_tiles_per_group(2, I, H);
     MOE_TRY(launch("wgrad_fc1", st, [&] {
-      hipLaunchKernelGGL(gemm::k_wgrad<1>, dim3(per + grid8((int64_t)E * per)), dim3(gemm::TL_WG::NTH), 0, st, a6);
+      const dim3 g(per + grid8((int64_t)E * per));
+      if (grad_bf16(mg->shared_gate)) hipLaunchKernelGGL((gemm::k_wgrad<1, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a6);
+      else hipLaunchKernelGGL((gemm::k_wgrad<1, false>), g, dim3(gemm::TL_WG::NTH), 0, st, a6);
     }));
   }
   return MOE_OK;

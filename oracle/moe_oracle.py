@@ -29,7 +29,8 @@ Readings of points the pages leave open:
   * FC1 holds the gate rows [0, I) then the up rows [I, 2I);
   * the shared expert has weight 1 and no output gate;
   * grad_probs is the full gradient of the dense probs tensor (zero off the
-    map); main_grad receives the weight gradient by accumulation (+=);
+    map); main_grad receives the weight gradient by accumulation (+=), in FP32,
+    or for a BF16 main_grad as described in main_grad_after;
   * MXFP8 forward uses the rowwise copy, dgrad the columnwise copy.
 """
 from __future__ import annotations
@@ -37,7 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_decode", "e4m3_decode", "e8m0_decode", "mxfp8_decode_rowwise",
+    "bf16_decode", "bf16_round", "main_grad_after", "e4m3_decode", "e8m0_decode", "mxfp8_decode_rowwise",
     "mxfp8_decode_colwise", "compact_routing", "dispatch_index", "silu", "dsilu",
     "swiglu_ffn", "Weights", "moe_forward", "moe_forward_f64", "moe_backward",
     "moe_backward_f64", "RouteOverflow",
@@ -55,6 +56,29 @@ def bf16_decode(bits: np.ndarray) -> np.ndarray:
     """BF16 bit patterns -> float64: a bfloat16 is the top half of a float32."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def bf16_round(v) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even), returned as
+    float64.  A bfloat16 has 8 significant bits and float32's exponent range, so the
+    spacing of representable values near |v| in [2^k, 2^(k+1)) is 2^(k-7), and 2^-133
+    below 2^-126."""
+    v = np.asarray(v, dtype=np.float64)
+    m, ex = np.frexp(v)                       # |v| = |m| 2^ex, |m| in [0.5, 1)
+    ulp = np.ldexp(1.0, np.maximum(ex - 8, -133))
+    return np.round(v / ulp) * ulp            # np.round rounds halves to even
+
+
+def main_grad_after(before: np.ndarray, dW: np.ndarray, dtype: str) -> np.ndarray:
+    """main_grad after one backward call (PR #8210, review thread on the wgrad
+    accumulation precision): FP32 main_grad receives before + dW; BF16 main_grad
+    receives the BF16 rounding of before + (dW rounded to BF16): the contribution is
+    rounded to BF16 before a BF16 reduction-store."""
+    if dtype == "fp32":
+        return before + dW
+    if dtype == "bf16":
+        return bf16_round(before + bf16_round(dW))
+    raise ValueError(dtype)
 
 
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:

@@ -154,3 +154,18 @@ def test_main_grad_rows_must_be_16_byte_aligned():
     assert mk.moe_backward(p, a, a, w, a, a, a, bad_ld, a, 1 << 30, 0) == mk.MOE_ERR_LAYOUT
     bad_stride = mk.moe_main_grads(G(H), G(H, I), G(I), G(H), G(H, I), G(I, 0, a, I * H + 2))
     assert mk.moe_backward(p, a, a, w, a, a, a, bad_stride, a, 1 << 30, 0) == mk.MOE_ERR_LAYOUT
+
+
+def test_main_grad_dtype_validation():
+    p = _ok_problem()
+    w = _fake_weights(p)
+    a = 1 << 41
+    H, I = p.hidden, p.intermediate
+    G = lambda ld, ro=0, dt=0: mk.moe_grad(a, 0, 0, ld, ro, dt)
+    bf = mk.MOE_BF16
+    all_bf16 = mk.moe_main_grads(G(H, 0, bf), G(H, I, bf), G(I, 0, bf), G(H, 0, bf), G(H, I, bf), G(I, 0, bf))
+    assert mk.moe_backward(p, a, a, w, a, a, a, all_bf16, a, 16, 0) == mk.MOE_ERR_WORKSPACE   # accepted
+    mixed = mk.moe_main_grads(G(H, 0, bf), G(H, I, bf), G(I, 0, bf), G(H), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, mixed, a, 1 << 30, 0) == mk.MOE_ERR_DTYPE
+    bad = mk.moe_main_grads(G(H), G(H, I), G(I), G(H), G(H, I), G(I, 0, mk.MOE_MXFP8_E4M3))
+    assert mk.moe_backward(p, a, a, w, a, a, a, bad, a, 1 << 30, 0) == mk.MOE_ERR_DTYPE

@@ -295,3 +295,46 @@ def test_hip_graph_replay_matches_eager(gpu_lib):
             a, b = getattr(dp, n), eager[n]
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, n)
+
+
+# ----------------------------------------------------------------------------------
+# BF16 main_grad: the call's contribution is rounded to BF16, then added with one BF16
+# rounding (the persistent accumulation is BF16)
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("routed,layout,shape", [
+    ("bf16", "single", (512, 1024, 16, 4, 512)),
+    ("mxfp8", "table", (300, 256, 6, 3, 128)),
+])
+def test_bf16_main_grad_matches_oracle(gpu_lib, routed, layout, shape):
+    T, H, E, K, I = shape
+    # the inputs of the FP32-main_grad cases above with the same shapes (config 1; the
+    # MXFP8 table case)
+    cfg = gen.config(1) if routed == "bf16" else gen.custom(
+        T, H, E, K, I, routed=routed, layout=layout, short_frac=0.05, short_max=max(1, K - 1), idx=400 + T)
+    dp = _dp(cfg, main_grad_dtype="bf16")
+    assert dp.mg_s1.dtype == torch.bfloat16
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    W = oracle_weights(dp)
+    tol = BF16_TOL if routed == "bf16" else MXFP8_TOL
+    _check_backward(dp, W, tol=tol)
+    if routed != "bf16":
+        return
+    # The same call with FP32 main_grad yields the GPU's own FP32 contribution (the K loop
+    # is identical); the BF16 result must be bf16(before + bf16(contribution)) of it.  A
+    # contribution within FP32 rounding of a BF16 rounding boundary may land one ulp away.
+    dp32 = _dp(cfg, main_grad_dtype="fp32")
+    dp32.forward()
+    dp32.backward()
+    torch.cuda.synchronize()
+    match = []
+    for e in range(E):
+        for t16, t32, shape in ((dp.mg_r1_list[e], dp32.mg_r1_list[e], (2 * I, H)),
+                                (dp.mg_r2_list[e], dp32.mg_r2_list[e], (H, I))):
+            start = dp.main_grad_start(shape, e)
+            model = O.main_grad_after(start, to_f64(t32) - start, "bf16")
+            match.append(np.mean(to_f64(t16) == model))
+    print(f"[parity] bf16 main_grad = bf16(before + bf16(fp32 contribution)): exact fraction min "
+          f"{min(match):.5f}", flush=True)
+    assert min(match) >= 0.999

@@ -471,3 +471,24 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
     errs = [_rel(out, ref["out"].numpy()), _rel(g["dx"], ref["dx"].numpy()),
             _rel(g["dprobs"], ref["dprobs"].numpy())]
     assert max(errs) > 1e-3, errs
+
+
+def test_bf16_round_matches_torch_rne():
+    rng = np.random.default_rng(21)
+    v = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 2.0 ** -130, 3 * 2.0 ** -134,
+                         0.0, 65504.0, 1.0 + 2.0 ** -8 + 2.0 ** -20]]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_main_grad_reduction_store_closed_forms():
+    # the contribution is rounded first: 1 + (2^-8 + 2^-20): bf16(c) = 2^-8, 1 + 2^-8 is a tie -> 1.0
+    assert O.main_grad_after(np.array([1.0]), np.array([2.0 ** -8 + 2.0 ** -20]), "bf16")[0] == 1.0
+    # without that first rounding the exact sum would round up to 1 + 2^-7
+    assert O.bf16_round(np.array([1.0 + 2.0 ** -8 + 2.0 ** -20]))[0] == 1.0 + 2.0 ** -7
+    assert O.main_grad_after(np.array([1.0]), np.array([3 * 2.0 ** -8]), "bf16")[0] == 1.0 + 2.0 ** -6
+    assert O.main_grad_after(np.array([0.5]), np.array([0.25]), "fp32")[0] == 0.75
+    with pytest.raises(ValueError):
+        O.main_grad_after(np.array([0.0]), np.array([0.0]), "fp16")
