@@ -9,7 +9,7 @@ backward with FP32 main_grad accumulation and the dense probability gradient).
 Inputs are resident in HBM before the timed region.  Prints one JSON line.
 
 Throughput is algorithmic TFLOPS: 18 * H * I * (S + T) flops per step, S = valid
-routed slots, T = tokens (shared expert).  The roofline object describes the
+routed slots, T = tokens (shared expert; 0 with --routed-only).  The roofline object describes the
 dominant kernel, timed live with HIP events on the stream it runs on; the
 cpu_baseline object times the CPU oracle on a bounded sample of the same workload.
 """
@@ -39,19 +39,22 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--main-grad", choices=("fp32", "bf16"), default="fp32",
                     help="main_grad dtype (bf16: contribution rounded to BF16 before a BF16 reduction-store)")
+    ap.add_argument("--routed-only", action="store_true",
+                    help="no fused shared expert (the layer's routed terms only)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before the steps (a known-size "
                          "reference for the HBM byte counters)")
     return ap.parse_args()
 
 
-def wgrad_fc1_bytes(cfg, slots, mg_bytes=4):
+def wgrad_fc1_bytes(cfg, slots, mg_bytes=4, shared=True):
     """Algorithmic HBM bytes of one launch of the FC1 weight-gradient kernel: every routed
     and shared FC1 main_grad element (2I x H per expert, mg_bytes each) read and written
     once, plus the dfc1 (2I) and input (H) bf16 rows of every routed slot and every token
-    read once."""
+    read once (without the shared expert: the routed terms only)."""
     E, H, I, T = cfg.experts, cfg.hidden, cfg.inter, cfg.tokens
-    return (E + 1) * 2 * I * H * 2 * mg_bytes + (slots + T) * (2 * I + H) * 2
+    ns = 1 if shared else 0
+    return (E + ns) * 2 * I * H * 2 * mg_bytes + (slots + ns * T) * (2 * I + H) * 2
 
 
 def kernel_source_hash():
@@ -100,7 +103,7 @@ def hbm_calibration():
     return res
 
 
-def cpu_baseline(cfg, dp, n_tokens):
+def cpu_baseline(cfg, dp, n_tokens, shared=True):
     """The oracle, as it stands, on the first n_tokens tokens of the same workload
     (forward + backward incl. every routed expert's and the shared expert's weight
     gradients over those tokens)."""
@@ -111,13 +114,14 @@ def cpu_baseline(cfg, dp, n_tokens):
     n = min(n_tokens, cfg.tokens)
     rm = dp.np_rmap[:n]
     pr = dp.np_probs[:n]
-    W = O.Weights.from_bits(cfg.inter, dp.np_s1, dp.np_s2, lambda e: dp.np_routed[e], cfg.routed)
+    W = O.Weights.from_bits(cfg.inter, dp.np_s1 if shared else None, dp.np_s2 if shared else None,
+                            lambda e: dp.np_routed[e], cfg.routed)
     t0 = time.perf_counter()
     O.moe_forward(dp.np_x[:n], pr, rm, cfg.topk, W)
     O.moe_backward(dp.np_dy[:n], dp.np_x[:n], pr, rm, cfg.topk, W)
     dt = time.perf_counter() - t0
     s = int(rm.sum())
-    flops = 18.0 * cfg.hidden * cfg.inter * (s + n)
+    flops = 18.0 * cfg.hidden * cfg.inter * (s + (n if shared else 0))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOPS", "cores": int(threads),
             "kind": "oracle",
@@ -143,7 +147,8 @@ def main():
     mk.load()
     cfg = gen.config(args.config)
     t0 = time.time()
-    dp = DeviceProblem(cfg, backward=True, main_grad_dtype=args.main_grad)
+    shared = not args.routed_only
+    dp = DeviceProblem(cfg, backward=True, main_grad_dtype=args.main_grad, shared=shared)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s: {cfg.name}", file=sys.stderr, flush=True)
 
@@ -174,21 +179,22 @@ def main():
 
     ms = elapsed / args.steps * 1e3
     slots = dp.slots
-    flops = 18.0 * cfg.hidden * cfg.inter * (slots + cfg.tokens)
+    n_shared = cfg.tokens if shared else 0
+    flops = 18.0 * cfg.hidden * cfg.inter * (slots + n_shared)
     tflops = flops / (ms * 1e-3) / 1e12
     dtype = cfg.routed
     routed_fl = 18.0 * cfg.hidden * cfg.inter * slots
-    shared_fl = 18.0 * cfg.hidden * cfg.inter * cfg.tokens
+    shared_fl = 18.0 * cfg.hidden * cfg.inter * n_shared
     mfma_frac = (routed_fl / (MFMA_PEAK[dtype] * 1e12) + shared_fl / (MFMA_PEAK["bf16"] * 1e12)) / (ms * 1e-3)
 
     dom = "wgrad_fc1"
     n_l, tot_ms = ktimes.get(dom, (0, 0.0))
     avg_ms = tot_ms / max(n_l, 1)
-    alg_bytes = wgrad_fc1_bytes(cfg, slots, 2 if args.main_grad == "bf16" else 4)
+    alg_bytes = wgrad_fc1_bytes(cfg, slots, 2 if args.main_grad == "bf16" else 4, shared)
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": counter_traffic(dom) if args.main_grad == "fp32" else None,
+                "traffic": counter_traffic(dom) if args.main_grad == "fp32" and shared else None,
                 "avg_launch_ms": round(avg_ms, 4),
                 "alg_bytes_per_launch": alg_bytes}
 
@@ -201,13 +207,14 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden,
                    "experts": cfg.experts, "topk": cfg.topk, "intermediate": cfg.inter,
                    "routed_slots": slots, "routed_weights": cfg.routed, "layout": cfg.layout,
-                   "routing": cfg.routing, "main_grad": args.main_grad, "parallelism": "single-gpu"},
+                   "routing": cfg.routing, "main_grad": args.main_grad, "shared_expert": shared,
+                   "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},
     }
     line["hbm_calibration"] = hbm_calibration()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, dp, args.cpu_sample_tokens)
+        line["cpu_baseline"] = cpu_baseline(cfg, dp, args.cpu_sample_tokens, shared)
     print(json.dumps(line), flush=True)
 
 

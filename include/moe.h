@@ -50,8 +50,7 @@ typedef enum {
   MOE_ERR_SHAPE = 2,           /* a size is out of range or not a multiple the kernels need */
   MOE_ERR_DTYPE = 3,           /* unsupported element type (e.g. non-BF16 shared expert)  */
   MOE_ERR_LAYOUT = 4,          /* inconsistent strides / both or neither of base and table */
-  MOE_ERR_UNSUPPORTED = 5,     /* a configuration the pages reject (no shared expert,
-                                  shared output gate, SwiGLU clamp)                        */
+  MOE_ERR_UNSUPPORTED = 5,     /* a configuration not implemented (SwiGLU clamp)           */
   MOE_ERR_WORKSPACE = 6,       /* saved / workspace buffer missing or too small            */
   MOE_ERR_ROUTE_OVERFLOW = 7,  /* device status word: a row had more than topk routes      */
   MOE_ERR_HIP = 8              /* a HIP launch failed                                      */
@@ -59,6 +58,12 @@ typedef enum {
 
 typedef enum { MOE_BF16 = 1, MOE_FP32 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
 
+/* Set: the shared expert is fused into the same launches (PR #6572, Summary: the
+ * backend runs dispatch, routed and shared experts, and combine).  Clear: routed-only
+ * mode, the follow-up named in PR #8210 (Summary and the review thread on TP for the
+ * shared expert) where the caller runs the shared expert itself; the output and the
+ * data gradient then hold the routed terms only, and the shared weights and shared
+ * main_grad buffers are neither validated nor touched (they may be all zero/NULL). */
 #define MOE_FLAG_HAS_SHARED 1u
 
 /* Problem sizes and options. */
@@ -69,8 +74,7 @@ typedef struct {
   int32_t experts;       /* E in [1, 255]                                                 */
   int32_t topk;          /* K in [1, min(8, E)]                                           */
   int32_t routed_dtype;  /* MOE_BF16 or MOE_MXFP8_E4M3 (PR #6572, Supported configurations) */
-  uint32_t flags;        /* MOE_FLAG_HAS_SHARED must be set: the fused shared expert is
-                            required (PR #8210, review thread on the config guards)        */
+  uint32_t flags;        /* MOE_FLAG_HAS_SHARED or 0 (routed-only)                        */
   float swiglu_limit;    /* must be 0 (no clamp)                                          */
 } moe_problem;
 
@@ -143,6 +147,8 @@ typedef struct {
 typedef struct {
   moe_grad shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
 } moe_main_grads;
+/* In routed-only mode only the three routed buffers are used, and they alone must share
+ * one dtype. */
 
 /* Byte offsets of the integer routing state inside `saved` (for tests and
  * callers that want the compacted routing).  All arrays are int32 unless
@@ -175,6 +181,7 @@ moe_status moe_saved_view(const moe_problem* p, moe_saved_layout* layout);
  *               Authoritative routing maps)
  *  out          bf16  [T][H]  overwritten:
  *               out[t] = shared(x_t) + sum_k w_tk * expert_{e_tk}(x_t)
+ *               (without the shared(x_t) term in routed-only mode)
  *  saved        moe_saved_bytes(p) bytes, written; pass it to moe_backward
  *  workspace    moe_workspace_bytes(p, 0) bytes of scratch
  */
@@ -186,11 +193,11 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
  *  grad_out     bf16  [T][H]
  *  hidden       the same bf16 [T][H] tensor given to moe_forward
  *  saved        the context moe_forward wrote (unchanged since)
- *  grad_hidden  bf16  [T][H]  overwritten
+ *  grad_hidden  bf16  [T][H]  overwritten (routed terms only in routed-only mode)
  *  grad_probs   float [T][E]  overwritten in full; zero where routing_map was 0
  *               (the router-weight gradient scattered back into the dense
  *               probability tensor: PR #6572, Design > Authoritative routing maps)
- *  mg           FP32 main_grad buffers, accumulated (+=)
+ *  mg           main_grad buffers (FP32 or BF16, see moe_main_grads), accumulated
  *  workspace    moe_workspace_bytes(p, 1) bytes of scratch
  */
 moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* hidden,

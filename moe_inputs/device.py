@@ -38,9 +38,11 @@ def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
 
 class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
-                 routing=None, main_grad_dtype: str = "fp32"):
+                 routing=None, main_grad_dtype: str = "fp32", shared: bool = True):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
-        configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16"."""
+        configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16".
+        shared=False: routed-only mode; the shared weight and main_grad descriptors are
+        passed all zero (the library must not touch them)."""
         self.cfg = cfg
         self.device = device
         T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
@@ -62,7 +64,8 @@ class DeviceProblem:
         self._keep = []
         mx = cfg.routed == "mxfp8"
         dt = mk.MOE_MXFP8_E4M3 if mx else mk.MOE_BF16
-        self.p = mk.problem(T, H, I, E, K, dt)
+        self.shared = shared
+        self.p = mk.problem(T, H, I, E, K, dt, flags=mk.MOE_FLAG_HAS_SHARED if shared else 0)
 
         def routed_mat(key, rows, cols, conv, elem_cols):
             """moe_mat for a routed tensor stored [E][rows][cols] (single) or per expert (table)."""
@@ -93,9 +96,12 @@ class DeviceProblem:
             rg = mk.weight(dt, I, H, fc1, 0, fc1s, fc1c, fc1cs)
             ru = mk.weight(dt, I, H, fc1, I, fc1s, fc1c, fc1cs)
             rd = mk.weight(dt, H, I, fc2, 0, fc2s, fc2c, fc2cs)
-        sg = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=0)
-        su = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=I)
-        sd = mk.weight(mk.MOE_BF16, H, I, mk.mat(base=self.s2, ld=I))
+        if shared:
+            sg = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=0)
+            su = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=I)
+            sd = mk.weight(mk.MOE_BF16, H, I, mk.mat(base=self.s2, ld=I))
+        else:
+            sg, su, sd = mk.moe_weight(), mk.moe_weight(), mk.moe_weight()
         self.weights = mk.moe_weights(sg, su, sd, rg, ru, rd)
 
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
@@ -123,10 +129,12 @@ class DeviceProblem:
                 g1 = dict(table=t1)
                 g2 = dict(table=t2)
             self.reset_main_grads()
+            sh = ((mk.grad(base=self.mg_s1, ld=H, row_offset=0, dtype=mgd),
+                   mk.grad(base=self.mg_s1, ld=H, row_offset=I, dtype=mgd),
+                   mk.grad(base=self.mg_s2, ld=I, dtype=mgd)) if shared
+                  else (mk.moe_grad(), mk.moe_grad(), mk.moe_grad()))
             self.main_grads = mk.moe_main_grads(
-                mk.grad(base=self.mg_s1, ld=H, row_offset=0, dtype=mgd),
-                mk.grad(base=self.mg_s1, ld=H, row_offset=I, dtype=mgd),
-                mk.grad(base=self.mg_s2, ld=I, dtype=mgd),
+                *sh,
                 mk.grad(ld=H, row_offset=0, dtype=mgd, **g1), mk.grad(ld=H, row_offset=I, dtype=mgd, **g1),
                 mk.grad(ld=I, dtype=mgd, **g2))
 

@@ -459,8 +459,8 @@ __device__ __forceinline__ void zero_acc(Acc<TL>& acc) {
 
 // ---------------------------------------------------------------------------------
 // Token-dimension grouped tiles: group g < E is routed expert g with counts[g] rows
-// starting at offsets[g] of the permuted buffers; group E is the shared expert with
-// T rows.  tile_prefix[g] = sum of ceil(rows / BMT) over groups before g.  Linear
+// starting at offsets[g] of the permuted buffers; group E, when present, is the
+// shared expert with T rows.  tile_prefix[g] = sum of ceil(rows / BMT) over groups before g.  Linear
 // tiles (m-tile major, n-tile minor) are split into 8 contiguous chunks, chunk x
 // run by the blocks with blockIdx % 8 == x (the blocks one XCD receives), so the
 // n-tiles that share an A row panel run on one L2.
@@ -500,7 +500,7 @@ struct TokArgs {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* tile_prefix;
-  int T, E, groups;           // groups = E + 1 (shared expert last)
+  int T, E, groups;           // E, or E + 1 with the shared expert (last group)
   int64_t shared_row0;        // first row of the shared expert in the routed+shared buffers
 };
 
@@ -822,8 +822,8 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
 // tiled by TM with a masked tail, so no tile straddles two main_grad buffers.  Each
 // output tile has exactly one owner: it runs the full token loop and then adds its
 // result to main_grad once (no split-K, no atomics).
-// Shared-expert tiles come first in launch order (their K is all T tokens); routed
-// tiles follow, chunked per XCD like the token-dim GEMMs.
+// Shared-expert tiles (when has_shared) come first in launch order (their K is all T
+// tokens); routed tiles follow, chunked per XCD like the token-dim GEMMs.
 // ---------------------------------------------------------------------------------
 struct WgradArgs {
   const int32_t* counts;

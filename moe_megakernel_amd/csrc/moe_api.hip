@@ -26,16 +26,18 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 struct Dims {
   int64_t T, H, I, E, K;
   int64_t SM;        // T*K: slot capacity of the routed buffers
-  int64_t R;         // SM + T: routed rows then shared rows
+  int64_t R;         // SM + T with the shared expert (routed rows, then shared rows), else SM
   int64_t nchunks;
   bool mx;
+  bool hs;           // the shared expert is fused in
 };
 
 Dims dims_of(const moe_problem* p) {
   Dims d;
   d.T = p->tokens; d.H = p->hidden; d.I = p->intermediate; d.E = p->experts; d.K = p->topk;
   d.SM = d.T * d.K;
-  d.R = d.SM + d.T;
+  d.hs = (p->flags & MOE_FLAG_HAS_SHARED) != 0;
+  d.R = d.SM + (d.hs ? d.T : 0);
   d.nchunks = (d.T + kRouteChunk - 1) / kRouteChunk;
   d.mx = p->routed_dtype == MOE_MXFP8_E4M3;
   return d;
@@ -125,7 +127,7 @@ moe_status check_problem(const moe_problem* p) {
   if (p->topk < 1 || p->topk > kMaxTopk || p->topk > p->experts) return MOE_ERR_SHAPE;
   if (p->tokens * (int64_t)p->topk > (int64_t)1 << 30) return MOE_ERR_SHAPE;
   if (p->hidden > (1 << 20) || p->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
-  if (!(p->flags & MOE_FLAG_HAS_SHARED)) return MOE_ERR_UNSUPPORTED;
+  if (p->flags & ~MOE_FLAG_HAS_SHARED) return MOE_ERR_UNSUPPORTED;
   if (p->swiglu_limit != 0.0f) return MOE_ERR_UNSUPPORTED;
   if (p->routed_dtype != MOE_BF16 && p->routed_dtype != MOE_MXFP8_E4M3) return MOE_ERR_DTYPE;
   return MOE_OK;
@@ -177,10 +179,11 @@ moe_status check_weights(const moe_problem* p, const moe_weights* w, bool backwa
   if (!w) return MOE_ERR_NULL;
   const int64_t H = p->hidden, I = p->intermediate;
   moe_status s;
-  // shared expert parameters must be BF16
-  if ((s = check_weight(w->shared_gate, I, H, false, MOE_BF16)) != MOE_OK) return s;
-  if ((s = check_weight(w->shared_up, I, H, false, MOE_BF16)) != MOE_OK) return s;
-  if ((s = check_weight(w->shared_down, H, I, false, MOE_BF16)) != MOE_OK) return s;
+  if (p->flags & MOE_FLAG_HAS_SHARED) {   // shared expert parameters must be BF16
+    if ((s = check_weight(w->shared_gate, I, H, false, MOE_BF16)) != MOE_OK) return s;
+    if ((s = check_weight(w->shared_up, I, H, false, MOE_BF16)) != MOE_OK) return s;
+    if ((s = check_weight(w->shared_down, H, I, false, MOE_BF16)) != MOE_OK) return s;
+  }
   if ((s = check_weight(w->routed_gate, I, H, true, p->routed_dtype, backward)) != MOE_OK) return s;
   if ((s = check_weight(w->routed_up, I, H, true, p->routed_dtype, backward)) != MOE_OK) return s;
   if ((s = check_weight(w->routed_down, H, I, true, p->routed_dtype, backward)) != MOE_OK) return s;
@@ -201,18 +204,23 @@ bool grad_bf16(const moe_grad& g) { return g.dtype == MOE_BF16; }
 
 moe_status check_grads(const moe_problem* p, const moe_main_grads* g) {
   if (!g) return MOE_ERR_NULL;
-  // one dtype for all six buffers: FP32 (0 or MOE_FP32) or BF16
-  const moe_grad* all[6] = {&g->shared_gate, &g->shared_up, &g->shared_down,
-                            &g->routed_gate, &g->routed_up, &g->routed_down};
-  for (const moe_grad* x : all)
-    if (x->dtype != 0 && x->dtype != MOE_FP32 && x->dtype != MOE_BF16) return MOE_ERR_DTYPE;
-  for (const moe_grad* x : all)
-    if (grad_bf16(*x) != grad_bf16(g->shared_gate)) return MOE_ERR_DTYPE;
+  // one dtype for every buffer in use (all six, or the three routed ones in routed-only
+  // mode): FP32 (0 or MOE_FP32) or BF16
+  const bool hs = (p->flags & MOE_FLAG_HAS_SHARED) != 0;
+  const moe_grad* all[6] = {&g->routed_gate, &g->routed_up, &g->routed_down,
+                            &g->shared_gate, &g->shared_up, &g->shared_down};
+  const int n = hs ? 6 : 3;
+  for (int i = 0; i < n; ++i)
+    if (all[i]->dtype != 0 && all[i]->dtype != MOE_FP32 && all[i]->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  for (int i = 0; i < n; ++i)
+    if (grad_bf16(*all[i]) != grad_bf16(g->routed_gate)) return MOE_ERR_DTYPE;
   const int64_t H = p->hidden, I = p->intermediate;
   moe_status s;
-  if ((s = check_grad(g->shared_gate, H, false)) != MOE_OK) return s;
-  if ((s = check_grad(g->shared_up, H, false)) != MOE_OK) return s;
-  if ((s = check_grad(g->shared_down, I, false)) != MOE_OK) return s;
+  if (hs) {
+    if ((s = check_grad(g->shared_gate, H, false)) != MOE_OK) return s;
+    if ((s = check_grad(g->shared_up, H, false)) != MOE_OK) return s;
+    if ((s = check_grad(g->shared_down, I, false)) != MOE_OK) return s;
+  }
   if ((s = check_grad(g->routed_gate, H, true)) != MOE_OK) return s;
   if ((s = check_grad(g->routed_up, H, true)) != MOE_OK) return s;
   if ((s = check_grad(g->routed_down, I, true)) != MOE_OK) return s;
@@ -303,7 +311,7 @@ moe_status launch(const char* name, hipStream_t st, F&& f) {
 int64_t tok_bm(const Dims& d) { return d.mx ? gemm::bm_of<true>() : gemm::bm_of<false>(); }
 int64_t max_mtiles(const Dims& d) {
   const int64_t bm = tok_bm(d);
-  return (d.SM + bm - 1) / bm + d.E + (d.T + bm - 1) / bm;
+  return (d.SM + bm - 1) / bm + d.E + (d.hs ? (d.T + bm - 1) / bm : 0);
 }
 unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
 
@@ -383,7 +391,7 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
                          I32(L.top), F32(L.rw), I32(L.chunk_counts), I32(L.chunk_status));
   }));
   MOE_TRY(launch("route_scan", st, [&] {
-    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, I32(L.chunk_counts), nch, E, T, 1,
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, I32(L.chunk_counts), nch, E, T, d.hs ? 1 : 0,
                        (int)tok_bm(d), I32(L.chunk_base), I32(L.counts), I32(L.offsets), I32(L.tile_prefix),
                        I32(L.chunk_status), I32(L.status));
   }));
@@ -407,7 +415,7 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   ta.counts = I32(L.counts);
   ta.offsets = I32(L.offsets);
   ta.tile_prefix = I32(L.tile_prefix);
-  ta.T = T; ta.E = E; ta.groups = E + 1;
+  ta.T = T; ta.E = E; ta.groups = E + (d.hs ? 1 : 0);
   ta.shared_row0 = d.SM;
   const int64_t mt = max_mtiles(d);
 
@@ -472,7 +480,7 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
 
   // F7 combine
   MOE_TRY(launch("combine", st, [&] {
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kRowThreads), 0, st, U16(L.y), d.SM, H, K,
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kRowThreads), 0, st, U16(L.y), d.hs ? d.SM : -1, H, K,
                        I32(L.slot_of), F32(L.rw), static_cast<uint16_t*>(out));
   }));
   return MOE_OK;
@@ -520,7 +528,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   ta.counts = I32(L.counts);
   ta.offsets = I32(L.offsets);
   ta.tile_prefix = I32(L.tile_prefix);
-  ta.T = T; ta.E = E; ta.groups = E + 1;
+  ta.T = T; ta.E = E; ta.groups = E + (d.hs ? 1 : 0);
   ta.shared_row0 = d.SM;
   const int64_t mt = max_mtiles(d);
 
@@ -583,7 +591,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
 
   // B7 dx combine
   MOE_TRY(launch("dx_combine", st, [&] {
-    hipLaunchKernelGGL(k_dx_combine, dim3(T), dim3(kRowThreads), 0, st, WU16(B.dxp), d.SM, H, K,
+    hipLaunchKernelGGL(k_dx_combine, dim3(T), dim3(kRowThreads), 0, st, WU16(B.dxp), d.hs ? d.SM : -1, H, K,
                        I32(L.slot_of), static_cast<uint16_t*>(grad_hidden));
   }));
 
@@ -591,7 +599,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   gemm::WgradArgs a5;
   a5.counts = I32(L.counts);
   a5.offsets = I32(L.offsets);
-  a5.T = T; a5.E = E; a5.has_shared = 1;
+  a5.T = T; a5.E = E; a5.has_shared = d.hs ? 1 : 0;
   a5.a_r = WU16(B.dyw); a5.a_s = dy; a5.lda = H; a5.a_s_row0 = 0;
   a5.b_r = U16(L.h); a5.b_s = U16(L.h); a5.ldb = I; a5.b_s_row0 = d.SM;
   a5.g_lo = gradref(mg->routed_down); a5.g_hi = a5.g_lo;
@@ -601,8 +609,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   {
     const int per = gemm::wgrad_tiles_per_group(1, H, I);
     MOE_TRY(launch("wgrad_fc2", st, [&] {
-      const dim3 g(per + grid8((int64_t)E * per));
-      if (grad_bf16(mg->shared_gate)) hipLaunchKernelGGL((gemm::k_wgrad<2, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a5);
+      const dim3 g((d.hs ? per : 0) + grid8((int64_t)E * per));
+      if (grad_bf16(mg->routed_gate)) hipLaunchKernelGGL((gemm::k_wgrad<2, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a5);
       else hipLaunchKernelGGL((gemm::k_wgrad<2, false>), g, dim3(gemm::TL_WG::NTH), 0, st, a5);
     }));
   }
@@ -611,7 +619,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   gemm::WgradArgs a6;
   a6.counts = I32(L.counts);
   a6.offsets = I32(L.offsets);
-  a6.T = T; a6.E = E; a6.has_shared = 1;
+  a6.T = T; a6.E = E; a6.has_shared = d.hs ? 1 : 0;
   a6.a_r = WU16(B.dfc1); a6.a_s = WU16(B.dfc1); a6.lda = 2 * (int64_t)I; a6.a_s_row0 = d.SM;
   a6.b_r = U16(L.xp); a6.b_s = x; a6.ldb = H; a6.b_s_row0 = 0;
   a6.g_lo = gradref(mg->routed_gate); a6.g_hi = gradref(mg->routed_up);
@@ -621,8 +629,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   {
     const int per = gemm::wgrad_tiles_per_group(2, I, H);
     MOE_TRY(launch("wgrad_fc1", st, [&] {
-      const dim3 g(per + grid8((int64_t)E * per));
-      if (grad_bf16(mg->shared_gate)) hipLaunchKernelGGL((gemm::k_wgrad<1, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a6);
+      const dim3 g((d.hs ? per : 0) + grid8((int64_t)E * per));
+      if (grad_bf16(mg->routed_gate)) hipLaunchKernelGGL((gemm::k_wgrad<1, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a6);
       else hipLaunchKernelGGL((gemm::k_wgrad<1, false>), g, dim3(gemm::TL_WG::NTH), 0, st, a6);
     }));
   }

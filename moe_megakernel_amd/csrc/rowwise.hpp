@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
 }
 
 // out[t] = y[shared_row0 + t] + sum_k w_tk * y[slot_of[t,k]], in float, fixed k order,
-// one rounding to bf16.
+// one rounding to bf16.  shared_row0 < 0: no shared row (the sum starts from zero).
 __global__ __launch_bounds__(kRowThreads) void k_combine(
     const uint16_t* __restrict__ y, int64_t shared_row0, int H, int K,
     const int32_t* __restrict__ slot_of, const float* __restrict__ rw, uint16_t* __restrict__ out) {
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
   float w[kMaxTopk];
 #pragma unroll
   for (int k = 0; k < kMaxTopk; ++k) w[k] = (s[k] >= 0) ? rw[(int64_t)t * K + k] : 0.0f;
-  const uint4* ys = reinterpret_cast<const uint4*>(y + (shared_row0 + t) * (int64_t)H);
+  const uint4* ys = shared_row0 >= 0 ? reinterpret_cast<const uint4*>(y + (shared_row0 + t) * (int64_t)H) : nullptr;
   const int nc = H / 8;
   for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
     uint4 v[2], r[2][kMaxTopk];
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
     for (int u = 0; u < 2; ++u) {
       const int c = c0 + u * kRowThreads;
       if (c >= nc) break;
-      v[u] = ys[c];
+      v[u] = ys ? ys[c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int k = 0; k < kMaxTopk; ++k)
         if (s[k] >= 0) r[u][k] = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H)[c];
@@ -245,14 +245,16 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
   }
 }
 
-// dx[t] = dxp[shared_row0 + t] + sum_k dxp[slot_of[t,k]] (float, fixed order, one rounding).
+// dx[t] = dxp[shared_row0 + t] + sum_k dxp[slot_of[t,k]] (float, fixed order, one rounding);
+// shared_row0 < 0: no shared row.
 __global__ __launch_bounds__(kRowThreads) void k_dx_combine(
     const uint16_t* __restrict__ dxp, int64_t shared_row0, int H, int K,
     const int32_t* __restrict__ slot_of, uint16_t* __restrict__ dx) {
   const int t = blockIdx.x;
   int s[kMaxTopk];
   load_slots(slot_of, t, K, s);
-  const uint4* src = reinterpret_cast<const uint4*>(dxp + (shared_row0 + t) * (int64_t)H);
+  const uint4* src =
+      shared_row0 >= 0 ? reinterpret_cast<const uint4*>(dxp + (shared_row0 + t) * (int64_t)H) : nullptr;
   const int nc = H / 8;
   for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
     uint4 v[2], r[2][kMaxTopk];
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(kRowThreads) void k_dx_combine(
     for (int u = 0; u < 2; ++u) {
       const int c = c0 + u * kRowThreads;
       if (c >= nc) break;
-      v[u] = src[c];
+      v[u] = src ? src[c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int k = 0; k < kMaxTopk; ++k)
         if (s[k] >= 0) r[u][k] = reinterpret_cast<const uint4*>(dxp + (int64_t)s[k] * H)[c];

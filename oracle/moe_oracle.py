@@ -28,6 +28,10 @@ Readings of points the pages leave open:
     ascending token;
   * FC1 holds the gate rows [0, I) then the up rows [I, 2I);
   * the shared expert has weight 1 and no output gate;
+  * routed-only mode (Weights with shared=None; PR #8210, Summary and the review
+    thread on TP for the shared expert, name it as a follow-up that lets the
+    caller run the shared expert itself) drops the FFN_shared term from out and
+    from every gradient, and yields no shared weight gradient;
   * grad_probs is the full gradient of the dense probs tensor (zero off the
     map); main_grad receives the weight gradient by accumulation (+=), in FP32,
     or for a BF16 main_grad as described in main_grad_after;
@@ -217,7 +221,7 @@ class Weights:
     (Megatron Core API docs, mok.runtime, _MoKWeightArguments: shared gate,
     shared up, shared down, routed gate, routed up, routed down).
 
-    shared      : (Wg [I,H], Wu [I,H], Wd [H,I])
+    shared      : (Wg [I,H], Wu [I,H], Wd [H,I]), or None in routed-only mode
     routed(e)   : (Wg, Wu, Wd) as used by the forward
     routed_t(e) : (Wg, Wu, Wd) as used by dgrad (columnwise decode for MXFP8)
 
@@ -243,9 +247,11 @@ class Weights:
         (Megatron Core API docs, mok.runtime, _gate_up_weight_arguments: gate and up
         are row views of the combined FC1)."""
         I = inter
-        s1 = bf16_decode(shared_fc1)
-        s2 = bf16_decode(shared_fc2)
-        shared = (s1[:I], s1[I:2 * I], s2)
+        shared = None
+        if shared_fc1 is not None:
+            s1 = bf16_decode(shared_fc1)
+            s2 = bf16_decode(shared_fc2)
+            shared = (s1[:I], s1[I:2 * I], s2)
 
         if routed_dtype == "bf16":
             def fwd(e):
@@ -293,14 +299,18 @@ def moe_forward_f64(x, probs, routing_map, topk, weights: Weights, tokens=None):
 
     out[t] = FFN_shared(x_t) + sum over valid routes of w_tk * FFN_{e_tk}(x_t)
     (shared expert weight 1, no output gate: Megatron-LM PR #6572, Supported
-    configurations, the shared output gate is not supported).
+    configurations, the shared output gate is not supported).  Without a shared
+    expert (routed-only mode) the first term is absent.
     """
     T, E = routing_map.shape
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     top, rw = compact_routing(routing_map, probs, topk)
     x = np.asarray(x, dtype=np.float64)
     pos = {int(t): i for i, t in enumerate(tokens)}
-    _, _, _, out = swiglu_ffn(x, *weights.shared)
+    if weights.shared is not None:
+        _, _, _, out = swiglu_ffn(x, *weights.shared)
+    else:
+        out = np.zeros_like(x)
     for e, lst in enumerate(_routes_by_expert(top, rw, tokens, E)):
         if not lst:
             continue
@@ -328,6 +338,7 @@ def moe_backward_f64(dy_all, x_all, probs, routing_map, topk, weights: Weights,
       dprobs  float64 [len(tokens), E]        zero where routing_map is false
       dW      {e: (dWg, dWu, dWd)} for e in `experts` (all when None), computed from
               every token routed to e;  "shared": (dWg, dWu, dWd) when shared_grads
+              and the layer has a shared expert
 
     Per route (t, k) to expert e with weight w, g = dy[t]:
       a = Wg x, b = Wu x, h = silu(a) b, y = Wd h
@@ -355,12 +366,13 @@ def moe_backward_f64(dy_all, x_all, probs, routing_map, topk, weights: Weights,
     dx = np.zeros_like(x)
     dprobs = np.zeros((len(tokens), E))
 
-    Wg, Wu, Wd = weights.shared
-    a, b, h, _ = swiglu_ffn(x, Wg, Wu, Wd)
-    gh = g @ Wd
-    da = gh * b * dsilu(a)
-    db = gh * silu(a)
-    dx += da @ Wg + db @ Wu
+    if weights.shared is not None:
+        Wg, Wu, Wd = weights.shared
+        a, b, h, _ = swiglu_ffn(x, Wg, Wu, Wd)
+        gh = g @ Wd
+        da = gh * b * dsilu(a)
+        db = gh * silu(a)
+        dx += da @ Wg + db @ Wu
 
     for e, lst in enumerate(_routes_by_expert(top, rw, tokens, E)):
         if not lst:
@@ -399,7 +411,7 @@ def moe_backward_f64(dy_all, x_all, probs, routing_map, topk, weights: Weights,
             da = gh * b * dsilu(a)
             db = gh * silu(a)
             dW[e] = (da.T @ X, db.T @ X, (w[:, None] * G).T @ h)
-    if shared_grads:
+    if shared_grads and weights.shared is not None:
         X = x_all
         G = dy_all
         Wg, Wu, Wd = weights.shared

@@ -3,6 +3,8 @@ expert is applied to every token and masked by routing_map * probs.
 
     out = FFN_shared(x) + sum_e (routing_map[:, e] * probs[:, e]) * FFN_e(x)
 
+(without the first term when `shared` is None: routed-only mode).
+
 It never builds the fixed-width table nor the dispatch permutation, and its
 backward comes from torch autograd, so it shares neither the oracle's
 formulation nor its hand-derived gradients.  Test infrastructure only.
@@ -18,7 +20,7 @@ def dense_forward(x, probs, rmap, shared, routed):
         gu = xx @ w1.t()
         return (F.silu(gu[:, :I]) * gu[:, I:]) @ w2.t()
 
-    out = ffn(x, *shared)
+    out = ffn(x, *shared) if shared is not None else torch.zeros_like(x)
     mask = rmap.to(x.dtype) * probs
     for e in range(routed[0].shape[0]):
         out = out + mask[:, e:e + 1] * ffn(x, routed[0][e], routed[1][e])
@@ -27,9 +29,11 @@ def dense_forward(x, probs, rmap, shared, routed):
 
 def dense_grads(x, probs, rmap, shared, routed, dy):
     """Autograd gradients of sum(dy * out) w.r.t. x, probs, shared and routed weights."""
+    sh = shared if shared is not None else (torch.zeros(1), torch.zeros(1))
     leaves = [t.detach().clone().requires_grad_(True)
-              for t in (x, probs, shared[0], shared[1], routed[0], routed[1])]
-    out = dense_forward(leaves[0], leaves[1], rmap, (leaves[2], leaves[3]), (leaves[4], leaves[5]))
+              for t in (x, probs, sh[0], sh[1], routed[0], routed[1])]
+    out = dense_forward(leaves[0], leaves[1], rmap,
+                        (leaves[2], leaves[3]) if shared is not None else None, (leaves[4], leaves[5]))
     (out * dy).sum().backward()
     g = [t.grad for t in leaves]
     return {"out": out.detach(), "dx": g[0], "dprobs": g[1] * rmap.to(g[1].dtype),

@@ -22,7 +22,9 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 def oracle_weights(dp) -> "O.Weights":
     cfg = dp.cfg
-    return O.Weights.from_bits(cfg.inter, dp.np_s1, dp.np_s2, lambda e: dp.np_routed[e], cfg.routed)
+    shared = getattr(dp, "shared", True)
+    return O.Weights.from_bits(cfg.inter, dp.np_s1 if shared else None, dp.np_s2 if shared else None,
+                               lambda e: dp.np_routed[e], cfg.routed)
 
 
 def check_routing_state(dp):

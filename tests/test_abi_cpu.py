@@ -78,7 +78,7 @@ def test_invalid_problem_is_rejected(kw, status):
 
 def test_unsupported_configurations_are_rejected():
     p = _ok_problem()
-    p.flags = 0                                   # no shared expert
+    p.flags = 2                                   # an unknown flag bit
     assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_UNSUPPORTED
     p = _ok_problem()
     p.swiglu_limit = 7.0                          # clamp not supported
@@ -169,3 +169,36 @@ def test_main_grad_dtype_validation():
     assert mk.moe_backward(p, a, a, w, a, a, a, mixed, a, 1 << 30, 0) == mk.MOE_ERR_DTYPE
     bad = mk.moe_main_grads(G(H), G(H, I), G(I), G(H), G(H, I), G(I, 0, mk.MOE_MXFP8_E4M3))
     assert mk.moe_backward(p, a, a, w, a, a, a, bad, a, 1 << 30, 0) == mk.MOE_ERR_DTYPE
+
+
+def test_routed_only_mode_ignores_shared_descriptors():
+    """flags = 0 (routed-only): shared weights and shared main_grads are not validated,
+    the saved context drops the T shared rows, and the routed ones are still checked."""
+    p = _ok_problem()
+    full = mk.moe_saved_bytes(p)
+    p.flags = 0
+    assert 0 < mk.moe_saved_bytes(p) < full
+    assert mk.moe_workspace_bytes(p, 1) < mk.moe_workspace_bytes(_ok_problem(), 1)
+    a = 1 << 41
+    w = _fake_weights(p)
+    w.shared_gate = mk.moe_weight()
+    w.shared_up = mk.moe_weight()
+    w.shared_down = mk.moe_weight()
+    assert mk.moe_forward(p, a, a, a, w, a, a, 0, 0, 0) == mk.MOE_ERR_WORKSPACE   # weights accepted
+    H, I = p.hidden, p.intermediate
+    G = lambda ld, ro=0, dt=0: mk.moe_grad(a, 0, 0, ld, ro, dt)
+    Z = mk.moe_grad()
+    bf = mk.MOE_BF16
+    g = mk.moe_main_grads(Z, Z, Z, G(H), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 16, 0) == mk.MOE_ERR_WORKSPACE      # accepted
+    g = mk.moe_main_grads(Z, Z, Z, G(H, 0, bf), G(H, I, bf), G(I, 0, bf))                 # BF16, shared 0
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 16, 0) == mk.MOE_ERR_WORKSPACE
+    g = mk.moe_main_grads(Z, Z, Z, G(H, 0, bf), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 1 << 30, 0) == mk.MOE_ERR_DTYPE
+    w.routed_down.rows = 128
+    assert mk.moe_forward(p, a, a, a, w, a, a, a, 1 << 20, 0) == mk.MOE_ERR_SHAPE
+    # with the flag set, the same all-zero shared descriptors are rejected
+    p.flags = mk.MOE_FLAG_HAS_SHARED
+    w = _fake_weights(p)
+    w.shared_down = mk.moe_weight()
+    assert mk.moe_forward(p, a, a, a, w, a, a, a, 1 << 20, 0) != mk.MOE_OK

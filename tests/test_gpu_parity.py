@@ -51,10 +51,14 @@ def _check_backward(dp, W, tokens=None, experts=None, tol=BF16_TOL):
         errs[f"down{e}"] = rel_err(d2, dd) if np.abs(dd).max() > 0 else float(np.abs(d2).max())
     s1 = to_f64(dp.mg_s1) - dp.main_grad_start((2 * I, cfg.hidden), 0)
     s2 = to_f64(dp.mg_s2) - dp.main_grad_start((cfg.hidden, I), 0)
-    dg, du, dd = g["dW"]["shared"]
-    errs["shared_gate"] = rel_err(s1[:I], dg)
-    errs["shared_up"] = rel_err(s1[I:], du)
-    errs["shared_down"] = rel_err(s2, dd)
+    if dp.shared:
+        dg, du, dd = g["dW"]["shared"]
+        errs["shared_gate"] = rel_err(s1[:I], dg)
+        errs["shared_up"] = rel_err(s1[I:], du)
+        errs["shared_down"] = rel_err(s2, dd)
+    else:   # routed-only: the shared main_grad buffers were not handed over and stay as they were
+        assert "shared" not in g["dW"]
+        assert np.all(s1 == 0) and np.all(s2 == 0)
     worst = max(errs, key=lambda k: errs[k])
     print(f"[parity] dx {errs['dx']:.3e} dprobs {errs['dprobs']:.3e} worst {worst} {errs[worst]:.3e} "
           f"(tol {tol})", flush=True)
@@ -295,6 +299,73 @@ def test_hip_graph_replay_matches_eager(gpu_lib):
             a, b = getattr(dp, n), eager[n]
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, n)
+
+
+# ----------------------------------------------------------------------------------
+# routed-only mode: no fused shared expert (flags = 0); out, dx and the main_grads hold
+# the routed terms only
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("routed,layout,shape", [
+    ("bf16", "single", (777, 384, 13, 4, 256)),
+    ("bf16", "table", (1, 128, 3, 2, 128)),
+    ("mxfp8", "table", (300, 256, 6, 3, 128)),
+    ("mxfp8", "single", (520, 384, 9, 2, 256)),
+])
+def test_routed_only_forward_backward_matches_oracle(gpu_lib, routed, layout, shape):
+    T, H, E, K, I = shape
+    cfg = gen.custom(T, H, E, K, I, routed=routed, layout=layout, short_frac=0.1, short_max=max(1, K - 1),
+                     idx=500 + T)
+    dp = _dp(cfg, shared=False)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    assert W.shared is None
+    tol = BF16_TOL if routed == "bf16" else MXFP8_TOL
+    _check_forward(dp, W, tol=tol)
+    _check_backward(dp, W, tol=tol)
+
+
+def test_routed_only_empty_map_gives_exact_zeros(gpu_lib):
+    cfg = gen.custom(200, 256, 6, 2, 128, idx=501)
+    dp = _dp(cfg, shared=False, routing=(np.zeros((200, 6), np.float32), np.zeros((200, 6), np.uint8)))
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    assert float(dp.out.float().abs().max()) == 0.0
+    assert float(dp.dx.float().abs().max()) == 0.0
+    assert float(dp.dprobs.abs().max()) == 0.0
+    W = oracle_weights(dp)
+    _check_backward(dp, W)
+
+
+def test_routed_only_full_size_sampled(gpu_lib):
+    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 without the shared expert;
+    sampled tokens and experts.  The fused run minus the routed-only run is the shared
+    expert's output, a dense SwiGLU MLP on every token."""
+    cfg = gen.config(2)
+    dp = _dp(cfg, shared=False)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    toks = sample_tokens(cfg.tokens, 32, seed=7)
+    _check_forward(dp, W, tokens=toks)
+    _check_backward(dp, W, tokens=toks, experts=[0, 50, cfg.experts - 1])
+    routed_out = to_f64(dp.out[torch.as_tensor(toks, device=dp.out.device)])
+    del dp
+    full = _dp(cfg, backward=False)
+    full.forward()
+    torch.cuda.synchronize()
+    Wf = oracle_weights(full)
+    x = O.bf16_decode(full.np_x[toks])
+    _, _, _, mlp = O.swiglu_ffn(x, *Wf.shared)
+    diff = to_f64(full.out[torch.as_tensor(toks, device=full.out.device)]) - routed_out
+    err = rel_err(diff, mlp)
+    print(f"[parity] fused - routed-only vs shared MLP: rel err {err:.3e}", flush=True)
+    assert err <= 2 * BF16_TOL
 
 
 # ----------------------------------------------------------------------------------

@@ -243,6 +243,45 @@ def test_backward_matches_dense_autograd(shape):
     assert I == d["shared"][1].shape[1]
 
 
+@pytest.mark.parametrize("shape", [(16, 32, 4, 2, 16), (24, 64, 5, 3, 32)])
+def test_routed_only_matches_dense_formulation(shape):
+    """Routed-only mode (no shared expert) against the dense form without FFN_shared."""
+    cfg, probs, rmap, x, dy, W, d = _small_problem(*shape, seed=19, short=0.25)
+    Wr = O.Weights(None, W.routed)
+    out = O.moe_forward(x, probs, rmap, cfg.topk, Wr)
+    ref_out = dense_forward(d["x"], d["probs"], d["rmap"], None, d["routed"]).numpy()
+    assert _rel(out, ref_out) < 1e-12
+    g = O.moe_backward(dy, x, probs, rmap, cfg.topk, Wr)
+    ref = dense_grads(d["x"], d["probs"], d["rmap"], None, d["routed"], d["dy"])
+    assert _rel(g["dx"], ref["dx"].numpy()) < 1e-12
+    assert _rel(g["dprobs"], ref["dprobs"].numpy()) < 1e-12
+    for e in range(cfg.experts):
+        dg, du, dd = g["dW"][e]
+        assert _rel(np.concatenate([dg, du]), ref["drouted1"][e].numpy()) < 1e-12
+        assert _rel(dd, ref["drouted2"][e].numpy()) < 1e-12
+    assert "shared" not in g["dW"]
+    # the fused layer is the routed-only layer plus one dense SwiGLU MLP on every token
+    full = O.moe_forward(x, probs, rmap, cfg.topk, W)
+    mlp = _textbook_swiglu(O.bf16_decode(x), np.concatenate(W.shared[:2]), W.shared[2])
+    assert _rel(full - out, mlp) < 1e-12
+
+
+def test_routed_only_edge_cases():
+    cfg, probs, rmap, x, dy, W, d = _small_problem(8, 32, 1, 1, 16, seed=20)
+    Wr = O.Weights(None, W.routed)
+    xs = O.bf16_decode(x)
+    # no route at all: output and every gradient are exactly zero
+    z = np.zeros_like(rmap)
+    assert np.all(O.moe_forward(x, probs, z, 1, Wr) == 0)
+    g = O.moe_backward(dy, x, probs, z, 1, Wr)
+    assert np.all(g["dx"] == 0) and np.all(g["dprobs"] == 0)
+    assert all(np.all(m == 0) for m in g["dW"][0])
+    # one expert, every token routed with weight 1: a single dense SwiGLU MLP
+    out = O.moe_forward(x, np.ones_like(probs), np.ones_like(rmap), 1, Wr)
+    wg, wu, wd = W.routed(0)
+    assert _rel(out, _textbook_swiglu(xs, np.concatenate([wg, wu]), wd)) < 1e-13
+
+
 def test_sampled_rows_and_experts_equal_full_run():
     cfg, probs, rmap, x, dy, W, d = _small_problem(30, 32, 5, 2, 16, seed=13, short=0.2)
     full = O.moe_backward(dy, x, probs, rmap, cfg.topk, W)
