@@ -41,6 +41,9 @@ def parse():
                     help="main_grad dtype (bf16: contribution rounded to BF16 before a BF16 reduction-store)")
     ap.add_argument("--routed-only", action="store_true",
                     help="no fused shared expert (the layer's routed terms only)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="MoE-layer recompute: saved holds the routing state only; the backward "
+                         "regenerates the activations (same flops counted: the recomputation is overhead)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before the steps (a known-size "
                          "reference for the HBM byte counters)")
@@ -148,7 +151,8 @@ def main():
     cfg = gen.config(args.config)
     t0 = time.time()
     shared = not args.routed_only
-    dp = DeviceProblem(cfg, backward=True, main_grad_dtype=args.main_grad, shared=shared)
+    dp = DeviceProblem(cfg, backward=True, main_grad_dtype=args.main_grad, shared=shared,
+                       recompute=args.recompute)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s: {cfg.name}", file=sys.stderr, flush=True)
 
@@ -208,6 +212,7 @@ def main():
                    "experts": cfg.experts, "topk": cfg.topk, "intermediate": cfg.inter,
                    "routed_slots": slots, "routed_weights": cfg.routed, "layout": cfg.layout,
                    "routing": cfg.routing, "main_grad": args.main_grad, "shared_expert": shared,
+                   "recompute": bool(args.recompute), "saved_bytes": int(dp.layer.saved.numel()),
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},

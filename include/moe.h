@@ -65,6 +65,14 @@ typedef enum { MOE_BF16 = 1, MOE_FP32 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
  * data gradient then hold the routed terms only, and the shared weights and shared
  * main_grad buffers are neither validated nor touched (they may be all zero/NULL). */
 #define MOE_FLAG_HAS_SHARED 1u
+/* Set: MoE-layer recompute (PR #6572, Validation: MoE layer recompute; PR #8210, Summary:
+ * whole-MoE recomputation).  `saved` then holds only the routing state (a few bytes per
+ * token); the forward keeps its activations in its workspace, and moe_backward
+ * regenerates them from `hidden` with the same kernels before the backward proper, so
+ * every result is bit-identical to the mode without the flag.  The flag must be the same
+ * in the forward and the backward of one layer call, and the workspaces grow by the
+ * activations (see moe_workspace_bytes). */
+#define MOE_FLAG_RECOMPUTE 2u
 
 /* Problem sizes and options. */
 typedef struct {
@@ -74,7 +82,7 @@ typedef struct {
   int32_t experts;       /* E in [1, 255]                                                 */
   int32_t topk;          /* K in [1, min(8, E)]                                           */
   int32_t routed_dtype;  /* MOE_BF16 or MOE_MXFP8_E4M3 (PR #6572, Supported configurations) */
-  uint32_t flags;        /* MOE_FLAG_HAS_SHARED or 0 (routed-only)                        */
+  uint32_t flags;        /* MOE_FLAG_HAS_SHARED (else routed-only) | MOE_FLAG_RECOMPUTE  */
   float swiglu_limit;    /* must be 0 (no clamp)                                          */
 } moe_problem;
 

@@ -38,11 +38,14 @@ def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
 
 class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
-                 routing=None, main_grad_dtype: str = "fp32", shared: bool = True):
+                 routing=None, main_grad_dtype: str = "fp32", shared: bool = True,
+                 recompute: bool = False):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
         configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16".
         shared=False: routed-only mode; the shared weight and main_grad descriptors are
-        passed all zero (the library must not touch them)."""
+        passed all zero (the library must not touch them).  recompute=True: MoE-layer
+        recompute mode (saved holds the routing state only; the backward regenerates the
+        activations)."""
         self.cfg = cfg
         self.device = device
         T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
@@ -65,7 +68,8 @@ class DeviceProblem:
         mx = cfg.routed == "mxfp8"
         dt = mk.MOE_MXFP8_E4M3 if mx else mk.MOE_BF16
         self.shared = shared
-        self.p = mk.problem(T, H, I, E, K, dt, flags=mk.MOE_FLAG_HAS_SHARED if shared else 0)
+        flags = (mk.MOE_FLAG_HAS_SHARED if shared else 0) | (mk.MOE_FLAG_RECOMPUTE if recompute else 0)
+        self.p = mk.problem(T, H, I, E, K, dt, flags=flags)
 
         def routed_mat(key, rows, cols, conv, elem_cols):
             """moe_mat for a routed tensor stored [E][rows][cols] (single) or per expert (table)."""

@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_LAYOUT = 0, 1, 2, 3,
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_ROUTE_OVERFLOW, MOE_ERR_HIP = 5, 6, 7, 8
 MOE_BF16, MOE_FP32, MOE_MXFP8_E4M3 = 1, 2, 3
 MOE_FLAG_HAS_SHARED = 1
+MOE_FLAG_RECOMPUTE = 2
 
 EXPORTED = ("moe_saved_bytes", "moe_workspace_bytes", "moe_saved_view", "moe_forward",
             "moe_backward", "moe_status_str", "moe_kernel_timer_enable", "moe_kernel_timer_read")

@@ -30,6 +30,7 @@ struct Dims {
   int64_t nchunks;
   bool mx;
   bool hs;           // the shared expert is fused in
+  bool rc;           // recompute: saved holds the routing state only
 };
 
 Dims dims_of(const moe_problem* p) {
@@ -40,13 +41,34 @@ Dims dims_of(const moe_problem* p) {
   d.R = d.SM + (d.hs ? d.T : 0);
   d.nchunks = (d.T + kRouteChunk - 1) / kRouteChunk;
   d.mx = p->routed_dtype == MOE_MXFP8_E4M3;
+  d.rc = (p->flags & MOE_FLAG_RECOMPUTE) != 0;
   return d;
+}
+
+// The forward's activations the backward reads: the gathered routed input xp, the FC1
+// output ab = [a | b], h = silu(a) * b and the unweighted FC2 output y (routed rows, then
+// the shared expert's T rows).  Placed at the end of `saved`, or in recompute mode at the
+// start of the forward and backward workspaces.
+struct ActLayout {
+  size_t xp, ab, h, y, end;
+};
+
+ActLayout act_layout(const Dims& d, size_t o) {
+  ActLayout A;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  A.xp = take(2 * d.SM * d.H);
+  A.ab = take(2 * d.R * 2 * d.I);
+  A.h = take(2 * d.R * d.I);
+  A.y = take(2 * d.R * d.H);
+  A.end = o;
+  return A;
 }
 
 // Byte offsets inside `saved`.
 struct SavedLayout {
   size_t top, rw, counts, offsets, slot_of, slot_token, status, slot_w, tile_prefix, chunk_base,
-      chunk_counts, chunk_status, xp, ab, h, y, total;
+      chunk_counts, chunk_status, total;
+  ActLayout act;     // not in recompute mode
 };
 
 SavedLayout saved_layout(const Dims& d) {
@@ -65,25 +87,38 @@ SavedLayout saved_layout(const Dims& d) {
   L.chunk_base = take(4 * d.nchunks * d.E);
   L.chunk_counts = take(4 * d.nchunks * d.E);
   L.chunk_status = take(4 * d.nchunks);
-  L.xp = take(2 * d.SM * d.H);
-  L.ab = take(2 * d.R * 2 * d.I);
-  L.h = take(2 * d.R * d.I);
-  L.y = take(2 * d.R * d.H);
+  L.act = ActLayout{};
+  if (!d.rc) {
+    L.act = act_layout(d, o);
+    o = L.act.end;
+  }
   L.total = o;
   return L;
 }
 
+// Backward workspace.  In recompute mode it starts with the activations the backward
+// regenerates; y is dead once the dy gather has read it, so the FC1 data gradient dxp
+// (the same [R][H] bf16 shape) reuses its bytes, and the forward's MXFP8 staging (xq, xs,
+// hq, hs) sits inside the backward's (dyq, dys, dfq, dfs; each at least as large), whose
+// first writer runs after the recomputed FC2 has consumed it.
 struct BwdLayout {
   size_t dyw, dfc1, dxp, dyq, dys, dfq, dfs, total;
+  ActLayout act;                 // recompute mode only
+  size_t fxq, fxs, fhq, fhs;     // recompute mode, MXFP8 only
 };
 
 BwdLayout bwd_layout(const Dims& d) {
   BwdLayout L;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  L.act = ActLayout{};
+  if (d.rc) {
+    L.act = act_layout(d, 0);
+    o = L.act.end;
+  }
   L.dyw = take(2 * d.SM * d.H);
   L.dfc1 = take(2 * d.R * 2 * d.I);
-  L.dxp = take(2 * d.R * d.H);
+  L.dxp = d.rc ? L.act.y : take(2 * d.R * d.H);
   L.dyq = L.dys = L.dfq = L.dfs = 0;
   if (d.mx) {   // MXFP8 codes + scales of the routed data-gradient GEMM inputs
     L.dyq = take(d.SM * d.H);
@@ -91,19 +126,26 @@ BwdLayout bwd_layout(const Dims& d) {
     L.dfq = take(d.SM * 2 * d.I);
     L.dfs = take(d.SM * 2 * d.I / 32);
   }
+  L.fxq = L.dyq; L.fxs = L.dys; L.fhq = L.dfq; L.fhs = L.dfs;
   L.total = o;
   return L;
 }
 
-// Forward workspace: MXFP8 codes + scales of the routed FC1 input (x) and FC2 input (h).
+// Forward workspace: the activations in recompute mode, then the MXFP8 codes + scales of
+// the routed FC1 input (x) and FC2 input (h).
 struct FwdLayout {
   size_t xq, xs, hq, hs, total;
+  ActLayout act;     // recompute mode only
 };
 
 FwdLayout fwd_layout(const Dims& d) {
   FwdLayout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+  if (d.rc) {
+    L.act = act_layout(d, 0);
+    o = L.act.end;
+  }
   if (d.mx) {
     L.xq = take(d.SM * d.H);
     L.xs = take(d.SM * d.H / 32);
@@ -127,7 +169,7 @@ moe_status check_problem(const moe_problem* p) {
   if (p->topk < 1 || p->topk > kMaxTopk || p->topk > p->experts) return MOE_ERR_SHAPE;
   if (p->tokens * (int64_t)p->topk > (int64_t)1 << 30) return MOE_ERR_SHAPE;
   if (p->hidden > (1 << 20) || p->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
-  if (p->flags & ~MOE_FLAG_HAS_SHARED) return MOE_ERR_UNSUPPORTED;
+  if (p->flags & ~(MOE_FLAG_HAS_SHARED | MOE_FLAG_RECOMPUTE)) return MOE_ERR_UNSUPPORTED;
   if (p->swiglu_limit != 0.0f) return MOE_ERR_UNSUPPORTED;
   if (p->routed_dtype != MOE_BF16 && p->routed_dtype != MOE_MXFP8_E4M3) return MOE_ERR_DTYPE;
   return MOE_OK;
@@ -315,6 +357,100 @@ int64_t max_mtiles(const Dims& d) {
 }
 unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
 
+// Pointers of one run of the routed + shared expert forward (F3-F6).
+struct FwdPtrs {
+  const int32_t *slot_of, *counts, *offsets, *tile_prefix;
+  uint16_t *xp, *ab, *h, *y;
+  uint8_t *xq, *xs, *hq, *hs;   // MXFP8 staging (unused for BF16 routed weights)
+};
+
+// Dispatch gather, FC1 + SwiGLU, FC2 (routed and shared expert in the same launches),
+// from the routing state already in place.  `again`: the backward's recomputation in
+// recompute mode (the same kernels on the same inputs, so the same bits; only the timer
+// names differ).
+moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, const moe_weights* w,
+                           hipStream_t st, bool again) {
+  const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
+  // F3 dispatch gather (+ Q: MXFP8 codes of the routed FC1 input)
+  MOE_TRY(launch(again ? "recompute_gather_x" : "gather_x", st, [&] {
+    if (d.mx)
+      hipLaunchKernelGGL(k_gather_rows<true>, dim3(T), dim3(kRowThreads), 0, st,
+                         x, H, K, P.slot_of, P.xp, P.xq, P.xs);
+    else
+      hipLaunchKernelGGL(k_gather_rows<false>, dim3(T), dim3(kRowThreads), 0, st,
+                         x, H, K, P.slot_of, P.xp, (uint8_t*)nullptr, (uint8_t*)nullptr);
+  }));
+
+  gemm::TokArgs ta;
+  ta.counts = P.counts;
+  ta.offsets = P.offsets;
+  ta.tile_prefix = P.tile_prefix;
+  ta.T = T; ta.E = E; ta.groups = E + (d.hs ? 1 : 0);
+  ta.shared_row0 = d.SM;
+  const int64_t mt = max_mtiles(d);
+
+  // F4 + F6: routed and shared FC1 with the SwiGLU epilogue, one launch
+  gemm::Fc1Args a1;
+  a1.t = ta;
+  a1.xp = P.xp;
+  a1.x = x;
+  a1.wg = matref(w->routed_gate, w->routed_gate.data, 2);
+  a1.wu = matref(w->routed_up, w->routed_up.data, 2);
+  a1.sg = matref(w->shared_gate, w->shared_gate.data, 2);
+  a1.su = matref(w->shared_up, w->shared_up.data, 2);
+  a1.ab = P.ab;
+  a1.h = P.h;
+  a1.H = H; a1.I = I;
+  a1.mx = gemm::MxOperands{};
+  if (d.mx) {
+    a1.mx.aq = P.xq;
+    a1.mx.as = P.xs;
+    a1.mx.b0 = mxref(w->routed_gate, false);
+    a1.mx.b1 = mxref(w->routed_up, false);
+  }
+  MOE_TRY(launch(again ? "recompute_fc1_swiglu" : "fc1_swiglu", st, [&] {
+    using S1 = gemm::Shapes<true>::FC1;
+    using S0 = gemm::Shapes<false>::FC1;
+    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, dim3(grid8(mt * (2 * I / S1::TN))), dim3(S1::NTH), 0, st, a1);
+    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, dim3(grid8(mt * (2 * I / S0::TN))), dim3(S0::NTH), 0, st, a1);
+  }));
+  if (d.mx) {   // Q: MXFP8 codes of the routed FC2 input h
+    MOE_TRY(launch(again ? "recompute_quantize_h" : "quantize_h", st, [&] {
+      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, P.h, d.SM, I, P.offsets + E, P.hq,
+                         P.hs);
+    }));
+  }
+
+  // F5 + F6: routed and shared FC2 -> y (unweighted)
+  gemm::PlainArgs a2;
+  a2.t = ta;
+  a2.a_r = P.h;
+  a2.a_s = P.h;
+  a2.a_s_row0 = d.SM;
+  a2.w0 = matref(w->routed_down, w->routed_down.data, 2);
+  a2.w1 = a2.w0;
+  a2.s0 = matref(w->shared_down, w->shared_down.data, 2);
+  a2.s1 = a2.s0;
+  a2.ksplit = I;
+  a2.c = P.y;
+  a2.N = H; a2.K = I;
+  a2.mx = gemm::MxOperands{};
+  if (d.mx) {
+    a2.mx.aq = P.hq;
+    a2.mx.as = P.hs;
+    a2.mx.b0 = mxref(w->routed_down, false);
+    a2.mx.b1 = a2.mx.b0;
+  }
+  MOE_TRY(launch(again ? "recompute_fc2" : "fc2", st, [&] {
+    using S1 = gemm::Shapes<true>::FC2;
+    using S0 = gemm::Shapes<false>::FC2;
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), dim3(grid8(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a2);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), dim3(grid8(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a2);
+  }));
+  return MOE_OK;
+}
+
+
 }  // namespace
 
 // ================================================================== C ABI
@@ -379,7 +515,10 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   uint8_t* S = static_cast<uint8_t*>(saved);
   auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(S + off); };
   auto F32 = [&](size_t off) { return reinterpret_cast<float*>(S + off); };
-  auto U16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(S + off); };
+  // activations: in `saved`, or in recompute mode in the workspace
+  uint8_t* AB = d.rc ? WS : S;
+  const ActLayout A = d.rc ? F.act : L.act;
+  auto U16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(AB + off); };
 
   const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
   const int nch = (int)d.nchunks;
@@ -400,87 +539,16 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
     hipLaunchKernelGGL(k_route_rank, dim3(nch), dim3(kRouteChunk * kMaxTopk), 0, st, I32(L.top), F32(L.rw), T, E, K,
                        I32(L.chunk_base), I32(L.offsets), I32(L.slot_of), I32(L.slot_token), F32(L.slot_w));
   }));
-  // F3 dispatch gather (+ Q: MXFP8 codes of the routed FC1 input)
-  MOE_TRY(launch("gather_x", st, [&] {
-    if (d.mx)
-      hipLaunchKernelGGL(k_gather_rows<true>, dim3(T), dim3(kRowThreads), 0, st,
-                         static_cast<const uint16_t*>(hidden), H, K, I32(L.slot_of), U16(L.xp), WS + F.xq, WS + F.xs);
-    else
-      hipLaunchKernelGGL(k_gather_rows<false>, dim3(T), dim3(kRowThreads), 0, st,
-                         static_cast<const uint16_t*>(hidden), H, K, I32(L.slot_of), U16(L.xp),
-                         (uint8_t*)nullptr, (uint8_t*)nullptr);
-  }));
-
-  gemm::TokArgs ta;
-  ta.counts = I32(L.counts);
-  ta.offsets = I32(L.offsets);
-  ta.tile_prefix = I32(L.tile_prefix);
-  ta.T = T; ta.E = E; ta.groups = E + (d.hs ? 1 : 0);
-  ta.shared_row0 = d.SM;
-  const int64_t mt = max_mtiles(d);
-
-  // F4 + F6: routed and shared FC1 with the SwiGLU epilogue, one launch
-  gemm::Fc1Args a1;
-  a1.t = ta;
-  a1.xp = U16(L.xp);
-  a1.x = static_cast<const uint16_t*>(hidden);
-  a1.wg = matref(w->routed_gate, w->routed_gate.data, 2);
-  a1.wu = matref(w->routed_up, w->routed_up.data, 2);
-  a1.sg = matref(w->shared_gate, w->shared_gate.data, 2);
-  a1.su = matref(w->shared_up, w->shared_up.data, 2);
-  a1.ab = U16(L.ab);
-  a1.h = U16(L.h);
-  a1.H = H; a1.I = I;
-  a1.mx = gemm::MxOperands{};
-  if (d.mx) {
-    a1.mx.aq = WS + F.xq;
-    a1.mx.as = WS + F.xs;
-    a1.mx.b0 = mxref(w->routed_gate, false);
-    a1.mx.b1 = mxref(w->routed_up, false);
-  }
-  MOE_TRY(launch("fc1_swiglu", st, [&] {
-    using S1 = gemm::Shapes<true>::FC1;
-    using S0 = gemm::Shapes<false>::FC1;
-    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, dim3(grid8(mt * (2 * I / S1::TN))), dim3(S1::NTH), 0, st, a1);
-    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, dim3(grid8(mt * (2 * I / S0::TN))), dim3(S0::NTH), 0, st, a1);
-  }));
-  if (d.mx) {   // Q: MXFP8 codes of the routed FC2 input h
-    MOE_TRY(launch("quantize_h", st, [&] {
-      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, U16(L.h), d.SM, I,
-                         I32(L.offsets) + E, WS + F.hq, WS + F.hs);
-    }));
-  }
-
-  // F5 + F6: routed and shared FC2 -> y (unweighted)
-  gemm::PlainArgs a2;
-  a2.t = ta;
-  a2.a_r = U16(L.h);
-  a2.a_s = U16(L.h);
-  a2.a_s_row0 = d.SM;
-  a2.w0 = matref(w->routed_down, w->routed_down.data, 2);
-  a2.w1 = a2.w0;
-  a2.s0 = matref(w->shared_down, w->shared_down.data, 2);
-  a2.s1 = a2.s0;
-  a2.ksplit = I;
-  a2.c = U16(L.y);
-  a2.N = H; a2.K = I;
-  a2.mx = gemm::MxOperands{};
-  if (d.mx) {
-    a2.mx.aq = WS + F.hq;
-    a2.mx.as = WS + F.hs;
-    a2.mx.b0 = mxref(w->routed_down, false);
-    a2.mx.b1 = a2.mx.b0;
-  }
-  MOE_TRY(launch("fc2", st, [&] {
-    using S1 = gemm::Shapes<true>::FC2;
-    using S0 = gemm::Shapes<false>::FC2;
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), dim3(grid8(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a2);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), dim3(grid8(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a2);
-  }));
+  FwdPtrs P;
+  P.slot_of = I32(L.slot_of); P.counts = I32(L.counts); P.offsets = I32(L.offsets);
+  P.tile_prefix = I32(L.tile_prefix);
+  P.xp = U16(A.xp); P.ab = U16(A.ab); P.h = U16(A.h); P.y = U16(A.y);
+  P.xq = WS + F.xq; P.xs = WS + F.xs; P.hq = WS + F.hq; P.hs = WS + F.hs;
+  MOE_TRY(experts_forward(d, P, static_cast<const uint16_t*>(hidden), w, st, false));
 
   // F7 combine
   MOE_TRY(launch("combine", st, [&] {
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kRowThreads), 0, st, U16(L.y), d.hs ? d.SM : -1, H, K,
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kRowThreads), 0, st, P.y, d.hs ? d.SM : -1, H, K,
                        I32(L.slot_of), F32(L.rw), static_cast<uint16_t*>(out));
   }));
   return MOE_OK;
@@ -507,19 +575,31 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   uint8_t* W = static_cast<uint8_t*>(workspace);
   auto I32 = [&](size_t off) { return reinterpret_cast<const int32_t*>(S + off); };
   auto F32 = [&](size_t off) { return reinterpret_cast<const float*>(S + off); };
-  auto U16 = [&](size_t off) { return reinterpret_cast<const uint16_t*>(S + off); };
+  // activations: read from `saved`, or in recompute mode regenerated into the workspace
+  const uint8_t* AB = d.rc ? W : S;
+  const ActLayout A = d.rc ? B.act : L.act;
+  auto U16 = [&](size_t off) { return reinterpret_cast<const uint16_t*>(AB + off); };
   auto WU16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(W + off); };
   const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
   const uint16_t* dy = static_cast<const uint16_t*>(grad_out);
   const uint16_t* x = static_cast<const uint16_t*>(hidden);
 
+  if (d.rc) {   // recompute mode: F3-F6 again from x and the saved routing state
+    FwdPtrs P;
+    P.slot_of = I32(L.slot_of); P.counts = I32(L.counts); P.offsets = I32(L.offsets);
+    P.tile_prefix = I32(L.tile_prefix);
+    P.xp = WU16(A.xp); P.ab = WU16(A.ab); P.h = WU16(A.h); P.y = WU16(A.y);
+    P.xq = W + B.fxq; P.xs = W + B.fxs; P.hq = W + B.fhq; P.hs = W + B.fhs;
+    MOE_TRY(experts_forward(d, P, x, w, st, true));
+  }
+
   // B1 weighted dy gather (+ Q) + B8 router-probability gradient (dense row, zeros off the map)
   MOE_TRY(launch("gather_dy_dprob", st, [&] {
     if (d.mx)
-      hipLaunchKernelGGL(k_gather_dy_dprob<true>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(L.y), H, E, K,
+      hipLaunchKernelGGL(k_gather_dy_dprob<true>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(A.y), H, E, K,
                          I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, W + B.dyq, W + B.dys);
     else
-      hipLaunchKernelGGL(k_gather_dy_dprob<false>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(L.y), H, E, K,
+      hipLaunchKernelGGL(k_gather_dy_dprob<false>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(A.y), H, E, K,
                          I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, (uint8_t*)nullptr,
                          (uint8_t*)nullptr);
   }));
@@ -539,7 +619,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a3.a_s = dy;
   a3.wd = matref(w->routed_down, w->routed_down.data, 2);
   a3.sd = matref(w->shared_down, w->shared_down.data, 2);
-  a3.ab = U16(L.ab);
+  a3.ab = U16(A.ab);
   a3.dfc1 = WU16(B.dfc1);
   a3.H = H; a3.I = I;
   a3.mx = gemm::MxOperands{};
@@ -601,7 +681,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a5.offsets = I32(L.offsets);
   a5.T = T; a5.E = E; a5.has_shared = d.hs ? 1 : 0;
   a5.a_r = WU16(B.dyw); a5.a_s = dy; a5.lda = H; a5.a_s_row0 = 0;
-  a5.b_r = U16(L.h); a5.b_s = U16(L.h); a5.ldb = I; a5.b_s_row0 = d.SM;
+  a5.b_r = U16(A.h); a5.b_s = U16(A.h); a5.ldb = I; a5.b_s_row0 = d.SM;
   a5.g_lo = gradref(mg->routed_down); a5.g_hi = a5.g_lo;
   a5.s_lo = gradref(mg->shared_down); a5.s_hi = a5.s_lo;
   a5.parts = 1; a5.mpart = H;
@@ -621,7 +701,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a6.offsets = I32(L.offsets);
   a6.T = T; a6.E = E; a6.has_shared = d.hs ? 1 : 0;
   a6.a_r = WU16(B.dfc1); a6.a_s = WU16(B.dfc1); a6.lda = 2 * (int64_t)I; a6.a_s_row0 = d.SM;
-  a6.b_r = U16(L.xp); a6.b_s = x; a6.ldb = H; a6.b_s_row0 = 0;
+  a6.b_r = U16(A.xp); a6.b_s = x; a6.ldb = H; a6.b_s_row0 = 0;
   a6.g_lo = gradref(mg->routed_gate); a6.g_hi = gradref(mg->routed_up);
   a6.s_lo = gradref(mg->shared_gate); a6.s_hi = gradref(mg->shared_up);
   a6.parts = 2; a6.mpart = I;

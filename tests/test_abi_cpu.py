@@ -78,7 +78,7 @@ def test_invalid_problem_is_rejected(kw, status):
 
 def test_unsupported_configurations_are_rejected():
     p = _ok_problem()
-    p.flags = 2                                   # an unknown flag bit
+    p.flags = 4                                   # an unknown flag bit
     assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_UNSUPPORTED
     p = _ok_problem()
     p.swiglu_limit = 7.0                          # clamp not supported
@@ -202,3 +202,20 @@ def test_routed_only_mode_ignores_shared_descriptors():
     w = _fake_weights(p)
     w.shared_down = mk.moe_weight()
     assert mk.moe_forward(p, a, a, a, w, a, a, a, 1 << 20, 0) != mk.MOE_OK
+
+
+def test_recompute_mode_shrinks_saved_to_routing_state():
+    """MOE_FLAG_RECOMPUTE: `saved` keeps only the routing state (same offsets as without
+    the flag), the activations move to the workspaces."""
+    p = _ok_problem(tokens=4096)
+    q = _ok_problem(tokens=4096)
+    q.flags |= mk.MOE_FLAG_RECOMPUTE
+    H, I, T, K = p.hidden, p.intermediate, p.tokens, p.topk
+    acts = 2 * (T * K * H + (T * K + T) * (3 * I + H))      # xp, ab, h, y in bf16
+    assert mk.moe_saved_bytes(p) - mk.moe_saved_bytes(q) >= acts
+    assert mk.moe_saved_bytes(q) < 64 * T * K                 # a few int32 per route
+    assert mk.moe_workspace_bytes(q, 0) >= acts
+    assert mk.moe_workspace_bytes(q, 1) > mk.moe_workspace_bytes(p, 1)
+    lp, lq = mk.moe_saved_view(p), mk.moe_saved_view(q)
+    for f, _ in mk.moe_saved_layout._fields_:
+        assert getattr(lp, f) == getattr(lq, f)
