@@ -51,12 +51,16 @@ struct Tile {
   static constexpr int A_BYTES = TM * KB, B_BYTES = TN * KB, STAGE = A_BYTES + B_BYTES;
   static constexpr int A_DMA = A_BYTES / 1024 / NW;      // 1 KB DMA instructions per wave per stage
   static constexpr int B_DMA = B_BYTES / 1024 / NW;
-  // MXFP8 scales of one stage (4 blocks of 32 codes): A [TM][4], B [TN][4] or [4][TN]
-  static constexpr int SC_A = TM * 4, SC_B = TN * 4, SC_STAGE = SC_A + SC_B;
-  static constexpr int SC_REAL = SC_STAGE / 256;         // 256-byte dword DMA instructions
-  static constexpr int SC_DMA = (SC_REAL + NW - 1) / NW; // per wave (the extra ones are dummies)
+  // MXFP8 scales (one E8M0 byte per 32 codes; a stage of 128 codes has 4 per row).  The
+  // K-contiguous scale rows (A, and B in KC mode) are staged SCG stages at a time, 4 SCG
+  // bytes per row, in two group buffers: fetching a row's scales once per group instead
+  // of once per stage cuts the L2 requests of these rows by SCG.  B in RC mode ([K/32][TN]
+  // bytes, contiguous along N) keeps one [4][TN] block per stage in an NS-deep ring.
+  static constexpr int SCG = 8;                           // stages per scale group
+  static constexpr int SCG_A = TM * 4 * SCG, SCG_B = TN * 4 * SCG;   // group buffer parts
+  static constexpr int SC_RCB = 4 * TN;                   // RC B scales of one stage
   static constexpr int LDS = NS * STAGE;
-  static constexpr int SC_LDS = NS * SC_STAGE + 256;     // + the dummies' target
+  static constexpr int SC_LDS = 2 * (SCG_A + SCG_B) + NS * SC_RCB;
   // L2 prefetch: one dword per 128-byte line of a stage (TM + TN lines), PF_N per wave
   static constexpr int PF_N = PF ? (TM + TN + NTH - 1) / NTH : 0;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
@@ -132,12 +136,19 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
   constexpr int EB = FP8 ? 1 : 2;        // bytes per element
   constexpr int KST = KB / EB;           // K elements per stage
   constexpr int RBA = TL::TM * EB, RBB = TL::TN * EB;   // RC row bytes
-  constexpr int LPS = TL::A_DMA + TL::B_DMA + (FP8 ? TL::SC_DMA : 0) + TL::PF_N;   // loads per stage per wave
+  // the RC swizzles permute 16 chunks (bf16) or 8/16 chunks (E4M3) inside a row
+  static_assert(AM != RC || (FP8 ? (RBA == 128 || RBA == 256) : (RBA == 256 || RBA == 512)), "RC A row bytes");
+  static_assert(BMODE != RC || (FP8 ? (RBB == 128 || RBB == 256) : (RBB == 256 || RBB == 512)), "RC B row bytes");
+  // loads per stage per wave (the waits below use it only for NS >= 3, which MXFP8 tiles
+  // do not take: their scale DMAs vary per stage)
+  constexpr int LPS = TL::A_DMA + TL::B_DMA + TL::PF_N;
+  static_assert(!FP8 || TL::NS == 2, "MXFP8 tiles use two stages");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / TL::NWN, wn = w % TL::NWN;
   const uint32_t lds0 = lds_off(lds);
-  const uint32_t sc0 = FP8 ? lds_off(sc) : 0u;
+  const uint32_t scg0 = FP8 ? lds_off(sc) : 0u;                    // group buffer 0
+  const uint32_t scr0 = scg0 + 2 * (TL::SCG_A + TL::SCG_B);          // RC B ring
   const uint8_t* zp = reinterpret_cast<const uint8_t*>(g_zero_page) + 16 * lane;
   const int nk = (kdim + KST - 1) / KST;
 
@@ -175,24 +186,35 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       cb[i] = 16 * c;
     }
   }
-  // MXFP8 scale DMA sources (dword per lane): instruction q < SC_A/256 covers A rows
-  // 64q.., the next ones B (KC rows, or RC [4 blocks][TN] bytes), the rest are dummies.
-  const uint8_t* ps[TL::SC_DMA];
-  int qs[TL::SC_DMA];
-  if constexpr (FP8) {
-#pragma unroll
-    for (int i = 0; i < TL::SC_DMA; ++i) {
-      const int q = w * TL::SC_DMA + i;
-      qs[i] = q;
-      ps[i] = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
-      if (q < TL::SC_A / 256) {
-        ps[i] = fas(q * 64 + lane);
-      } else if (q < TL::SC_REAL) {
-        const int idx = (q - TL::SC_A / 256) * 64 + lane;
-        if constexpr (BMODE == KC) ps[i] = fbs(idx);
+  // MXFP8 scale groups.  Dword DMA instruction q of a group covers 8 scale rows x SCG
+  // stages: A rows 8q.. for q < GA, then (KC B) B rows.  Lane l loads row 8q' + l / 8 at
+  // group stage (l % 8) ^ (q' % 8) to byte 4 l of the instruction's 256-byte block, so
+  // row R's stage s sits at byte 32 R + 4 (s ^ (R / 8 % 8)) and 32 consecutive rows read
+  // at one stage hit 32 different banks.  Stages past K come from the zero page.  A group
+  // is issued in SCG pieces, piece p with the data of the group before's stage p + 1.
+  constexpr int GA = TL::TM / 8, GB = (BMODE == KC) ? TL::TN / 8 : 0;
+  constexpr int GPP = (GA + GB) / TL::SCG;   // instructions per piece
+  static_assert(!FP8 || (TL::SCG == 8 && (GA + GB) % TL::SCG == 0), "scale group split");
+  auto scale_piece = [&](int G, int piece) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      const uint32_t gbase = scg0 + (G & 1) * (TL::SCG_A + TL::SCG_B);
+      for (int q = piece * GPP + w; q < (piece + 1) * GPP; q += TL::NW) {
+        const bool isa = q < GA;
+        const int qq = isa ? q : q - GA;
+        const int R = 8 * qq + (lane >> 3);
+        const int kt = G * TL::SCG + ((lane & 7) ^ (qq & 7));
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
+        if (kt < nk) {
+          if (isa) {
+            src = reinterpret_cast<const uint8_t*>(fas(R)) + 4 * kt;
+          } else {
+            if constexpr (BMODE == KC) src = reinterpret_cast<const uint8_t*>(fbs(R)) + 4 * kt;
+          }
+        }
+        dma4(src, gbase + (isa ? 0 : TL::SCG_A) + qq * 256);
       }
     }
-  }
+  };
 
   // L2 prefetch sources: line p * NTH + 64 w + lane of a stage; lines < TM belong to A.
   const uint32_t pfm0 = TL::PF ? lds_off(pf_lds) : 0u;
@@ -247,32 +269,28 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       }
     }
     if constexpr (FP8) {
-#pragma unroll
-      for (int i = 0; i < TL::SC_DMA; ++i) {
-        const int q = qs[i];
-        if (q < TL::SC_A / 256) {
-          dma4(ps[i] + kt * 4, sc0 + slot * TL::SC_STAGE + q * 256);
-        } else if (q < TL::SC_REAL) {
-          const uint32_t m0v = sc0 + slot * TL::SC_STAGE + q * 256;
-          if constexpr (BMODE == KC) {
-            dma4(ps[i] + kt * 4, m0v);
-          } else {
-            const int idx = (q - TL::SC_A / 256) * 64 + lane;   // [kb][TN] bytes 4 idx .. 4 idx + 3
-            const int kblk = (4 * idx) / TL::TN, col = (4 * idx) % TL::TN;
-            dma4(col < bcols ? reinterpret_cast<const uint8_t*>(fbs(kt * 4 + kblk)) + col
-                             : reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane,
-                 m0v);
-          }
-        } else {
-          dma4(ps[i], sc0 + TL::NS * TL::SC_STAGE);
+      if constexpr (BMODE == RC) {   // this stage's [4][TN] block of B scales
+        for (int q = w; q < TL::SC_RCB / 256; q += TL::NW) {
+          const int idx = q * 64 + lane;   // bytes 4 idx .. 4 idx + 3
+          const int kblk = (4 * idx) / TL::TN, col = (4 * idx) % TL::TN;
+          dma4(col < bcols ? reinterpret_cast<const uint8_t*>(fbs(kt * 4 + kblk)) + col
+                           : reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane,
+               scr0 + slot * TL::SC_RCB + q * 256);
         }
+      }
+      if (kt == 0) {
+        for (int piece = 0; piece < TL::SCG; ++piece) scale_piece(0, piece);
+      } else {
+        const int G = (kt - 1) / TL::SCG + 1;
+        if (G * TL::SCG < nk) scale_piece(G, (kt - 1) % TL::SCG);
       }
     }
     if constexpr (TL::PF > 0) pf_issue(min(kt + TL::PF, nk - 1));
   };
 
   // ---- fragment reads and MFMAs of one stage
-  auto compute = [&](int slot) __attribute__((always_inline)) {
+  auto compute = [&](int kt) __attribute__((always_inline)) {
+    const int slot = kt % TL::NS;
     const uint8_t* As = lds + slot * TL::STAGE;
     const uint8_t* Bs = As + TL::A_BYTES;
     const int g = lane >> 5, grp = lane >> 4, j16 = lane & 15;
@@ -344,8 +362,13 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     } else {
       // Per 64-code K step, lane (r, g) holds codes 16g..16g+15 and 32+16g..32+16g+15 and
       // carries the scale of 32-code block g (the scaled MFMA's measured lane layout).
-      const uint8_t* sA = sc + slot * TL::SC_STAGE;
-      const uint8_t* sB = sA + TL::SC_A;
+      const int gs = kt % TL::SCG;   // stage inside its scale group
+      const uint8_t* sA = sc + ((kt / TL::SCG) & 1) * (TL::SCG_A + TL::SCG_B);
+      const uint8_t* sB = sA + TL::SCG_A;
+      const uint8_t* sR = sc + 2 * (TL::SCG_A + TL::SCG_B) + slot * TL::SC_RCB;
+      auto gsc = [&](const uint8_t* base, int R, int ks) __attribute__((always_inline)) {
+        return base[32 * R + 4 * (gs ^ ((R >> 3) & 7)) + 2 * ks + g];
+      };
       constexpr bool PRE = 2 * (TL::MI + TL::NJ) * 8 <= 64;
       i32x8_t a[2][TL::MI], b[2][TL::NJ];
       int sa[2][TL::MI], sb[2][TL::NJ];
@@ -357,7 +380,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
           const u32x4_t u0 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g) ^ swz_kc<KB>(r)) << 4));
           const u32x4_t u1 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g + 2) ^ swz_kc<KB>(r)) << 4));
           a[ks][i] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-          sa[ks][i] = sA[r * 4 + 2 * ks + g];
+          sa[ks][i] = gsc(sA, r, ks);
         }
 #pragma unroll
         for (int j = 0; j < TL::NJ; ++j) {
@@ -367,7 +390,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
             const u32x4_t u0 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g) ^ swz_kc<KB>(c)) << 4));
             const u32x4_t u1 = *reinterpret_cast<const u32x4_t*>(p + (((4 * ks + g + 2) ^ swz_kc<KB>(c)) << 4));
             b[ks][j] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-            sb[ks][j] = sB[c * 4 + 2 * ks + g];
+            sb[ks][j] = gsc(sB, c, ks);
           } else {
             const int n0 = wn * TL::WNC + j * 32 + 16 * (grp & 1);
             i32x2_t q[4];
@@ -379,7 +402,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
                   (lds_i32x2*)((lds_u8*)Bs + k * RBB + ((((byte >> 4) ^ swz_rc8<RBB>(k)) << 4) | (byte & 15))));
             }
             b[ks][j] = i32x8_t{q[0][0], q[0][1], q[1][0], q[1][1], q[2][0], q[2][1], q[3][0], q[3][1]};
-            sb[ks][j] = sB[(2 * ks + g) * TL::TN + c];
+            sb[ks][j] = sR[(2 * ks + g) * TL::TN + c];
           }
         }
       };
@@ -431,7 +454,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       }
       __syncthreads();
       if (kt + TL::NS - 1 < nk) issue(kt + TL::NS - 1, (kt + TL::NS - 1) % TL::NS);
-      if constexpr (decltype(act)::value) compute(kt % TL::NS);
+      if constexpr (decltype(act)::value) compute(kt);
     }
   };
   if (wave_active) run(std::true_type{});
