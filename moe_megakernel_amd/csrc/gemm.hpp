@@ -558,10 +558,10 @@ struct MxOperands {
 #define MOE_TL_FC2_MX 192, 256, 2, 4, 2, 1
 #endif
 #ifndef MOE_TL_DG2_MX
-#define MOE_TL_DG2_MX 192, 256, 2, 4, 2, 1, 2
+#define MOE_TL_DG2_MX 192, 256, 2, 4, 2, 1, 1
 #endif
 #ifndef MOE_TL_DG1_MX
-#define MOE_TL_DG1_MX 192, 256, 2, 4, 2, 1, 2
+#define MOE_TL_DG1_MX 192, 256, 2, 4, 2, 1, 1
 #endif
 #ifndef MOE_TL_WG
 #define MOE_TL_WG 128, 128, 2, 2, 2, 4, 0, 64
