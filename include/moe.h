@@ -53,7 +53,9 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = 5,     /* a configuration not implemented (SwiGLU clamp)           */
   MOE_ERR_WORKSPACE = 6,       /* saved / workspace buffer missing or too small            */
   MOE_ERR_ROUTE_OVERFLOW = 7,  /* device status word: a row had more than topk routes      */
-  MOE_ERR_HIP = 8              /* a HIP launch failed                                      */
+  MOE_ERR_HIP = 8,             /* a HIP launch failed                                      */
+  MOE_ERR_ROUTE_INVALID = 9    /* device status word: a top_experts entry outside [-1, E)
+                                  or listed twice in one row (moe_forward_topk)            */
 } moe_status;
 
 typedef enum { MOE_BF16 = 1, MOE_FP32 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
@@ -73,6 +75,12 @@ typedef enum { MOE_BF16 = 1, MOE_FP32 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
  * in the forward and the backward of one layer call, and the workspaces grow by the
  * activations (see moe_workspace_bytes). */
 #define MOE_FLAG_RECOMPUTE 2u
+/* Set: the routing arrives as the router's fixed-width table (top_experts and
+ * router_weights, [T][K]), the form the runtime consumes (Megatron Core API docs,
+ * mok.runtime, _MoKFunction.forward), through moe_forward_topk; moe_backward then writes
+ * grad_probs as [T][K].  Clear: the dense routing map and probabilities through
+ * moe_forward. */
+#define MOE_FLAG_TOPK_ROUTING 4u
 
 /* Problem sizes and options. */
 typedef struct {
@@ -82,7 +90,8 @@ typedef struct {
   int32_t experts;       /* E in [1, 255]                                                 */
   int32_t topk;          /* K in [1, min(8, E)]                                           */
   int32_t routed_dtype;  /* MOE_BF16 or MOE_MXFP8_E4M3 (PR #6572, Supported configurations) */
-  uint32_t flags;        /* MOE_FLAG_HAS_SHARED (else routed-only) | MOE_FLAG_RECOMPUTE  */
+  uint32_t flags;        /* MOE_FLAG_HAS_SHARED (else routed-only) | MOE_FLAG_RECOMPUTE
+                            | MOE_FLAG_TOPK_ROUTING                                        */
   float swiglu_limit;    /* must be 0 (no clamp)                                          */
 } moe_problem;
 
@@ -197,6 +206,18 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
                        const uint8_t* routing_map, const moe_weights* w, void* out,
                        void* saved, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward from the router's fixed-width table (requires MOE_FLAG_TOPK_ROUTING; without
+ * it, and moe_forward with it, return MOE_ERR_UNSUPPORTED).
+ *  top_experts     int32 [T][K] expert IDs in any order, -1 for a missing route
+ *  router_weights  float [T][K] the weight of each listed route (ignored at -1)
+ * An ID outside [-1, E) or an ID listed twice in a row is dropped (treated as -1) and
+ * sets the status word to MOE_ERR_ROUTE_INVALID.  The layer is the same function as
+ * moe_forward on the dense map with routing_map[t][e_tk] = 1 and probs[t][e_tk] =
+ * router_weights[t][k].  Other arguments as for moe_forward. */
+moe_status moe_forward_topk(const moe_problem* p, const void* hidden, const int32_t* top_experts,
+                            const float* router_weights, const moe_weights* w, void* out,
+                            void* saved, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Backward of sum(grad_out * out).
  *  grad_out     bf16  [T][H]
  *  hidden       the same bf16 [T][H] tensor given to moe_forward
@@ -204,7 +225,9 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
  *  grad_hidden  bf16  [T][H]  overwritten (routed terms only in routed-only mode)
  *  grad_probs   float [T][E]  overwritten in full; zero where routing_map was 0
  *               (the router-weight gradient scattered back into the dense
- *               probability tensor: PR #6572, Design > Authoritative routing maps)
+ *               probability tensor: PR #6572, Design > Authoritative routing maps);
+ *               with MOE_FLAG_TOPK_ROUTING float [T][K], the gradient of
+ *               router_weights, 0 at -1 entries
  *  mg           main_grad buffers (FP32 or BF16, see moe_main_grads), accumulated
  *  workspace    moe_workspace_bytes(p, 1) bytes of scratch
  */

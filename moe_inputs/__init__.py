@@ -23,7 +23,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "Config", "CONFIGS", "config", "routing", "hidden", "grad_out",
+    "Config", "CONFIGS", "config", "routing", "routing_table", "hidden", "grad_out",
     "shared_weights", "routed_expert", "routed_all", "main_grad_pattern",
     "to_bf16_bits", "mxfp8_quantize",
 ]
@@ -76,7 +76,7 @@ def custom(tokens, hidden, experts, topk, inter, *, routed="bf16", layout="singl
 # random streams
 # ----------------------------------------------------------------------------------
 _TAGS = {"logits": 1, "x": 2, "shared_fc1": 3, "shared_fc2": 4, "routed_fc1": 5,
-         "routed_fc2": 6, "short": 7, "dy": 8, "balanced": 9}
+         "routed_fc2": 6, "short": 7, "dy": 8, "balanced": 9, "table": 10}
 
 
 def _rng(cfg: Config, tag: str, sub: int = 0) -> np.random.Generator:
@@ -212,6 +212,25 @@ def routing(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
     rmap[rows[keep], order[keep]] = 1
     probs[rows[keep], order[keep]] = top_p[keep].astype(np.float32)  # dropped: prob 0, no renorm
     return probs, rmap
+
+
+def routing_table(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
+    """The same routing decisions as routing(cfg) in the router's fixed-width form:
+    top_experts int32 [T, K] and router_weights float32 [T, K].  Each row holds its
+    listed experts and K - n entries of -1 at seeded random positions, in a seeded random
+    order (a router's own order need not be ascending); the weight at -1 is a seeded
+    random value, which the layer must ignore."""
+    probs, rmap = routing(cfg)
+    T, K = cfg.tokens, cfg.topk
+    rng = _rng(cfg, "table")
+    top = np.full((T, K), -1, dtype=np.int32)
+    rw = rng.random((T, K)).astype(np.float32)
+    for t in range(T):
+        listed = np.nonzero(rmap[t])[0]
+        pos = rng.permutation(K)[:len(listed)]
+        top[t, pos] = listed
+        rw[t, pos] = probs[t, listed]
+    return top, rw
 
 
 def hidden(cfg: Config) -> np.ndarray:

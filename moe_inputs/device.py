@@ -39,28 +39,38 @@ def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
 class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
                  routing=None, main_grad_dtype: str = "fp32", shared: bool = True,
-                 recompute: bool = False):
+                 recompute: bool = False, routing_table=None):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
         configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16".
         shared=False: routed-only mode; the shared weight and main_grad descriptors are
         passed all zero (the library must not touch them).  recompute=True: MoE-layer
         recompute mode (saved holds the routing state only; the backward regenerates the
-        activations)."""
+        activations).  routing_table: optional (top_experts [T,K] int32, router_weights
+        [T,K] float32), the router's fixed-width table given to moe_forward_topk instead of
+        the dense map; grad_probs is then [T,K]."""
         self.cfg = cfg
         self.device = device
         T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
         self.backward_enabled = cfg.backward if backward is None else backward
         probs, rmap = gen.routing(cfg) if routing is None else routing
         self.np_probs, self.np_rmap = probs, rmap
+        self.table = routing_table is not None
+        if self.table:
+            self.np_top = np.ascontiguousarray(routing_table[0], dtype=np.int32)
+            self.np_rw = np.ascontiguousarray(routing_table[1], dtype=np.float32)
         self.np_x = gen.hidden(cfg)
         self.np_dy = gen.grad_out(cfg) if self.backward_enabled else None
         self.np_s1, self.np_s2 = gen.shared_weights(cfg)
         self.np_routed = gen.routed_all(cfg, threads=threads)
-        self.slots = int(rmap.sum())
+        self.slots = int(rmap.sum()) if not self.table else int(
+            sum(len({int(e) for e in row if 0 <= e < E}) for row in self.np_top))
 
         self.x = _bf16(self.np_x, device)
         self.probs = torch.from_numpy(probs).to(device)
         self.rmap = torch.from_numpy(rmap).to(device)
+        if self.table:
+            self.top = torch.from_numpy(self.np_top).to(device)
+            self.rw = torch.from_numpy(self.np_rw).to(device)
         self.dy = _bf16(self.np_dy, device) if self.np_dy is not None else None
         self.s1 = _bf16(self.np_s1, device)
         self.s2 = _bf16(self.np_s2, device)
@@ -68,7 +78,8 @@ class DeviceProblem:
         mx = cfg.routed == "mxfp8"
         dt = mk.MOE_MXFP8_E4M3 if mx else mk.MOE_BF16
         self.shared = shared
-        flags = (mk.MOE_FLAG_HAS_SHARED if shared else 0) | (mk.MOE_FLAG_RECOMPUTE if recompute else 0)
+        flags = ((mk.MOE_FLAG_HAS_SHARED if shared else 0) | (mk.MOE_FLAG_RECOMPUTE if recompute else 0)
+                 | (mk.MOE_FLAG_TOPK_ROUTING if self.table else 0))
         self.p = mk.problem(T, H, I, E, K, dt, flags=flags)
 
         def routed_mat(key, rows, cols, conv, elem_cols):
@@ -112,7 +123,7 @@ class DeviceProblem:
         self.layer = mk.Layer(self.p, device=device)
         if self.backward_enabled:
             self.dx = torch.empty(T, H, dtype=torch.bfloat16, device=device)
-            self.dprobs = torch.empty(T, E, dtype=torch.float32, device=device)
+            self.dprobs = torch.empty(T, K if self.table else E, dtype=torch.float32, device=device)
             mgt = {"fp32": torch.float32, "bf16": torch.bfloat16}[main_grad_dtype]
             mgd = mk.MOE_BF16 if main_grad_dtype == "bf16" else mk.MOE_FP32
             self.mg_s1 = torch.empty(2 * I, H, dtype=mgt, device=device)
@@ -156,7 +167,10 @@ class DeviceProblem:
         return gen.main_grad_pattern(n, phase).reshape(shape)
 
     def forward(self):
-        self.layer.forward(self.x, self.probs, self.rmap, self.weights, self.out)
+        if self.table:
+            self.layer.forward_topk(self.x, self.top, self.rw, self.weights, self.out)
+        else:
+            self.layer.forward(self.x, self.probs, self.rmap, self.weights, self.out)
         return self.out
 
     def backward(self):

@@ -18,12 +18,14 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_LAYOUT = 0, 1, 2, 3, 4
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_ROUTE_OVERFLOW, MOE_ERR_HIP = 5, 6, 7, 8
+MOE_ERR_ROUTE_INVALID = 9
 MOE_BF16, MOE_FP32, MOE_MXFP8_E4M3 = 1, 2, 3
 MOE_FLAG_HAS_SHARED = 1
 MOE_FLAG_RECOMPUTE = 2
+MOE_FLAG_TOPK_ROUTING = 4
 
 EXPORTED = ("moe_saved_bytes", "moe_workspace_bytes", "moe_saved_view", "moe_forward",
-            "moe_backward", "moe_status_str", "moe_kernel_timer_enable", "moe_kernel_timer_read")
+            "moe_forward_topk", "moe_backward", "moe_status_str", "moe_kernel_timer_enable", "moe_kernel_timer_read")
 
 
 class moe_problem(C.Structure):
@@ -85,6 +87,8 @@ def load(path: str | None = None):
     lib.moe_forward.argtypes = [P(moe_problem), C.c_void_p, C.c_void_p, C.c_void_p, P(moe_weights),
                                 C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.moe_forward.restype = C.c_int
+    lib.moe_forward_topk.argtypes = lib.moe_forward.argtypes
+    lib.moe_forward_topk.restype = C.c_int
     lib.moe_backward.argtypes = [P(moe_problem), C.c_void_p, C.c_void_p, P(moe_weights), C.c_void_p,
                                  C.c_void_p, C.c_void_p, P(moe_main_grads), C.c_void_p, C.c_size_t,
                                  C.c_void_p]
@@ -131,6 +135,13 @@ def moe_forward(p, hidden, probs, routing_map, weights, out, saved, workspace, w
     """Raw call with integer device addresses; returns the status code."""
     return load().moe_forward(C.byref(p), hidden, probs, routing_map, C.byref(weights), out, saved,
                               workspace, workspace_bytes, stream)
+
+
+def moe_forward_topk(p, hidden, top_experts, router_weights, weights, out, saved, workspace, workspace_bytes,
+                     stream) -> int:
+    """Raw call with integer device addresses (routing as the [T][K] table); returns the status."""
+    return load().moe_forward_topk(C.byref(p), hidden, top_experts, router_weights, C.byref(weights), out,
+                                   saved, workspace, workspace_bytes, stream)
 
 
 def moe_backward(p, grad_out, hidden, weights, saved, grad_hidden, grad_probs, main_grads, workspace,
@@ -211,6 +222,14 @@ class Layer:
                          _ptr(self.saved), _ptr(self.workspace), self.ws_bytes, current_stream())
         if st != MOE_OK:
             raise MoeError(st, "moe_forward")
+        return out
+
+    def forward_topk(self, hidden, top_experts, router_weights, weights: moe_weights, out):
+        st = moe_forward_topk(self.p, _ptr(hidden), _ptr(top_experts), _ptr(router_weights), weights,
+                              _ptr(out), _ptr(self.saved), _ptr(self.workspace), self.ws_bytes,
+                              current_stream())
+        if st != MOE_OK:
+            raise MoeError(st, "moe_forward_topk")
         return out
 
     def backward(self, grad_out, hidden, weights: moe_weights, grad_hidden, grad_probs,

@@ -31,6 +31,7 @@ struct Dims {
   bool mx;
   bool hs;           // the shared expert is fused in
   bool rc;           // recompute: saved holds the routing state only
+  bool tk;           // routing given as the fixed-width [T][K] table
 };
 
 Dims dims_of(const moe_problem* p) {
@@ -42,6 +43,7 @@ Dims dims_of(const moe_problem* p) {
   d.nchunks = (d.T + kRouteChunk - 1) / kRouteChunk;
   d.mx = p->routed_dtype == MOE_MXFP8_E4M3;
   d.rc = (p->flags & MOE_FLAG_RECOMPUTE) != 0;
+  d.tk = (p->flags & MOE_FLAG_TOPK_ROUTING) != 0;
   return d;
 }
 
@@ -169,7 +171,7 @@ moe_status check_problem(const moe_problem* p) {
   if (p->topk < 1 || p->topk > kMaxTopk || p->topk > p->experts) return MOE_ERR_SHAPE;
   if (p->tokens * (int64_t)p->topk > (int64_t)1 << 30) return MOE_ERR_SHAPE;
   if (p->hidden > (1 << 20) || p->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
-  if (p->flags & ~(MOE_FLAG_HAS_SHARED | MOE_FLAG_RECOMPUTE)) return MOE_ERR_UNSUPPORTED;
+  if (p->flags & ~(MOE_FLAG_HAS_SHARED | MOE_FLAG_RECOMPUTE | MOE_FLAG_TOPK_ROUTING)) return MOE_ERR_UNSUPPORTED;
   if (p->swiglu_limit != 0.0f) return MOE_ERR_UNSUPPORTED;
   if (p->routed_dtype != MOE_BF16 && p->routed_dtype != MOE_MXFP8_E4M3) return MOE_ERR_DTYPE;
   return MOE_OK;
@@ -467,6 +469,7 @@ const char* moe_status_str(moe_status s) {
     case MOE_ERR_WORKSPACE: return "saved or workspace buffer missing or too small";
     case MOE_ERR_ROUTE_OVERFLOW: return "a routing-map row has more than topk routes";
     case MOE_ERR_HIP: return "a HIP launch failed";
+    case MOE_ERR_ROUTE_INVALID: return "a top_experts entry is out of range or repeated in its row";
   }
   return "unknown status";
 }
@@ -496,13 +499,22 @@ moe_status moe_saved_view(const moe_problem* p, moe_saved_layout* out) {
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_problem* p, const void* hidden, const float* probs,
-                       const uint8_t* routing_map, const moe_weights* w, void* out, void* saved,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both forward entry points: the routing is the dense map + probabilities (rmap, probs),
+// or the router's fixed-width table (top_in, rw_in).
+moe_status forward_impl(const moe_problem* p, const void* hidden, const float* probs,
+                        const uint8_t* routing_map, const int32_t* top_in, const float* rw_in,
+                        const moe_weights* w, void* out, void* saved, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   MOE_TRY(check_problem(p));
   MOE_TRY(check_weights(p, w));
   const Dims d = dims_of(p);
-  if (d.T > 0 && (!hidden || !probs || !routing_map || !out)) return MOE_ERR_NULL;
+  if (d.tk != (top_in != nullptr || rw_in != nullptr)) return MOE_ERR_UNSUPPORTED;
+  const bool have_routing = d.tk ? (top_in && rw_in) : (probs && routing_map);
+  if (d.T > 0 && (!hidden || !have_routing || !out)) return MOE_ERR_NULL;
   if (!saved) return MOE_ERR_WORKSPACE;
   const FwdLayout F = fwd_layout(d);
   if (workspace_bytes < F.total || !workspace) return MOE_ERR_WORKSPACE;
@@ -523,12 +535,20 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
   const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
   const int nch = (int)d.nchunks;
 
-  // F1 compaction, F2 histogram + scan + stable rank
-  MOE_TRY(launch("route_compact", st, [&] {
-    if (nch > 0)
-      hipLaunchKernelGGL(k_route_compact, dim3(nch), dim3(256), 0, st, routing_map, probs, T, E, K,
-                         I32(L.top), F32(L.rw), I32(L.chunk_counts), I32(L.chunk_status));
-  }));
+  // F1 compaction (or validation of the router's table), F2 histogram + scan + stable rank
+  if (d.tk) {
+    MOE_TRY(launch("route_table", st, [&] {
+      if (nch > 0)
+        hipLaunchKernelGGL(k_route_table, dim3(nch), dim3(kRouteChunk * kMaxTopk), 0, st, top_in, rw_in, T, E, K,
+                           I32(L.top), F32(L.rw), I32(L.chunk_counts), I32(L.chunk_status));
+    }));
+  } else {
+    MOE_TRY(launch("route_compact", st, [&] {
+      if (nch > 0)
+        hipLaunchKernelGGL(k_route_compact, dim3(nch), dim3(256), 0, st, routing_map, probs, T, E, K,
+                           I32(L.top), F32(L.rw), I32(L.chunk_counts), I32(L.chunk_status));
+    }));
+  }
   MOE_TRY(launch("route_scan", st, [&] {
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, I32(L.chunk_counts), nch, E, T, d.hs ? 1 : 0,
                        (int)tok_bm(d), I32(L.chunk_base), I32(L.counts), I32(L.offsets), I32(L.tile_prefix),
@@ -552,6 +572,29 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
                        I32(L.slot_of), F32(L.rw), static_cast<uint16_t*>(out));
   }));
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_problem* p, const void* hidden, const float* probs,
+                       const uint8_t* routing_map, const moe_weights* w, void* out, void* saved,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (p && (p->flags & MOE_FLAG_TOPK_ROUTING)) return MOE_ERR_UNSUPPORTED;
+  return forward_impl(p, hidden, probs, routing_map, nullptr, nullptr, w, out, saved, workspace,
+                      workspace_bytes, stream);
+}
+
+moe_status moe_forward_topk(const moe_problem* p, const void* hidden, const int32_t* top_experts,
+                            const float* router_weights, const moe_weights* w, void* out, void* saved,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (p && !(p->flags & MOE_FLAG_TOPK_ROUTING)) return MOE_ERR_UNSUPPORTED;
+  if (!top_experts || !router_weights) {
+    if (p && p->tokens > 0) return MOE_ERR_NULL;
+  }
+  return forward_impl(p, hidden, nullptr, nullptr, top_experts, router_weights, w, out, saved, workspace,
+                      workspace_bytes, stream);
 }
 
 moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* hidden,
@@ -597,11 +640,12 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   MOE_TRY(launch("gather_dy_dprob", st, [&] {
     if (d.mx)
       hipLaunchKernelGGL(k_gather_dy_dprob<true>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(A.y), H, E, K,
-                         I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, W + B.dyq, W + B.dys);
+                         I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, W + B.dyq, W + B.dys,
+                         d.tk ? 0 : 1);
     else
       hipLaunchKernelGGL(k_gather_dy_dprob<false>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(A.y), H, E, K,
                          I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, (uint8_t*)nullptr,
-                         (uint8_t*)nullptr);
+                         (uint8_t*)nullptr, d.tk ? 0 : 1);
   }));
 
   gemm::TokArgs ta;

@@ -110,6 +110,43 @@ __global__ __launch_bounds__(256) void k_route_compact(
   if (threadIdx.x == 0) chunk_status[blockIdx.x] = overflow ? 7 /* MOE_ERR_ROUTE_OVERFLOW */ : 0;
 }
 
+// Kernel 1 for a router that already produced the fixed-width table (the form the
+// runtime consumes: Megatron Core API docs, mok.runtime, _MoKFunction.forward takes
+// router_weights and top_experts): validation and the chunk histogram in one pass.
+// Thread (i, k) for the chunk's token i and route k.  An ID outside [-1, E) or an ID a
+// row lists twice marks the chunk invalid and is stored as -1 (weight 0), so every later
+// kernel sees an in-range table; the status word reports the error.
+__global__ __launch_bounds__(kRouteChunk * kMaxTopk) void k_route_table(
+    const int32_t* __restrict__ top_in, const float* __restrict__ rw_in, int T, int E, int K,
+    int32_t* __restrict__ top, float* __restrict__ rw, int32_t* __restrict__ chunk_counts,
+    int32_t* __restrict__ chunk_status) {
+  __shared__ int cnt[kMaxExperts + 1];
+  __shared__ int tab[kRouteChunk * kMaxTopk];
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) bad = 0;
+  for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
+  const int64_t base = (int64_t)blockIdx.x * kRouteChunk * K;
+  const int n = min(kRouteChunk, T - (int)blockIdx.x * kRouteChunk) * K;
+  const int e = tid < n ? top_in[base + tid] : -1;
+  tab[tid] = e;
+  __syncthreads();
+  if (tid < n) {
+    const int k = tid % K;
+    bool ok = e >= 0 && e < E;
+    bool err = e < -1 || e >= E;
+    for (int q = tid - k; q < tid; ++q)   // earlier routes of the same token
+      if (ok && tab[q] == e) { ok = false; err = true; }
+    top[base + tid] = ok ? e : -1;
+    rw[base + tid] = ok ? rw_in[base + tid] : 0.0f;
+    if (ok) atomicAdd(&cnt[e], 1);
+    if (err) bad = 1;
+  }
+  __syncthreads();
+  for (int x = tid; x < E; x += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + x] = cnt[x];
+  if (tid == 0) chunk_status[blockIdx.x] = bad ? 9 /* MOE_ERR_ROUTE_INVALID */ : 0;
+}
+
 // Kernel 2: one block of 1024 threads.  Thread (s, e) owns expert e's chunks of segment
 // s (segments of ceil(nchunks / S) consecutive chunks, S = 1024 / 256 = 4 or more): it
 // sums them, the segment sums are scanned in LDS, and a second pass over the segment

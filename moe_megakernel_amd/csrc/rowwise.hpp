@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
 // Backward gather: dyw[slot] = w_tk * dy[t] (the router weight folded into the
 // routed expert's upstream gradient), and the router-probability gradient
 // dprobs[t, e_tk] = dy[t] . y[slot] (y is the unweighted expert output), written
-// into the dense [T][E] row with zeros off the map.  The dot products are
+// into the dense [T][E] row with zeros off the map, or (dense = 0, routing given as the
+// fixed-width table) into the [T][K] row of the table, 0 at -1 entries.  The dot products are
 // reduced per thread in a fixed order, then across each wave by a fixed butterfly,
 // then across the waves in order.  With Q, w_tk * dy[t] is also quantised to MXFP8
 // along H (the A operand of the scaled-FP8 data-gradient GEMM).  One block per token.
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y, int H, int E, int K,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ top,
     const float* __restrict__ rw, uint16_t* __restrict__ dyw, float* __restrict__ dprobs,
-    uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys) {
+    uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys, int dense) {
   __shared__ float red[kRowThreads / 64][kMaxTopk];
   __shared__ float dp[kMaxTopk];
   const int t = blockIdx.x;
@@ -236,6 +237,10 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     dp[threadIdx.x] = v;
   }
   __syncthreads();
+  if (!dense) {   // a route with no slot accumulated nothing: dp[k] = 0 there
+    if (threadIdx.x < K) dprobs[(int64_t)t * K + threadIdx.x] = dp[threadIdx.x];
+    return;
+  }
   for (int e = threadIdx.x; e < E; e += kRowThreads) {
     float v = 0.0f;
 #pragma unroll

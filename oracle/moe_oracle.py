@@ -35,7 +35,11 @@ Readings of points the pages leave open:
   * grad_probs is the full gradient of the dense probs tensor (zero off the
     map); main_grad receives the weight gradient by accumulation (+=), in FP32,
     or for a BF16 main_grad as described in main_grad_after;
-  * MXFP8 forward uses the rowwise copy, dgrad the columnwise copy.
+  * MXFP8 forward uses the rowwise copy, dgrad the columnwise copy;
+  * a router's fixed-width table (the runtime's input form) lists each expert at most
+    once per row, in any order, with -1 anywhere; the weight at -1 is ignored.  Its
+    layer is the dense-map layer with the table scattered into map and probs, and its
+    probability gradient is that of router_weights ([T, K], 0 at -1).
 """
 from __future__ import annotations
 
@@ -45,12 +49,17 @@ __all__ = [
     "bf16_decode", "bf16_round", "main_grad_after", "e4m3_decode", "e8m0_decode", "mxfp8_decode_rowwise",
     "mxfp8_decode_colwise", "compact_routing", "dispatch_index", "silu", "dsilu",
     "swiglu_ffn", "Weights", "moe_forward", "moe_forward_f64", "moe_backward",
-    "moe_backward_f64", "RouteOverflow",
+    "moe_backward_f64", "RouteOverflow", "RouteInvalid", "check_table", "moe_forward_table",
+    "moe_backward_table",
 ]
 
 
 class RouteOverflow(ValueError):
     """A routing-map row has more true entries than the fixed table width."""
+
+
+class RouteInvalid(ValueError):
+    """A top_experts entry outside [-1, E), or an expert listed twice in one row."""
 
 
 # ----------------------------------------------------------------------------------
@@ -157,6 +166,21 @@ def compact_routing(routing_map: np.ndarray, probs: np.ndarray, topk: int):
             top[t, k] = e
             rw[t, k] = probs[t, e]
     return top, rw
+
+
+def check_table(top_experts: np.ndarray, num_experts: int) -> None:
+    """A router's fixed-width table as the runtime consumes it (Megatron Core API docs,
+    mok.runtime, _MoKFunction.forward takes top_experts and router_weights): every entry
+    is an expert ID in [0, E) or -1 for a missing route, and a row names an expert at
+    most once (a token has one decision per expert, as in the dense map)."""
+    for t, row in enumerate(np.asarray(top_experts)):
+        ids = [int(e) for e in row]
+        for e in ids:
+            if e < -1 or e >= num_experts:
+                raise RouteInvalid(f"token {t}: expert id {e} outside [-1, {num_experts})")
+        valid = [e for e in ids if e >= 0]
+        if len(valid) != len(set(valid)):
+            raise RouteInvalid(f"token {t}: an expert is listed twice")
 
 
 def dispatch_index(top_experts: np.ndarray, num_experts: int):
@@ -303,8 +327,25 @@ def moe_forward_f64(x, probs, routing_map, topk, weights: Weights, tokens=None):
     expert (routed-only mode) the first term is absent.
     """
     T, E = routing_map.shape
-    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     top, rw = compact_routing(routing_map, probs, topk)
+    return _forward_table_f64(x, top, rw, E, weights, tokens)
+
+
+def moe_forward_table(x_bits, top_experts, router_weights, num_experts, weights: Weights, tokens=None):
+    """The forward from the router's fixed-width table (top_experts int [T, K] in any
+    order, -1 for a missing route; router_weights [T, K], ignored at -1): out rows for
+    `tokens` from BF16 hidden-state bits.  The same function as moe_forward on the dense
+    map with routing_map[t, e_tk] = 1 and probs[t, e_tk] = router_weights[t, k]."""
+    check_table(top_experts, num_experts)
+    T = np.asarray(top_experts).shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    return _forward_table_f64(bf16_decode(x_bits[tokens]), top_experts, router_weights, num_experts,
+                              weights, tokens)
+
+
+def _forward_table_f64(x, top, rw, E, weights: Weights, tokens=None):
+    T = np.asarray(top).shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     x = np.asarray(x, dtype=np.float64)
     pos = {int(t): i for i, t in enumerate(tokens)}
     if weights.shared is not None:
@@ -352,9 +393,38 @@ def moe_backward_f64(dy_all, x_all, probs, routing_map, topk, weights: Weights,
     review thread on the wgrad accumulation precision).
     """
     T, E = routing_map.shape
+    top, rw = compact_routing(routing_map, probs, topk)
+    return _backward_table_f64(dy_all, x_all, top, rw, E, weights, tokens, experts, shared_grads)
+
+
+def moe_backward_table(dy_bits, x_bits, top_experts, router_weights, num_experts, weights: Weights,
+                       tokens=None, experts=None, shared_grads=True):
+    """moe_backward for the router's fixed-width table: as moe_backward_f64, except that
+    "dprobs" is the gradient of router_weights, float64 [len(tokens), K], 0 at -1 entries.
+    A token names an expert at most once, so it is the dense gradient read at
+    (t, top_experts[t, k])."""
+    check_table(top_experts, num_experts)
+    top = np.asarray(top_experts)
+    g = _backward_table_f64(bf16_decode(dy_bits), bf16_decode(x_bits), top, router_weights, num_experts,
+                            weights, tokens, experts, shared_grads)
+    T, K = top.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    dense = g["dprobs"]
+    tab = np.zeros((len(tokens), K))
+    for i, t in enumerate(tokens):
+        for k in range(K):
+            e = int(top[t, k])
+            if e >= 0:
+                tab[i, k] = dense[i, e]
+    g["dprobs"] = tab
+    return g
+
+
+def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None, experts=None,
+                        shared_grads=True):
+    T = np.asarray(top).shape[0]
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     experts = range(E) if experts is None else experts
-    top, rw = compact_routing(routing_map, probs, topk)
 
     x_all = np.asarray(x_all, dtype=np.float64)
     dy_all = np.asarray(dy_all, dtype=np.float64)

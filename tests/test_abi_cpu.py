@@ -219,3 +219,19 @@ def test_recompute_mode_shrinks_saved_to_routing_state():
     lp, lq = mk.moe_saved_view(p), mk.moe_saved_view(q)
     for f, _ in mk.moe_saved_layout._fields_:
         assert getattr(lp, f) == getattr(lq, f)
+
+
+def test_topk_routing_entry_point_validation():
+    """moe_forward_topk needs MOE_FLAG_TOPK_ROUTING and moe_forward refuses it; the table
+    pointers are required for a non-empty batch."""
+    p = _ok_problem()
+    a = 1 << 41
+    w = _fake_weights(p)
+    assert mk.moe_forward_topk(p, a, a, a, w, a, a, a, 1 << 20, 0) == mk.MOE_ERR_UNSUPPORTED
+    p.flags |= mk.MOE_FLAG_TOPK_ROUTING
+    assert mk.moe_forward(p, a, a, a, w, a, a, a, 1 << 20, 0) == mk.MOE_ERR_UNSUPPORTED
+    assert mk.moe_forward_topk(p, a, 0, a, w, a, a, a, 1 << 20, 0) == mk.MOE_ERR_NULL
+    assert mk.moe_forward_topk(p, a, a, 0, w, a, a, a, 1 << 20, 0) == mk.MOE_ERR_NULL
+    assert mk.moe_forward_topk(p, a, a, a, w, a, a, 0, 0, 0) == mk.MOE_ERR_WORKSPACE   # accepted so far
+    assert mk.moe_saved_bytes(p) == mk.moe_saved_bytes(_ok_problem())
+    assert "repeated" in mk.moe_status_str(mk.MOE_ERR_ROUTE_INVALID)

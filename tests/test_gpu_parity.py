@@ -435,6 +435,118 @@ def test_recompute_full_size_bit_identical(gpu_lib):
 
 
 # ----------------------------------------------------------------------------------
+# routing given as the router's fixed-width table (moe_forward_topk)
+# ----------------------------------------------------------------------------------
+def _check_table_state(dp, top_ref):
+    """Stored table = the given one with invalid entries dropped; dispatch bit-exact."""
+    cfg = dp.cfg
+    st = {k: v.cpu().numpy() for k, v in dp.layer.routing_state().items()}
+    counts, offsets, slot_of, slot_token = O.dispatch_index(top_ref, cfg.experts)
+    S = int(offsets[-1])
+    assert np.array_equal(st["top_experts"], top_ref)
+    rw = np.where(top_ref >= 0, dp.np_rw, np.float32(0))
+    assert np.array_equal(st["router_weights"].view(np.uint32), rw.view(np.uint32))
+    assert np.array_equal(st["counts"], counts)
+    assert np.array_equal(st["offsets"], offsets)
+    assert np.array_equal(st["slot_of"], slot_of)
+    assert np.array_equal(st["slot_token"][:S], slot_token)
+    return int(st["status_word"][0])
+
+
+@pytest.mark.parametrize("routed,layout,shape", [
+    ("bf16", "single", (777, 384, 13, 4, 256)),
+    ("mxfp8", "table", (300, 256, 6, 3, 128)),
+])
+def test_topk_table_input_matches_oracle_and_map_path(gpu_lib, routed, layout, shape):
+    T, H, E, K, I = shape
+    # MXFP8: the inputs of the MXFP8 cases above (see the recompute test)
+    cfg = gen.custom(T, H, E, K, I, routed=routed, layout=layout, short_frac=0.1 if routed == "bf16" else 0.05,
+                     short_max=max(1, K - 1), idx=(700 if routed == "bf16" else 400) + T)
+    top, rw = gen.routing_table(cfg)
+    dp = _dp(cfg, routing_table=(top, rw))
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    assert _check_table_state(dp, top) == 0
+    W = oracle_weights(dp)
+    tol = BF16_TOL if routed == "bf16" else MXFP8_TOL
+    ref = O.moe_forward_table(dp.np_x, top, rw, E, W)
+    err = rel_err(to_f64(dp.out), ref)
+    print(f"[parity] table out rel err {err:.3e}", flush=True)
+    assert err <= tol
+    g = O.moe_backward_table(dp.np_dy, dp.np_x, top, rw, E, W)
+    dpr = dp.dprobs.cpu().numpy().astype(np.float64)
+    assert dpr.shape == (T, K) and np.all(dpr[top < 0] == 0)
+    assert rel_err(to_f64(dp.dx), g["dx"]) <= tol and rel_err(dpr, g["dprobs"]) <= tol
+    # the dense-map call on the same decisions: same slots, so the weight gradients and
+    # the probability gradients agree bit for bit; out and dx sum the routes in another
+    # order, so only to rounding
+    mp = _dp(cfg)
+    mp.forward()
+    mp.backward()
+    torch.cuda.synchronize()
+    for a, b in zip(dp.mg_r1_list + dp.mg_r2_list + [dp.mg_s1, dp.mg_s2],
+                    mp.mg_r1_list + mp.mg_r2_list + [mp.mg_s1, mp.mg_s2]):
+        assert torch.equal(_bits(a), _bits(b)), "main_grad differs between table and map input"
+    dense = mp.dprobs.cpu().numpy()
+    m = top >= 0
+    dtab = np.zeros((T, K), np.float32)
+    dtab[m] = dense[np.nonzero(m)[0], top[m]]
+    assert np.array_equal(dtab.view(np.uint32), dp.dprobs.cpu().numpy().view(np.uint32))
+    assert rel_err(to_f64(dp.out), to_f64(mp.out)) <= 1e-2
+
+
+def test_topk_table_invalid_entries_are_dropped_and_reported(gpu_lib):
+    T, E, K = 96, 6, 3
+    cfg = gen.custom(T, 256, E, K, 128, idx=801)
+    top, rw = gen.routing_table(cfg)
+    bad = top.copy()
+    bad[5, 0], bad[5, 1], bad[5, 2] = 2, 2, -1      # the same expert twice
+    bad[40, 1] = E                                  # out of range
+    bad[77, 2] = -7                                 # negative other than -1
+    dp = _dp(cfg, routing_table=(bad, rw))
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    clean = bad.copy()
+    clean[5, 1] = -1
+    clean[40, 1] = -1
+    clean[77, 2] = -1
+    assert _check_table_state(dp, clean) == mk_status("MOE_ERR_ROUTE_INVALID")
+    W = oracle_weights(dp)
+    ref = O.moe_forward_table(dp.np_x, clean, rw, E, W)
+    assert rel_err(to_f64(dp.out), ref) <= BF16_TOL
+
+
+def mk_status(name):
+    import moe_megakernel_amd as mk
+    return getattr(mk, name)
+
+
+def test_topk_table_full_size_sampled(gpu_lib):
+    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 from the router's table."""
+    cfg = gen.config(2)
+    top, rw = gen.routing_table(cfg)
+    dp = _dp(cfg, routing_table=(top, rw))
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    assert _check_table_state(dp, top) == 0
+    W = oracle_weights(dp)
+    toks = sample_tokens(cfg.tokens, 32, seed=11)
+    ref = O.moe_forward_table(dp.np_x, top, rw, cfg.experts, W, tokens=toks)
+    assert rel_err(to_f64(dp.out[torch.as_tensor(toks, device=dp.out.device)]), ref) <= BF16_TOL
+    g = O.moe_backward_table(dp.np_dy, dp.np_x, top, rw, cfg.experts, W, tokens=toks, experts=[3, 60])
+    sel = torch.as_tensor(toks, device=dp.dx.device)
+    assert rel_err(to_f64(dp.dx[sel]), g["dx"]) <= BF16_TOL
+    assert rel_err(dp.dprobs[sel].cpu().numpy().astype(np.float64), g["dprobs"]) <= BF16_TOL
+    I = cfg.inter
+    for e in (3, 60):
+        d1 = to_f64(dp.mg_r1_list[e]) - dp.main_grad_start((2 * I, cfg.hidden), e)
+        assert rel_err(d1[:I], g["dW"][e][0]) <= BF16_TOL
+
+
+# ----------------------------------------------------------------------------------
 # BF16 main_grad: the call's contribution is rounded to BF16, then added with one BF16
 # rounding (the persistent accumulation is BF16)
 # ----------------------------------------------------------------------------------

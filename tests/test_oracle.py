@@ -282,6 +282,70 @@ def test_routed_only_edge_cases():
     assert _rel(out, _textbook_swiglu(xs, np.concatenate([wg, wu]), wd)) < 1e-13
 
 
+def _table_problem(T, H, E, K, I, seed, short=0.3):
+    cfg = gen.custom(T, H, E, K, I, short_frac=short, short_max=max(1, K - 1), idx=seed)
+    top, rw = gen.routing_table(cfg)
+    _, _, _, x, dy, W, d = _small_problem(T, H, E, K, I, seed=seed, short=short)
+    # the table scattered into a dense map and probabilities (independent of the oracle)
+    P = np.zeros((T, E))
+    M = np.zeros((T, E), np.uint8)
+    for t in range(T):
+        for k in range(K):
+            if top[t, k] >= 0:
+                P[t, top[t, k]] = rw[t, k]
+                M[t, top[t, k]] = 1
+    return cfg, top, rw, x, dy, W, d, torch.from_numpy(P), torch.from_numpy(M)
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 4, 3, 16), (24, 64, 6, 4, 32)])
+def test_table_input_matches_dense_autograd(shape):
+    """Router table input (any order, -1 anywhere, junk weights at -1) against the dense
+    autograd form built from the scattered table; dprobs is the [T, K] gather."""
+    cfg, top, rw, x, dy, W, d, P, M = _table_problem(*shape, seed=21)
+    assert (top == -1).any() and not np.all(np.diff(np.where(top < 0, 99, top), axis=1) >= 0)
+    E, K = cfg.experts, cfg.topk
+    out = O.moe_forward_table(x, top, rw, E, W)
+    assert _rel(out, dense_forward(d["x"], P, M, d["shared"], d["routed"]).numpy()) < 1e-12
+    g = O.moe_backward_table(dy, x, top, rw, E, W)
+    ref = dense_grads(d["x"], P, M, d["shared"], d["routed"], d["dy"])
+    assert _rel(g["dx"], ref["dx"].numpy()) < 1e-12
+    want = np.zeros_like(g["dprobs"])
+    for t in range(cfg.tokens):
+        for k in range(K):
+            if top[t, k] >= 0:
+                want[t, k] = ref["dprobs"][t, top[t, k]].item()
+    assert g["dprobs"].shape == (cfg.tokens, K)
+    assert _rel(g["dprobs"], want) < 1e-12
+    assert np.all(g["dprobs"][top < 0] == 0)
+    for e in range(E):
+        dg, du, dd = g["dW"][e]
+        assert _rel(np.concatenate([dg, du]), ref["drouted1"][e].numpy()) < 1e-12
+        assert _rel(dd, ref["drouted2"][e].numpy()) < 1e-12
+
+
+def test_table_row_order_and_pad_weights_do_not_matter():
+    cfg, top, rw, x, dy, W, d, P, M = _table_problem(12, 32, 5, 3, 16, seed=22)
+    E = cfg.experts
+    rng = np.random.default_rng(5)
+    perm = np.stack([rng.permutation(cfg.topk) for _ in range(cfg.tokens)])
+    top2 = np.take_along_axis(top, perm, axis=1)
+    rw2 = np.take_along_axis(rw, perm, axis=1)
+    rw2[top2 < 0] = 123.0
+    assert np.array_equal(O.moe_forward_table(x, top, rw, E, W), O.moe_forward_table(x, top2, rw2, E, W))
+    g1 = O.moe_backward_table(dy, x, top, rw, E, W)
+    g2 = O.moe_backward_table(dy, x, top2, rw2, E, W)
+    assert np.array_equal(g1["dx"], g2["dx"])
+    assert np.array_equal(np.take_along_axis(g1["dprobs"], perm, axis=1), g2["dprobs"])
+
+
+def test_check_table_rejects_invalid_entries():
+    ok = np.array([[0, -1, 2], [-1, -1, -1]], np.int32)
+    O.check_table(ok, 3)
+    for bad in ([[0, 3, -1], [1, 2, 0]], [[0, -2, 1], [1, 2, 0]], [[1, 1, -1], [0, 2, -1]]):
+        with pytest.raises(O.RouteInvalid):
+            O.check_table(np.array(bad, np.int32), 3)
+
+
 def test_sampled_rows_and_experts_equal_full_run():
     cfg, probs, rmap, x, dy, W, d = _small_problem(30, 32, 5, 2, 16, seed=13, short=0.2)
     full = O.moe_backward(dy, x, probs, rmap, cfg.topk, W)
