@@ -126,10 +126,11 @@ struct NoScale {
 //  MXFP8 scales: fas(r) / fbs(r) -> E8M0 row of tile row r (KC operand), or for a
 //              row-contiguous B, fbs(kb) -> E8M0 byte of (K block kb, tile column 0).
 // ---------------------------------------------------------------------------------
-template <class TL, int AM, int BMODE, bool FP8, class FA, class FB, class FAS, class FBS>
+template <class TL, int AM, int BMODE, bool FP8, bool BMAP = false, class FA, class FB, class FAS, class FBS>
 __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, const FB& fb, const FAS& fas,
                                          const FBS& fbs, uint8_t* lds, uint8_t* sc, bool wave_active,
-                                         int acols = TL::TM, uint8_t* pf_lds = nullptr, int bcols = TL::TN) {
+                                         int acols = TL::TM, uint8_t* pf_lds = nullptr, int bcols = TL::TN,
+                                         const int32_t* bmap = nullptr, int32_t* map_lds = nullptr) {
   static_assert(!(FP8 && AM == RC), "MXFP8 A operands are K-contiguous");
   static_assert(!FP8 || TL::KB == 128, "MXFP8 stages are 128 codes (4 scale blocks)");
   constexpr int KB = TL::KB;
@@ -143,6 +144,11 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
   // do not take: their scale DMAs vary per stage)
   constexpr int LPS = TL::A_DMA + TL::B_DMA + TL::PF_N;
   static_assert(!FP8 || TL::NS == 2, "MXFP8 tiles use two stages");
+  // BMAP: a row-contiguous B whose k-th row is source row bmap[k] (bmap null: row k).
+  // Stage kt's KST map entries are DMA'd into map_lds[(kt & 1) * 64 ..] by wave 0 with the
+  // stage before (two stages: every wait drains all loads, so the map has landed when the
+  // next issue reads it behind the barrier).
+  static_assert(!BMAP || (BMODE == RC && TL::NS == 2 && !FP8), "row-mapped B");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / TL::NWN, wn = w % TL::NWN;
@@ -245,6 +251,16 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     }
   };
 
+  const uint32_t map0 = BMAP ? lds_off(map_lds) : 0u;
+  auto map_issue = [&](int kt) __attribute__((always_inline)) {
+    if (w == 0) {
+      const int k = kt * KST + lane;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
+      if (lane < KST && k < kdim) src = reinterpret_cast<const uint8_t*>(bmap + k);
+      dma4(src, map0 + (kt & 1) * 256);
+    }
+  };
+
   auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
     const uint32_t sa = lds0 + slot * TL::STAGE, sb = sa + TL::A_BYTES;
     const int k0 = kt * KST;
@@ -265,8 +281,15 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
         dma16(pb[i] + kt * KB, m0v);
       } else {
         const int k = k0 + kb[i];
-        dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fb(k)) + cb[i] : zp, m0v);
+        int row = k;
+        if constexpr (BMAP) {
+          if (bmap) row = map_lds[(kt & 1) * 64 + kb[i]];
+        }
+        dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fb(row)) + cb[i] : zp, m0v);
       }
+    }
+    if constexpr (BMAP) {
+      if (bmap) map_issue(kt + 1);
     }
     if constexpr (FP8) {
       if constexpr (BMODE == RC) {   // this stage's [4][TN] block of B scales
@@ -299,7 +322,9 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     // in registers beside the accumulators) read and multiply one K step at a time.
     if constexpr (!FP8) {
       constexpr int NKS = KB / 32;   // 16-element K steps per stage
-      constexpr bool PRE = NKS * (TL::MI + TL::NJ) * 4 <= 64;
+      // (the row-mapped instantiation sits at its register cap: reading every fragment of
+      // the stage ahead there spills)
+      constexpr bool PRE = NKS * (TL::MI + TL::NJ) * 4 <= 64 && !BMAP;
       bf16x8_t a[NKS][TL::MI], b[NKS][TL::NJ];
       auto load = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
@@ -432,6 +457,13 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
   // ---- NS-stage pipeline, one barrier per stage.  At the top of step kt the wave's
   // DMAs of stage kt must have landed; those of the up to NS - 2 later stages may fly
   // (with PF, each stage's group of loads ends with its prefetch, which may fly too).
+  if constexpr (BMAP) {
+    if (bmap && nk > 0) {
+      map_issue(0);
+      wait_vm<0>();
+      __syncthreads();
+    }
+  }
 #pragma unroll
   for (int s = 0; s < TL::NS - 1; ++s)
     if (s < nk) issue(s, s);
@@ -529,7 +561,7 @@ struct TokArgs {
 
 // MXFP8 operands of the routed tiles of a token-dim GEMM (unused for BF16 routed weights).
 struct MxOperands {
-  const uint8_t* aq;     // routed A codes [rows][K]
+  const uint8_t* aq;     // routed A codes [rows][K] (FC1: one row per token)
   const uint8_t* as;     // routed A scales [rows][K/32]
   MxRef b0, b1;          // routed B: rowwise (forward) or columnwise (data gradient) copies
 };
@@ -595,8 +627,8 @@ __device__ __forceinline__ int wave_n() { return __builtin_amdgcn_readfirstlane(
 // MX: routed tiles take E4M3 x and rowwise E4M3 weights.
 struct Fc1Args {
   TokArgs t;
-  const uint16_t* xp;   // routed A [S][H]
-  const uint16_t* x;    // shared A [T][H]
+  const int32_t* slot_t;   // token of each routed slot
+  const uint16_t* x;       // A [T][H]: routed rows through slot_t, shared rows directly
   MatRef wg, wu, sg, su;
   MxOperands mx;        // b0 = gate, b1 = up
   uint16_t* ab;
@@ -612,12 +644,16 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
   __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
   __shared__ __align__(16) uint8_t sc[MX ? TL::SC_LDS : 16];
   __shared__ int sp[kMaxExperts + 2];
+  __shared__ int tok[TL::TM];   // token (x row) of each tile row
   const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, 2 * p.I / TL::TN, p.t.E, p.t.counts, p.t.T, sp);
   if (!tt.ok) return;
   const bool shared = tt.g == p.t.E;
   const int e = shared ? 0 : tt.g;
   const int64_t arow0 = shared ? tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int H = p.H, last = tt.rows - 1;
+  for (int i = threadIdx.x; i < tt.rows; i += TL::NTH)
+    tok[i] = shared ? tt.m0 + i : p.slot_t[arow0 + i];
+  __syncthreads();
   const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
   auto brow = [&](int rr) { return tt.nt * (TL::TN / 2) + (rr >> 6) * 32 + (rr & 31); };   // logical column
   Acc<TL> acc;
@@ -626,8 +662,8 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
   bool done = false;
   if constexpr (MX) {
     if (!shared) {
-      auto fa = [&](int r) { return p.mx.aq + (arow0 + min(r, last)) * H; };
-      auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (H / 32); };
+      auto fa = [&](int r) { return p.mx.aq + (int64_t)tok[min(r, last)] * H; };
+      auto fas = [&](int r) { return p.mx.as + (int64_t)tok[min(r, last)] * (H / 32); };
       auto fb = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).data.row(e, brow(rr)); };
       auto fbs = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).scale.row(e, brow(rr)); };
       tile_mma<TL, KC, KC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb);
@@ -635,8 +671,7 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
     }
   }
   if (!done) {
-    const uint16_t* abase = shared ? p.x : p.xp;
-    auto fa = [&](int r) { return abase + (arow0 + min(r, last)) * H; };
+    auto fa = [&](int r) { return p.x + (int64_t)tok[min(r, last)] * H; };
     const uint8_t* gb = shared ? p.sg.row(0, 0) : p.wg.row(e, 0);
     const uint8_t* ub = shared ? p.su.row(0, 0) : p.wu.row(e, 0);
     const int64_t gld = shared ? p.sg.ld_bytes : p.wg.ld_bytes;
@@ -854,6 +889,8 @@ struct WgradArgs {
   int T, E, has_shared;
   const uint16_t* a_r; const uint16_t* a_s; int64_t lda; int64_t a_s_row0;
   const uint16_t* b_r; const uint16_t* b_s; int64_t ldb; int64_t b_s_row0;
+  const int32_t* b_map;   // routed B row k of the group = b_r row b_map[offsets[g] + k]
+                          //   (null: row offsets[g] + k)
   GradRef g_lo, g_hi, s_lo, s_hi;   // part 0 -> *_lo, part 1 -> *_hi
   int parts, mpart;                 // M = parts * mpart; A column of part p row m: p * mpart + m
   int N;
@@ -871,6 +908,7 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
   using TL = TL_WG;
   __shared__ __align__(16) uint8_t lds[TL::LDS];
   __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
+  __shared__ __align__(16) int32_t bmap_lds[FC == 1 ? 128 : 4];
   const int mtp = (p.mpart + TL::TM - 1) / TL::TM, ntn = p.N / TL::TN;
   const int per = p.parts * mtp * ntn;
   const int nshared = p.has_shared ? per : 0;
@@ -906,10 +944,11 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
   const int64_t ar0 = shared ? p.a_s_row0 : (int64_t)p.offsets[g];
   const int64_t br0 = shared ? p.b_s_row0 : (int64_t)p.offsets[g];
   const uint16_t* A = (shared ? p.a_s : p.a_r) + (int64_t)part * p.mpart + m0;
-  const uint16_t* B = (shared ? p.b_s : p.b_r) + n0;
   const int64_t lda = p.lda, ldb = p.ldb;
+  const int32_t* bmap = (!shared && p.b_map) ? p.b_map + br0 : nullptr;
+  const uint16_t* B = (shared ? p.b_s : p.b_r) + n0 + (bmap ? 0 : br0 * ldb);
   auto fa = [&](int k) { return A + (ar0 + k) * lda; };
-  auto fb = [&](int k) { return B + (br0 + k) * ldb; };
+  auto fb = [&](int row) { return B + (int64_t)row * ldb; };
 
   constexpr int ES = MG16 ? 2 : 4;   // main_grad element bytes
   const GradRef& G = part == 0 ? (shared ? p.s_lo : p.g_lo) : (shared ? p.s_hi : p.g_hi);
@@ -920,7 +959,8 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
   Acc<TL> acc;
   zero_acc<TL>(acc);
   const bool active = wm * TL::WMR < mrows;
-  tile_mma<TL, RC, RC, false>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, active, mrows, pfb);
+  tile_mma<TL, RC, RC, false, FC == 1>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, active, mrows, pfb,
+                                        TL::TN, bmap, bmap_lds);
 
   // main_grad += acc, one slice of WMR rows per round: the waves of wave row `rd` park
   // their accumulators in LDS, then every thread adds pieces of 4 elements of whole rows

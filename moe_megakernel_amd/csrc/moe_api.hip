@@ -47,18 +47,18 @@ Dims dims_of(const moe_problem* p) {
   return d;
 }
 
-// The forward's activations the backward reads: the gathered routed input xp, the FC1
-// output ab = [a | b], h = silu(a) * b and the unweighted FC2 output y (routed rows, then
-// the shared expert's T rows).  Placed at the end of `saved`, or in recompute mode at the
-// start of the forward and backward workspaces.
+// The forward's activations the backward reads: the FC1 output ab = [a | b],
+// h = silu(a) * b and the unweighted FC2 output y (routed rows, then the shared expert's
+// T rows).  Routed FC1 inputs are the hidden-state rows themselves, reached through
+// slot_t, so no gathered copy exists.  Placed at the end of `saved`, or in recompute
+// mode at the start of the forward and backward workspaces.
 struct ActLayout {
-  size_t xp, ab, h, y, end;
+  size_t ab, h, y, end;
 };
 
 ActLayout act_layout(const Dims& d, size_t o) {
   ActLayout A;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
-  A.xp = take(2 * d.SM * d.H);
   A.ab = take(2 * d.R * 2 * d.I);
   A.h = take(2 * d.R * d.I);
   A.y = take(2 * d.R * d.H);
@@ -68,7 +68,7 @@ ActLayout act_layout(const Dims& d, size_t o) {
 
 // Byte offsets inside `saved`.
 struct SavedLayout {
-  size_t top, rw, counts, offsets, slot_of, slot_token, status, slot_w, tile_prefix, chunk_base,
+  size_t top, rw, counts, offsets, slot_of, slot_token, status, slot_w, slot_t, tile_prefix, chunk_base,
       chunk_counts, chunk_status, total;
   ActLayout act;     // not in recompute mode
 };
@@ -85,6 +85,7 @@ SavedLayout saved_layout(const Dims& d) {
   L.slot_token = take(4 * d.SM);
   L.status = take(4);
   L.slot_w = take(4 * d.SM);
+  L.slot_t = take(4 * d.SM);
   L.tile_prefix = take(4 * (d.E + 2));
   L.chunk_base = take(4 * d.nchunks * d.E);
   L.chunk_counts = take(4 * d.nchunks * d.E);
@@ -134,7 +135,7 @@ BwdLayout bwd_layout(const Dims& d) {
 }
 
 // Forward workspace: the activations in recompute mode, then the MXFP8 codes + scales of
-// the routed FC1 input (x) and FC2 input (h).
+// the routed FC1 input (x, one row per token) and FC2 input (h, one row per slot).
 struct FwdLayout {
   size_t xq, xs, hq, hs, total;
   ActLayout act;     // recompute mode only
@@ -149,8 +150,8 @@ FwdLayout fwd_layout(const Dims& d) {
     o = L.act.end;
   }
   if (d.mx) {
-    L.xq = take(d.SM * d.H);
-    L.xs = take(d.SM * d.H / 32);
+    L.xq = take(d.T * d.H);
+    L.xs = take(d.T * d.H / 32);
     L.hq = take(d.SM * d.I);
     L.hs = take(d.SM * d.I / 32);
   }
@@ -361,27 +362,27 @@ unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
 
 // Pointers of one run of the routed + shared expert forward (F3-F6).
 struct FwdPtrs {
-  const int32_t *slot_of, *counts, *offsets, *tile_prefix;
-  uint16_t *xp, *ab, *h, *y;
+  const int32_t *slot_t, *counts, *offsets, *tile_prefix;
+  uint16_t *ab, *h, *y;
   uint8_t *xq, *xs, *hq, *hs;   // MXFP8 staging (unused for BF16 routed weights)
 };
 
-// Dispatch gather, FC1 + SwiGLU, FC2 (routed and shared expert in the same launches),
-// from the routing state already in place.  `again`: the backward's recomputation in
+// FC1 + SwiGLU (routed rows read from x through slot_t: the dispatch gather happens
+// in the GEMM's own DMA), FC2; routed and shared expert in the same launches, from the
+// routing state already in place.  `again`: the backward's recomputation in
 // recompute mode (the same kernels on the same inputs, so the same bits; only the timer
 // names differ).
 moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, const moe_weights* w,
                            hipStream_t st, bool again) {
   const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
-  // F3 dispatch gather (+ Q: MXFP8 codes of the routed FC1 input)
-  MOE_TRY(launch(again ? "recompute_gather_x" : "gather_x", st, [&] {
-    if (d.mx)
-      hipLaunchKernelGGL(k_gather_rows<true>, dim3(T), dim3(kRowThreads), 0, st,
-                         x, H, K, P.slot_of, P.xp, P.xq, P.xs);
-    else
-      hipLaunchKernelGGL(k_gather_rows<false>, dim3(T), dim3(kRowThreads), 0, st,
-                         x, H, K, P.slot_of, P.xp, (uint8_t*)nullptr, (uint8_t*)nullptr);
-  }));
+  // Q: MXFP8 codes of x, one row per token (the routed FC1 input; F3's gather is the
+  // FC1 kernel's row addressing)
+  if (d.mx) {
+    MOE_TRY(launch(again ? "recompute_quantize_x" : "quantize_x", st, [&] {
+      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, x, d.T, H, (const int32_t*)nullptr,
+                         P.xq, P.xs);
+    }));
+  }
 
   gemm::TokArgs ta;
   ta.counts = P.counts;
@@ -394,7 +395,7 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   // F4 + F6: routed and shared FC1 with the SwiGLU epilogue, one launch
   gemm::Fc1Args a1;
   a1.t = ta;
-  a1.xp = P.xp;
+  a1.slot_t = P.slot_t;
   a1.x = x;
   a1.wg = matref(w->routed_gate, w->routed_gate.data, 2);
   a1.wu = matref(w->routed_up, w->routed_up.data, 2);
@@ -557,12 +558,13 @@ moe_status forward_impl(const moe_problem* p, const void* hidden, const float* p
   if (T == 0) return MOE_OK;
   MOE_TRY(launch("route_rank", st, [&] {
     hipLaunchKernelGGL(k_route_rank, dim3(nch), dim3(kRouteChunk * kMaxTopk), 0, st, I32(L.top), F32(L.rw), T, E, K,
-                       I32(L.chunk_base), I32(L.offsets), I32(L.slot_of), I32(L.slot_token), F32(L.slot_w));
+                       I32(L.chunk_base), I32(L.offsets), I32(L.slot_of), I32(L.slot_token), I32(L.slot_t),
+                       F32(L.slot_w));
   }));
   FwdPtrs P;
-  P.slot_of = I32(L.slot_of); P.counts = I32(L.counts); P.offsets = I32(L.offsets);
+  P.slot_t = I32(L.slot_t); P.counts = I32(L.counts); P.offsets = I32(L.offsets);
   P.tile_prefix = I32(L.tile_prefix);
-  P.xp = U16(A.xp); P.ab = U16(A.ab); P.h = U16(A.h); P.y = U16(A.y);
+  P.ab = U16(A.ab); P.h = U16(A.h); P.y = U16(A.y);
   P.xq = WS + F.xq; P.xs = WS + F.xs; P.hq = WS + F.hq; P.hs = WS + F.hs;
   MOE_TRY(experts_forward(d, P, static_cast<const uint16_t*>(hidden), w, st, false));
 
@@ -629,9 +631,9 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
 
   if (d.rc) {   // recompute mode: F3-F6 again from x and the saved routing state
     FwdPtrs P;
-    P.slot_of = I32(L.slot_of); P.counts = I32(L.counts); P.offsets = I32(L.offsets);
+    P.slot_t = I32(L.slot_t); P.counts = I32(L.counts); P.offsets = I32(L.offsets);
     P.tile_prefix = I32(L.tile_prefix);
-    P.xp = WU16(A.xp); P.ab = WU16(A.ab); P.h = WU16(A.h); P.y = WU16(A.y);
+    P.ab = WU16(A.ab); P.h = WU16(A.h); P.y = WU16(A.y);
     P.xq = W + B.fxq; P.xs = W + B.fxs; P.hq = W + B.fhq; P.hs = W + B.fhs;
     MOE_TRY(experts_forward(d, P, x, w, st, true));
   }
@@ -726,6 +728,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a5.T = T; a5.E = E; a5.has_shared = d.hs ? 1 : 0;
   a5.a_r = WU16(B.dyw); a5.a_s = dy; a5.lda = H; a5.a_s_row0 = 0;
   a5.b_r = U16(A.h); a5.b_s = U16(A.h); a5.ldb = I; a5.b_s_row0 = d.SM;
+  a5.b_map = nullptr;
   a5.g_lo = gradref(mg->routed_down); a5.g_hi = a5.g_lo;
   a5.s_lo = gradref(mg->shared_down); a5.s_hi = a5.s_lo;
   a5.parts = 1; a5.mpart = H;
@@ -745,7 +748,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a6.offsets = I32(L.offsets);
   a6.T = T; a6.E = E; a6.has_shared = d.hs ? 1 : 0;
   a6.a_r = WU16(B.dfc1); a6.a_s = WU16(B.dfc1); a6.lda = 2 * (int64_t)I; a6.a_s_row0 = d.SM;
-  a6.b_r = U16(A.xp); a6.b_s = x; a6.ldb = H; a6.b_s_row0 = 0;
+  a6.b_r = x; a6.b_s = x; a6.ldb = H; a6.b_s_row0 = 0;
+  a6.b_map = I32(L.slot_t);   // routed rows of x through the slot's token
   a6.g_lo = gradref(mg->routed_gate); a6.g_hi = gradref(mg->routed_up);
   a6.s_lo = gradref(mg->shared_gate); a6.s_hi = gradref(mg->shared_up);
   a6.parts = 2; a6.mpart = I;

@@ -223,7 +223,8 @@ __global__ __launch_bounds__(kScanThreads) void k_route_scan(
 __global__ __launch_bounds__(kRouteChunk * kMaxTopk) void k_route_rank(
     const int32_t* __restrict__ top, const float* __restrict__ rw, int T, int E, int K,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ slot_of, int32_t* __restrict__ slot_token, float* __restrict__ slot_w) {
+    int32_t* __restrict__ slot_of, int32_t* __restrict__ slot_token, int32_t* __restrict__ slot_t,
+    float* __restrict__ slot_w) {
   __shared__ int tab[kRouteChunk * kMaxTopk];
   const int tid = threadIdx.x;
   const int tb = blockIdx.x * kRouteChunk;
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(kRouteChunk * kMaxTopk) void k_route_rank(
   const int s = offsets[e] + r;
   slot_of[(int64_t)tb * K + tid] = s;
   slot_token[s] = tb * K + tid;
+  slot_t[s] = tb + i;   // the token alone: the x row the GEMMs read for this slot
   slot_w[s] = rw[(int64_t)tb * K + tid];
 }
 

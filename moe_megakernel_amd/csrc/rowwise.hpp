@@ -1,4 +1,4 @@
-// Per-token row kernels: dispatch gather, probability-weighted combine, the
+// Per-token row kernels: MXFP8 quantisation of rows, probability-weighted combine, the
 // backward's weighted gather of dy fused with the router-probability gradient,
 // and the data-gradient combine.  All are HBM-bound row copies/reductions: each
 // thread moves 16-byte pieces (8 bf16) of a row, and the loads of two pieces are in
@@ -46,49 +46,6 @@ __device__ __forceinline__ uint4 pack_bf8(const float (&a)[8]) {
   o.x = pack_bf2(a[0], a[1]); o.y = pack_bf2(a[2], a[3]);
   o.z = pack_bf2(a[4], a[5]); o.w = pack_bf2(a[6], a[7]);
   return o;
-}
-
-// xp[slot_of[t,k]] = x[t] for every valid route (dispatch into expert-contiguous rows).
-// With Q, the row is also quantised to MXFP8 along H (one E8M0 scale per 32 elements)
-// into xq / xs, the A operand of the scaled-FP8 FC1.  One block per token.
-template <bool Q>
-__global__ __launch_bounds__(kRowThreads) void k_gather_rows(
-    const uint16_t* __restrict__ x, int H, int K, const int32_t* __restrict__ slot_of,
-    uint16_t* __restrict__ xp, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
-  const int t = blockIdx.x;
-  int s[kMaxTopk];
-  load_slots(slot_of, t, K, s);
-  const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * H);
-  const int nc = H / 8;
-  for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
-    uint4 v[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = c0 + u * kRowThreads;
-      if (c < nc) v[u] = src[c];
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = c0 + u * kRowThreads;
-      if (c >= nc) break;
-      uint2 q = make_uint2(0, 0);
-      uint32_t sc = 0;
-      if constexpr (Q) {
-        float f[8];
-        unpack_bf16x8(v[u], f);
-        sc = mx_quantize8(f, quad_max(absmax8(f)), q);
-      }
-#pragma unroll
-      for (int k = 0; k < kMaxTopk; ++k) {
-        if (s[k] < 0) continue;
-        reinterpret_cast<uint4*>(xp + (int64_t)s[k] * H)[c] = v[u];
-        if constexpr (Q) {
-          reinterpret_cast<uint2*>(xq + (int64_t)s[k] * H)[c] = q;
-          if ((c & 3) == 0) xs[(int64_t)s[k] * (H / 32) + (c >> 2)] = (uint8_t)sc;
-        }
-      }
-    }
-  }
 }
 
 // MXFP8 quantisation of bf16 rows along their length: payload [rows][cols] E4M3 and
