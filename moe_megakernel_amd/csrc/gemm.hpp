@@ -596,7 +596,10 @@ struct MxOperands {
 #define MOE_TL_DG1_MX 192, 256, 2, 4, 2, 1, 1
 #endif
 #ifndef MOE_TL_WG
-#define MOE_TL_WG 128, 128, 2, 2, 2, 4, 0, 64
+#define MOE_TL_WG 128, 256, 2, 4, 2, 2, 0, 64
+#endif
+#ifndef MOE_TL_WG16
+#define MOE_TL_WG16 128, 128, 2, 2, 2, 4, 0, 64
 #endif
 template <bool MX> struct Shapes;
 template <> struct Shapes<false> {
@@ -607,7 +610,10 @@ template <> struct Shapes<true> {
   using FC1 = Tile<MOE_TL_FC1_MX>; using FC2 = Tile<MOE_TL_FC2_MX>;
   using DG2 = Tile<MOE_TL_DG2_MX>; using DG1 = Tile<MOE_TL_DG1_MX>;
 };
-using TL_WG = Tile<MOE_TL_WG>;
+// weight gradients: FP32 main_grad (MG16 = false) and BF16 main_grad (true; half the
+// read-modify-write bytes per tile, so smaller tiles at higher occupancy win there)
+template <bool MG16>
+using TL_WG = typename std::conditional<MG16, Tile<MOE_TL_WG16>, Tile<MOE_TL_WG>>::type;
 template <bool MX>
 constexpr int bm_of() { return Shapes<MX>::FC1::TM; }
 static_assert(Shapes<false>::FC2::TM == bm_of<false>() && Shapes<false>::DG2::TM == bm_of<false>() &&
@@ -896,20 +902,22 @@ struct WgradArgs {
   int N;
 };
 
+template <bool MG16>
 __host__ __device__ inline int wgrad_tiles_per_group(int parts, int mpart, int N) {
-  return parts * ((mpart + TL_WG::TM - 1) / TL_WG::TM) * (N / TL_WG::TN);
+  using TL = TL_WG<MG16>;
+  return parts * ((mpart + TL::TM - 1) / TL::TM) * ((N + TL::TN - 1) / TL::TN);
 }
 
 // FC is 1 or 2 (which projection's gradient); it only names the kernel symbol apart.
 // MG16: BF16 main_grad (the contribution is rounded to BF16, then added with one BF16
 // rounding), else FP32.
 template <int FC, bool MG16>
-__global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) {
-  using TL = TL_WG;
+__global__ __launch_bounds__(TL_WG<MG16>::NTH, TL_WG<MG16>::MINB) void k_wgrad(WgradArgs p) {
+  using TL = TL_WG<MG16>;
   __shared__ __align__(16) uint8_t lds[TL::LDS];
   __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
   __shared__ __align__(16) int32_t bmap_lds[FC == 1 ? 128 : 4];
-  const int mtp = (p.mpart + TL::TM - 1) / TL::TM, ntn = p.N / TL::TN;
+  const int mtp = (p.mpart + TL::TM - 1) / TL::TM, ntn = (p.N + TL::TN - 1) / TL::TN;
   const int per = p.parts * mtp * ntn;
   const int nshared = p.has_shared ? per : 0;
   int g, tile;
@@ -940,6 +948,7 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
   const int sbn = ntn / sn;
   const int mt = (sblk / sbn) * sm + sin / sn, nt = (sblk % sbn) * sn + sin % sn;
   const int m0 = mt * TL::TM, n0 = nt * TL::TN;
+  const int ncols = min(TL::TN, p.N - n0);   // the last N tile may be partial (a multiple of 128)
   const int mrows = min(TL::TM, p.mpart - m0);
   const int64_t ar0 = shared ? p.a_s_row0 : (int64_t)p.offsets[g];
   const int64_t br0 = shared ? p.b_s_row0 : (int64_t)p.offsets[g];
@@ -960,54 +969,63 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
   zero_acc<TL>(acc);
   const bool active = wm * TL::WMR < mrows;
   tile_mma<TL, RC, RC, false, FC == 1>(acc, kdim, fa, fb, NoScale{}, NoScale{}, lds, nullptr, active, mrows, pfb,
-                                        TL::TN, bmap, bmap_lds);
+                                        ncols, bmap, bmap_lds);
 
-  // main_grad += acc, one slice of WMR rows per round: the waves of wave row `rd` park
-  // their accumulators in LDS, then every thread adds pieces of 4 elements of whole rows
-  // to main_grad (coalesced row reads and writes).  The main_grad loads of a round are
-  // issued before its LDS traffic.  LDS slice [WMR][TN] fp32; 16-byte chunk c of row r
+  // main_grad += acc, one slice of SR rows per round: the waves of the wave row holding
+  // them park those accumulators in LDS, then every thread adds pieces of 4 elements of
+  // whole rows to main_grad (coalesced row reads and writes).  The main_grad loads of a
+  // round are issued before its LDS traffic.  LDS slice [SR][TN] fp32; 16-byte chunk c of row r
   // sits at c ^ 8 ((r >> 2) & 1), so the two row groups a wave writes at once use
   // disjoint banks.
   constexpr int CPRW = TL::TN / 4;                       // 16-byte chunks per row
-  constexpr int CPT = TL::WMR * CPRW / TL::NTH;          // chunks per thread per round
-  static_assert(TL::WMR * TL::TN * 4 <= TL::LDS && (TL::WMR * CPRW) % TL::NTH == 0, "epilogue slice");
+  // rows per round: a wave row, or (when its slice does not fit the LDS) the largest
+  // multiple of 32 rows that does
+  constexpr int SR = (TL::WMR * TL::TN * 4 <= TL::LDS) ? TL::WMR : 32 * (TL::LDS / (32 * TL::TN * 4));
+  constexpr int NR = TL::TM / SR;                        // rounds
+  constexpr int CPT = SR * CPRW / TL::NTH;               // chunks per thread per round
+  static_assert(SR >= 32 && TL::WMR % SR == 0 && (SR * CPRW) % TL::NTH == 0, "epilogue slice");
   float* ct = reinterpret_cast<float*>(lds);
   const int t = threadIdx.x;
   auto sw = [](int r) { return ((r >> 2) & 1) << 3; };
 #pragma unroll
-  for (int rd = 0; rd < TL::NWM; ++rd) {
+  for (int q = 0; q < NR; ++q) {
+    const int r0 = q * SR;                               // first tile row of the round
+    const int rd = r0 / TL::WMR, ib = (r0 % TL::WMR) / 32;   // its wave row and first 32-row block
     f32x4_t mg[CPT];
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = q * TL::NTH + t, row = c / CPRW, cc = c % CPRW;
-      const int grow = rd * TL::WMR + row;
+    for (int u = 0; u < CPT; ++u) {
+      const int c = u * TL::NTH + t, row = c / CPRW, cc = c % CPRW;
+      const int grow = r0 + row;
       const uint8_t* src = cb + grow * ldc + cc * 4 * ES;
+      const bool in = grow < mrows && 4 * cc < ncols;
       if constexpr (MG16) {
-        const uint2 v = grow < mrows ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
-        mg[q] = f32x4_t{lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y)};
+        const uint2 v = in ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
+        mg[u] = f32x4_t{lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y)};
       } else {
-        mg[q] = grow < mrows ? *reinterpret_cast<const f32x4_t*>(src) : f32x4_t{};
+        mg[u] = in ? *reinterpret_cast<const f32x4_t*>(src) : f32x4_t{};
       }
     }
     __syncthreads();   // the LDS slice is free (K loop or previous round done)
     if (wm == rd) {
 #pragma unroll
-      for (int i = 0; i < TL::MI; ++i)
+      for (int i = 0; i < TL::MI; ++i) {
+        if (i < ib || i >= ib + SR / 32) continue;
 #pragma unroll
         for (int j = 0; j < TL::NJ; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int row = (i - ib) * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
             const int col = acc_col<TL>(wn, j, lane);
             ct[row * TL::TN + (((col >> 2) ^ sw(row)) << 2) + (col & 3)] = acc[i][j][r];
           }
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int c = q * TL::NTH + t, row = c / CPRW, cc = c % CPRW;
-      const int grow = rd * TL::WMR + row;
-      if (grow < mrows) {
+    for (int u = 0; u < CPT; ++u) {
+      const int c = u * TL::NTH + t, row = c / CPRW, cc = c % CPRW;
+      const int grow = r0 + row;
+      if (grow < mrows && 4 * cc < ncols) {
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(ct + row * TL::TN + ((cc ^ sw(row)) << 2));
         uint8_t* dst = cb + grow * ldc + cc * 4 * ES;
         if constexpr (MG16) {
@@ -1015,10 +1033,10 @@ __global__ __launch_bounds__(TL_WG::NTH, TL_WG::MINB) void k_wgrad(WgradArgs p) 
           // sum of two BF16 values rounds to the same BF16 as their exact sum)
           f32x4_t r;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) r[u] = mg[q][u] + bf2f(f2bf(v[u]));
+          for (int k = 0; k < 4; ++k) r[k] = mg[u][k] + bf2f(f2bf(v[k]));
           *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3]));
         } else {
-          *reinterpret_cast<f32x4_t*>(dst) = mg[q] + v;
+          *reinterpret_cast<f32x4_t*>(dst) = mg[u] + v;
         }
       }
     }

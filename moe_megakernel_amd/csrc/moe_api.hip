@@ -360,6 +360,20 @@ int64_t max_mtiles(const Dims& d) {
 }
 unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
 
+// Weight-gradient launch: the shared expert's tiles first (when present), then E groups
+// of routed tiles rounded up to a multiple of 8 blocks (one chunk per XCD).
+template <int FC, bool MG16>
+void launch_wgrad_t(const gemm::WgradArgs& a, const Dims& d, hipStream_t st) {
+  const int per = gemm::wgrad_tiles_per_group<MG16>(a.parts, a.mpart, a.N);
+  const dim3 g((d.hs ? per : 0) + grid8((int64_t)d.E * per));
+  hipLaunchKernelGGL((gemm::k_wgrad<FC, MG16>), g, dim3(gemm::TL_WG<MG16>::NTH), 0, st, a);
+}
+template <int FC>
+void launch_wgrad(const gemm::WgradArgs& a, const Dims& d, bool mg16, hipStream_t st) {
+  if (mg16) launch_wgrad_t<FC, true>(a, d, st);
+  else launch_wgrad_t<FC, false>(a, d, st);
+}
+
 // Pointers of one run of the routed + shared expert forward (F3-F6).
 struct FwdPtrs {
   const int32_t *slot_t, *counts, *offsets, *tile_prefix;
@@ -733,14 +747,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a5.s_lo = gradref(mg->shared_down); a5.s_hi = a5.s_lo;
   a5.parts = 1; a5.mpart = H;
   a5.N = I;
-  {
-    const int per = gemm::wgrad_tiles_per_group(1, H, I);
-    MOE_TRY(launch("wgrad_fc2", st, [&] {
-      const dim3 g((d.hs ? per : 0) + grid8((int64_t)E * per));
-      if (grad_bf16(mg->routed_gate)) hipLaunchKernelGGL((gemm::k_wgrad<2, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a5);
-      else hipLaunchKernelGGL((gemm::k_wgrad<2, false>), g, dim3(gemm::TL_WG::NTH), 0, st, a5);
-    }));
-  }
+  MOE_TRY(launch("wgrad_fc2", st, [&] { launch_wgrad<2>(a5, d, grad_bf16(mg->routed_gate), st); }));
 
   // B5 (+B6): FC1 weight gradient: main_grad_{gate,up}[e] += dfc1^T xp
   gemm::WgradArgs a6;
@@ -754,14 +761,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a6.s_lo = gradref(mg->shared_gate); a6.s_hi = gradref(mg->shared_up);
   a6.parts = 2; a6.mpart = I;
   a6.N = H;
-  {
-    const int per = gemm::wgrad_tiles_per_group(2, I, H);
-    MOE_TRY(launch("wgrad_fc1", st, [&] {
-      const dim3 g((d.hs ? per : 0) + grid8((int64_t)E * per));
-      if (grad_bf16(mg->routed_gate)) hipLaunchKernelGGL((gemm::k_wgrad<1, true>), g, dim3(gemm::TL_WG::NTH), 0, st, a6);
-      else hipLaunchKernelGGL((gemm::k_wgrad<1, false>), g, dim3(gemm::TL_WG::NTH), 0, st, a6);
-    }));
-  }
+  MOE_TRY(launch("wgrad_fc1", st, [&] { launch_wgrad<1>(a6, d, grad_bf16(mg->routed_gate), st); }));
   return MOE_OK;
 }
 
