@@ -587,3 +587,76 @@ def test_bf16_main_grad_matches_oracle(gpu_lib, routed, layout, shape):
     print(f"[parity] bf16 main_grad = bf16(before + bf16(fp32 contribution)): exact fraction min "
           f"{min(match):.5f}", flush=True)
     assert min(match) >= 0.999
+
+
+# ----------------------------------------------------------------------------------
+# the options together: routed-only x recompute x table input x BF16 main_grad
+# ----------------------------------------------------------------------------------
+def test_feature_combinations_are_consistent(gpu_lib):
+    """Relations that must hold exactly between the modes, on one set of inputs:
+    recompute changes no bit; table input gives the map input's weight and probability
+    gradients bit for bit; routed-only leaves the routed gradients unchanged bit for bit;
+    BF16 main_grad is bf16(before + bf16(the FP32 run's contribution)).  Plus the oracle
+    on the mode with every option on."""
+    T, H, E, K, I = 300, 256, 6, 3, 128
+    cfg = gen.custom(T, H, E, K, I, short_frac=0.1, short_max=2, idx=900)
+    table = gen.routing_table(cfg)
+    runs = {}
+    for shared in (True, False):
+        for rc in (False, True):
+            for tab in (False, True):
+                for mgd in ("fp32", "bf16"):
+                    dp = _dp(cfg, shared=shared, recompute=rc, routing_table=table if tab else None,
+                             main_grad_dtype=mgd)
+                    dp.forward()
+                    dp.backward()
+                    runs[(shared, rc, tab, mgd)] = dp
+    torch.cuda.synchronize()
+
+    def dprobs_table(dp, tab):
+        if tab:
+            return dp.dprobs.cpu().numpy()
+        dense = dp.dprobs.cpu().numpy()
+        top = table[0]
+        out = np.zeros(top.shape, np.float32)
+        m = top >= 0
+        out[m] = dense[np.nonzero(m)[0], top[m]]
+        return out
+
+    routed = lambda dp: dp.mg_r1_list + dp.mg_r2_list
+    for key, dp in runs.items():
+        shared, rc, tab, mgd = key
+        base = runs[(shared, False, tab, mgd)]
+        if rc:   # recompute: every output bit for bit
+            _assert_same_bits(base, dp)
+        if tab:  # table vs map: gradients of the weights and of the router weights
+            mp = runs[(shared, rc, False, mgd)]
+            for a, b in zip(routed(dp) + [dp.mg_s1, dp.mg_s2], routed(mp) + [mp.mg_s1, mp.mg_s2]):
+                assert torch.equal(_bits(a), _bits(b))
+            assert np.array_equal(dprobs_table(dp, True).view(np.uint32), dprobs_table(mp, False).view(np.uint32))
+        if not shared:  # routed gradients do not depend on the shared expert
+            fu = runs[(True, rc, tab, mgd)]
+            for a, b in zip(routed(dp), routed(fu)):
+                assert torch.equal(_bits(a), _bits(b))
+            assert np.array_equal(dprobs_table(dp, tab).view(np.uint32), dprobs_table(fu, tab).view(np.uint32))
+        if mgd == "bf16":   # per-element semantics against the FP32 run's contribution
+            f32 = runs[(shared, rc, tab, "fp32")]
+            match = []
+            for e in range(E):
+                for t16, t32, shape in ((dp.mg_r1_list[e], f32.mg_r1_list[e], (2 * I, H)),
+                                        (dp.mg_r2_list[e], f32.mg_r2_list[e], (H, I))):
+                    start = dp.main_grad_start(shape, e)
+                    model = O.main_grad_after(start, to_f64(t32) - start, "bf16")
+                    match.append(np.mean(to_f64(t16) == model))
+            assert min(match) >= 0.999, (key, min(match))
+    # every option on, against the oracle
+    dp = runs[(False, True, True, "fp32")]
+    W = O.Weights.from_bits(I, None, None, lambda e: dp.np_routed[e], "bf16")
+    ref = O.moe_forward_table(dp.np_x, table[0], table[1], E, W)
+    assert rel_err(to_f64(dp.out), ref) <= BF16_TOL
+    g = O.moe_backward_table(dp.np_dy, dp.np_x, table[0], table[1], E, W)
+    assert rel_err(to_f64(dp.dx), g["dx"]) <= BF16_TOL
+    assert rel_err(dp.dprobs.cpu().numpy().astype(np.float64), g["dprobs"]) <= BF16_TOL
+    for e in range(E):
+        d2 = to_f64(dp.mg_r2_list[e]) - dp.main_grad_start((H, I), e)
+        assert rel_err(d2, g["dW"][e][2]) <= BF16_TOL
