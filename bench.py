@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload index (2: 4096-token BF16 layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--main-grad", choices=("fp32", "bf16"), default="fp32",
                     help="main_grad dtype (bf16: contribution rounded to BF16 before a BF16 reduction-store)")
     ap.add_argument("--routed-only", action="store_true",
