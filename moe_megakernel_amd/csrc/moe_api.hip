@@ -520,14 +520,14 @@ namespace {
 
 // Both forward entry points: the routing is the dense map + probabilities (rmap, probs),
 // or the router's fixed-width table (top_in, rw_in).
-moe_status forward_impl(const moe_problem* p, const void* hidden, const float* probs,
+moe_status forward_impl(bool table, const moe_problem* p, const void* hidden, const float* probs,
                         const uint8_t* routing_map, const int32_t* top_in, const float* rw_in,
                         const moe_weights* w, void* out, void* saved, void* workspace,
                         size_t workspace_bytes, void* stream) {
   MOE_TRY(check_problem(p));
+  if (((p->flags & MOE_FLAG_TOPK_ROUTING) != 0) != table) return MOE_ERR_UNSUPPORTED;
   MOE_TRY(check_weights(p, w));
   const Dims d = dims_of(p);
-  if (d.tk != (top_in != nullptr || rw_in != nullptr)) return MOE_ERR_UNSUPPORTED;
   const bool have_routing = d.tk ? (top_in && rw_in) : (probs && routing_map);
   if (d.T > 0 && (!hidden || !have_routing || !out)) return MOE_ERR_NULL;
   if (!saved) return MOE_ERR_WORKSPACE;
@@ -597,19 +597,14 @@ extern "C" {
 moe_status moe_forward(const moe_problem* p, const void* hidden, const float* probs,
                        const uint8_t* routing_map, const moe_weights* w, void* out, void* saved,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (p && (p->flags & MOE_FLAG_TOPK_ROUTING)) return MOE_ERR_UNSUPPORTED;
-  return forward_impl(p, hidden, probs, routing_map, nullptr, nullptr, w, out, saved, workspace,
+  return forward_impl(false, p, hidden, probs, routing_map, nullptr, nullptr, w, out, saved, workspace,
                       workspace_bytes, stream);
 }
 
 moe_status moe_forward_topk(const moe_problem* p, const void* hidden, const int32_t* top_experts,
                             const float* router_weights, const moe_weights* w, void* out, void* saved,
                             void* workspace, size_t workspace_bytes, void* stream) {
-  if (p && !(p->flags & MOE_FLAG_TOPK_ROUTING)) return MOE_ERR_UNSUPPORTED;
-  if (!top_experts || !router_weights) {
-    if (p && p->tokens > 0) return MOE_ERR_NULL;
-  }
-  return forward_impl(p, hidden, nullptr, nullptr, top_experts, router_weights, w, out, saved, workspace,
+  return forward_impl(true, p, hidden, nullptr, nullptr, top_experts, router_weights, w, out, saved, workspace,
                       workspace_bytes, stream);
 }
 

@@ -163,16 +163,27 @@ def test_forward_backward_bitwise_deterministic(gpu_lib):
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a, b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
 
 
-def test_zero_tokens_is_a_no_op(gpu_lib):
+@pytest.mark.parametrize("flags", [1, 0, 1 | 2, 1 | 4, 2 | 4])
+def test_zero_tokens_is_a_no_op(gpu_lib, flags):
+    """An empty batch in every mode (shared, routed-only, recompute, table input): the
+    calls succeed, read no input and leave every main_grad as it was."""
     import moe_megakernel_amd as mk
-    p = mk.problem(0, 256, 128, 4, 2)
+    p = mk.problem(0, 256, 128, 4, 2, flags=flags)
     layer = mk.Layer(p)
     dp = _dp(gen.custom(4, 256, 4, 2, 128, idx=304), backward=True)
+    before = [t.clone() for t in dp.mg_r1_list + dp.mg_r2_list + [dp.mg_s1, dp.mg_s2]]
     empty = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
-    layer.forward(empty, torch.empty(0, 4, device="cuda"), torch.empty(0, 4, dtype=torch.uint8, device="cuda"),
-                  dp.weights, empty)
+    if flags & mk.MOE_FLAG_TOPK_ROUTING:
+        layer.forward_topk(empty, torch.empty(0, 2, dtype=torch.int32, device="cuda"),
+                           torch.empty(0, 2, device="cuda"), dp.weights, empty)
+    else:
+        layer.forward(empty, torch.empty(0, 4, device="cuda"), torch.empty(0, 4, dtype=torch.uint8, device="cuda"),
+                      dp.weights, empty)
     layer.backward(empty, empty, dp.weights, empty, torch.empty(0, 4, device="cuda"), dp.main_grads)
     torch.cuda.synchronize()
+    after = dp.mg_r1_list + dp.mg_r2_list + [dp.mg_s1, dp.mg_s2]
+    assert all(torch.equal(a, b) for a, b in zip(before, after))
+    assert int(layer.routing_state()["status_word"][0]) == 0
 
 
 @pytest.mark.parametrize("idx", [2])
