@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "config", "routing", "routing_table", "hidden", "grad_out",
-    "shared_weights", "routed_expert", "routed_all", "main_grad_pattern",
+    "shared_weights", "shared_gate_weight", "routed_expert", "routed_all", "main_grad_pattern",
     "to_bf16_bits", "mxfp8_quantize",
 ]
 
@@ -76,7 +76,7 @@ def custom(tokens, hidden, experts, topk, inter, *, routed="bf16", layout="singl
 # random streams
 # ----------------------------------------------------------------------------------
 _TAGS = {"logits": 1, "x": 2, "shared_fc1": 3, "shared_fc2": 4, "routed_fc1": 5,
-         "routed_fc2": 6, "short": 7, "dy": 8, "balanced": 9, "table": 10}
+         "routed_fc2": 6, "short": 7, "dy": 8, "balanced": 9, "table": 10, "shared_gate": 11}
 
 
 def _rng(cfg: Config, tag: str, sub: int = 0) -> np.random.Generator:
@@ -212,6 +212,12 @@ def routing(cfg: Config) -> tuple[np.ndarray, np.ndarray]:
     rmap[rows[keep], order[keep]] = 1
     probs[rows[keep], order[keep]] = top_p[keep].astype(np.float32)  # dropped: prob 0, no renorm
     return probs, rmap
+
+
+def shared_gate_weight(cfg: Config) -> np.ndarray:
+    """The shared expert's output gate weight g ~ N(0, 0.02^2), BF16 bits [H] (x . g then
+    spreads over about N(0, 0.0004 H): sigmoid scores across (0, 1))."""
+    return to_bf16_bits(_normal_f32(_rng(cfg, "shared_gate"), (cfg.hidden,), 0.02))
 
 
 def routing_table(cfg: Config) -> tuple[np.ndarray, np.ndarray]:

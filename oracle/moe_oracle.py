@@ -50,7 +50,7 @@ __all__ = [
     "mxfp8_decode_colwise", "compact_routing", "dispatch_index", "silu", "dsilu",
     "swiglu_ffn", "Weights", "moe_forward", "moe_forward_f64", "moe_backward",
     "moe_backward_f64", "RouteOverflow", "RouteInvalid", "check_table", "moe_forward_table",
-    "moe_backward_table",
+    "moe_backward_table", "shared_gate_score",
 ]
 
 
@@ -240,12 +240,25 @@ def swiglu_ffn(X, Wg, Wu, Wd):
     return a, b, h, y
 
 
+def shared_gate_score(x, g):
+    """The shared expert's output gate, one scalar per token: sigmoid(x_t . g).
+
+    Reading of the shared-output gate (named on the pages as MCore's optional
+    shared-expert output gate, PR #6572 Supported configurations, and as the runtime's
+    shared_output_gate_weight argument, Megatron Core API docs, mok.runtime,
+    _MoKFunction.forward; its formula is not given there): a weight vector g [H] whose
+    sigmoid score per token scales the shared expert's output.
+    """
+    return 1.0 / (1.0 + np.exp(-(np.asarray(x, dtype=np.float64) @ g)))
+
+
 class Weights:
     """Float64 views of the six weights, in the runtime's argument order
     (Megatron Core API docs, mok.runtime, _MoKWeightArguments: shared gate,
     shared up, shared down, routed gate, routed up, routed down).
 
     shared      : (Wg [I,H], Wu [I,H], Wd [H,I]), or None in routed-only mode
+    shared_gate : the shared expert's output gate weight g [H], or None (no gate)
     routed(e)   : (Wg, Wu, Wd) as used by the forward
     routed_t(e) : (Wg, Wu, Wd) as used by dgrad (columnwise decode for MXFP8)
 
@@ -253,8 +266,9 @@ class Weights:
     decoded on demand, one at a time.
     """
 
-    def __init__(self, shared, routed_fn, routed_dgrad_fn=None):
+    def __init__(self, shared, routed_fn, routed_dgrad_fn=None, shared_gate=None):
         self.shared = shared
+        self.shared_gate = None if shared_gate is None else np.asarray(shared_gate, dtype=np.float64)
         self._routed = routed_fn
         self._routed_t = routed_dgrad_fn or routed_fn
 
@@ -265,13 +279,14 @@ class Weights:
         return self._routed_t(e)
 
     @staticmethod
-    def from_bits(inter: int, shared_fc1, shared_fc2, routed_getter, routed_dtype: str):
+    def from_bits(inter: int, shared_fc1, shared_fc2, routed_getter, routed_dtype: str, shared_gate=None):
         """shared_fc1 u16 [2I, H], shared_fc2 u16 [H, I]; routed_getter(e) -> dict of
         bits (see moe_inputs.routed_expert).  Gate = FC1 rows [0, I), up = rows [I, 2I)
         (Megatron Core API docs, mok.runtime, _gate_up_weight_arguments: gate and up
         are row views of the combined FC1)."""
         I = inter
         shared = None
+        gate = None if shared_gate is None else bf16_decode(np.asarray(shared_gate).reshape(-1))
         if shared_fc1 is not None:
             s1 = bf16_decode(shared_fc1)
             s2 = bf16_decode(shared_fc2)
@@ -282,7 +297,7 @@ class Weights:
                 d = routed_getter(e)
                 w1 = bf16_decode(d["fc1"])
                 return w1[:I], w1[I:2 * I], bf16_decode(d["fc2"])
-            return Weights(shared, fwd)
+            return Weights(shared, fwd, shared_gate=gate)
 
         def fwd(e):
             d = routed_getter(e)
@@ -293,7 +308,7 @@ class Weights:
             d = routed_getter(e)
             w1 = mxfp8_decode_colwise(d["fc1_c"], d["fc1_cs"])
             return w1[:I], w1[I:2 * I], mxfp8_decode_colwise(d["fc2_c"], d["fc2_cs"])
-        return Weights(shared, fwd, bwd)
+        return Weights(shared, fwd, bwd, shared_gate=gate)
 
 
 # ----------------------------------------------------------------------------------
@@ -350,6 +365,8 @@ def _forward_table_f64(x, top, rw, E, weights: Weights, tokens=None):
     pos = {int(t): i for i, t in enumerate(tokens)}
     if weights.shared is not None:
         _, _, _, out = swiglu_ffn(x, *weights.shared)
+        if weights.shared_gate is not None:
+            out = shared_gate_score(x, weights.shared_gate)[:, None] * out
     else:
         out = np.zeros_like(x)
     for e, lst in enumerate(_routes_by_expert(top, rw, tokens, E)):
@@ -379,7 +396,8 @@ def moe_backward_f64(dy_all, x_all, probs, routing_map, topk, weights: Weights,
       dprobs  float64 [len(tokens), E]        zero where routing_map is false
       dW      {e: (dWg, dWu, dWd)} for e in `experts` (all when None), computed from
               every token routed to e;  "shared": (dWg, dWu, dWd) when shared_grads
-              and the layer has a shared expert
+              and the layer has a shared expert; "shared_out_gate": dg [H] when it
+              also has the output gate
 
     Per route (t, k) to expert e with weight w, g = dy[t]:
       a = Wg x, b = Wu x, h = silu(a) b, y = Wd h
@@ -438,8 +456,15 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
 
     if weights.shared is not None:
         Wg, Wu, Wd = weights.shared
-        a, b, h, _ = swiglu_ffn(x, Wg, Wu, Wd)
-        gh = g @ Wd
+        a, b, h, ys = swiglu_ffn(x, Wg, Wu, Wd)
+        gs = g
+        if weights.shared_gate is not None:
+            # out_t = s_t u_t: the shared expert sees s_t dy_t; s_t itself gets dy_t . u_t
+            sc = shared_gate_score(x, weights.shared_gate)
+            dz = sc * (1.0 - sc) * np.sum(g * ys, axis=1)
+            dx += dz[:, None] * weights.shared_gate[None, :]
+            gs = sc[:, None] * g
+        gh = gs @ Wd
         da = gh * b * dsilu(a)
         db = gh * silu(a)
         dx += da @ Wg + db @ Wu
@@ -485,7 +510,12 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
         X = x_all
         G = dy_all
         Wg, Wu, Wd = weights.shared
-        a, b, h, _ = swiglu_ffn(X, Wg, Wu, Wd)
+        a, b, h, ys = swiglu_ffn(X, Wg, Wu, Wd)
+        if weights.shared_gate is not None:
+            sc = shared_gate_score(X, weights.shared_gate)
+            dz = sc * (1.0 - sc) * np.sum(G * ys, axis=1)
+            dW["shared_out_gate"] = dz @ X          # sum over all tokens of dz_t x_t
+            G = sc[:, None] * G
         gh = G @ Wd
         da = gh * b * dsilu(a)
         db = gh * silu(a)

@@ -346,6 +346,45 @@ def test_check_table_rejects_invalid_entries():
             O.check_table(np.array(bad, np.int32), 3)
 
 
+@pytest.mark.parametrize("shape", [(16, 32, 4, 2, 16), (24, 64, 5, 3, 32)])
+def test_shared_output_gate_matches_dense_autograd(shape):
+    """Shared output gate sigmoid(x . g) on the shared expert's output, against the dense
+    autograd form (including the gradient of g)."""
+    cfg, probs, rmap, x, dy, W, d = _small_problem(*shape, seed=23, short=0.2)
+    gbits = gen.shared_gate_weight(cfg)
+    gv = O.bf16_decode(gbits)
+    Wg = O.Weights(W.shared, W.routed, shared_gate=gv)
+    gt = torch.from_numpy(gv)
+    out = O.moe_forward(x, probs, rmap, cfg.topk, Wg)
+    assert _rel(out, dense_forward(d["x"], d["probs"], d["rmap"], d["shared"], d["routed"], gt).numpy()) < 1e-12
+    g = O.moe_backward(dy, x, probs, rmap, cfg.topk, Wg)
+    ref = dense_grads(d["x"], d["probs"], d["rmap"], d["shared"], d["routed"], d["dy"], gt)
+    assert _rel(g["dx"], ref["dx"].numpy()) < 1e-12
+    assert _rel(g["dprobs"], ref["dprobs"].numpy()) < 1e-12
+    assert _rel(g["dW"]["shared_out_gate"], ref["dgate"].numpy()) < 1e-12
+    dg, du, dd = g["dW"]["shared"]
+    assert _rel(np.concatenate([dg, du]), ref["dshared1"].numpy()) < 1e-12
+    assert _rel(dd, ref["dshared2"].numpy()) < 1e-12
+    for e in range(cfg.experts):
+        assert _rel(g["dW"][e][2], ref["drouted2"][e].numpy()) < 1e-12
+
+
+def test_shared_output_gate_zero_weight_halves_the_shared_expert():
+    """g = 0: every score is exactly 1/2, so out = routed + shared / 2, and the gradient of
+    g is sum_t (1/4)(dy_t . shared_t) x_t."""
+    cfg, probs, rmap, x, dy, W, d = _small_problem(12, 32, 4, 2, 16, seed=24)
+    H = cfg.hidden
+    Wz = O.Weights(W.shared, W.routed, shared_gate=np.zeros(H))
+    xs = O.bf16_decode(x)
+    shared = _textbook_swiglu(xs, np.concatenate(W.shared[:2]), W.shared[2])
+    routed = O.moe_forward(x, probs, rmap, cfg.topk, O.Weights(None, W.routed))
+    assert _rel(O.moe_forward(x, probs, rmap, cfg.topk, Wz), routed + 0.5 * shared) < 1e-13
+    g = O.moe_backward(dy, x, probs, rmap, cfg.topk, Wz)
+    dys = O.bf16_decode(dy)
+    want = (0.25 * np.sum(dys * shared, axis=1)) @ xs
+    assert _rel(g["dW"]["shared_out_gate"], want) < 1e-12
+
+
 def test_sampled_rows_and_experts_equal_full_run():
     cfg, probs, rmap, x, dy, W, d = _small_problem(30, 32, 5, 2, 16, seed=13, short=0.2)
     full = O.moe_backward(dy, x, probs, rmap, cfg.topk, W)
