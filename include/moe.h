@@ -81,6 +81,16 @@ typedef enum { MOE_BF16 = 1, MOE_FP32 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
  * grad_probs as [T][K].  Clear: the dense routing map and probabilities through
  * moe_forward. */
 #define MOE_FLAG_TOPK_ROUTING 4u
+/* Set (with MOE_FLAG_HAS_SHARED): the shared expert's output gate, MCore's optional
+ * shared-expert output gate (PR #6572, Supported configurations) and the runtime's
+ * shared_output_gate_weight argument (Megatron Core API docs, mok.runtime,
+ * _MoKFunction.forward).  The pages give no formula; the reading implemented: a BF16
+ * weight g [1][H] (moe_weights.shared_out_gate) and one score per token,
+ * s_t = sigmoid(x_t . g), multiplying the shared expert's output:
+ *     out[t] = s_t shared(x_t) + sum_k w_tk expert_{e_tk}(x_t)
+ * The backward adds sum_t s_t (1 - s_t) (grad_out_t . shared(x_t)) x_t to
+ * moe_main_grads.shared_out_gate. */
+#define MOE_FLAG_SHARED_GATE 8u
 
 /* Problem sizes and options. */
 typedef struct {
@@ -91,7 +101,7 @@ typedef struct {
   int32_t topk;          /* K in [1, min(8, E)]                                           */
   int32_t routed_dtype;  /* MOE_BF16 or MOE_MXFP8_E4M3 (PR #6572, Supported configurations) */
   uint32_t flags;        /* MOE_FLAG_HAS_SHARED (else routed-only) | MOE_FLAG_RECOMPUTE
-                            | MOE_FLAG_TOPK_ROUTING                                        */
+                            | MOE_FLAG_TOPK_ROUTING | MOE_FLAG_SHARED_GATE                 */
   float swiglu_limit;    /* must be 0 (no clamp)                                          */
 } moe_problem;
 
@@ -136,6 +146,8 @@ typedef struct {
  * configurations: shared expert parameters must remain BF16). */
 typedef struct {
   moe_weight shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
+  moe_weight shared_out_gate;   /* [1][H] BF16, `data.base` only; used with
+                                   MOE_FLAG_SHARED_GATE, ignored otherwise */
 } moe_weights;
 
 /* A main_grad buffer [rows][cols] per expert, same addressing as moe_mat, in FP32 or
@@ -163,6 +175,8 @@ typedef struct {
  * accumulation is BF16. */
 typedef struct {
   moe_grad shared_gate, shared_up, shared_down, routed_gate, routed_up, routed_down;
+  moe_grad shared_out_gate;     /* [1][H], `base` only, same dtype as the others; used
+                                   with MOE_FLAG_SHARED_GATE, ignored otherwise */
 } moe_main_grads;
 /* In routed-only mode only the three routed buffers are used, and they alone must share
  * one dtype. */

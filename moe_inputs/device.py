@@ -39,7 +39,7 @@ def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
 class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
                  routing=None, main_grad_dtype: str = "fp32", shared: bool = True,
-                 recompute: bool = False, routing_table=None):
+                 recompute: bool = False, routing_table=None, shared_gate: bool = False):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
         configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16".
         shared=False: routed-only mode; the shared weight and main_grad descriptors are
@@ -47,7 +47,8 @@ class DeviceProblem:
         recompute mode (saved holds the routing state only; the backward regenerates the
         activations).  routing_table: optional (top_experts [T,K] int32, router_weights
         [T,K] float32), the router's fixed-width table given to moe_forward_topk instead of
-        the dense map; grad_probs is then [T,K]."""
+        the dense map; grad_probs is then [T,K].  shared_gate: the shared expert's output gate
+        (a seeded [H] weight and its main_grad)."""
         self.cfg = cfg
         self.device = device
         T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
@@ -78,8 +79,9 @@ class DeviceProblem:
         mx = cfg.routed == "mxfp8"
         dt = mk.MOE_MXFP8_E4M3 if mx else mk.MOE_BF16
         self.shared = shared
+        self.gated = shared_gate
         flags = ((mk.MOE_FLAG_HAS_SHARED if shared else 0) | (mk.MOE_FLAG_RECOMPUTE if recompute else 0)
-                 | (mk.MOE_FLAG_TOPK_ROUTING if self.table else 0))
+                 | (mk.MOE_FLAG_TOPK_ROUTING if self.table else 0) | (mk.MOE_FLAG_SHARED_GATE if shared_gate else 0))
         self.p = mk.problem(T, H, I, E, K, dt, flags=flags)
 
         def routed_mat(key, rows, cols, conv, elem_cols):
@@ -118,6 +120,10 @@ class DeviceProblem:
         else:
             sg, su, sd = mk.moe_weight(), mk.moe_weight(), mk.moe_weight()
         self.weights = mk.moe_weights(sg, su, sd, rg, ru, rd)
+        self.np_gate = gen.shared_gate_weight(cfg) if shared_gate else None
+        if shared_gate:
+            self.gate = _bf16(self.np_gate, device)
+            self.weights.shared_out_gate = mk.weight(mk.MOE_BF16, 1, H, mk.mat(base=self.gate, ld=H))
 
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=device)
         self.layer = mk.Layer(self.p, device=device)
@@ -128,6 +134,7 @@ class DeviceProblem:
             mgd = mk.MOE_BF16 if main_grad_dtype == "bf16" else mk.MOE_FP32
             self.mg_s1 = torch.empty(2 * I, H, dtype=mgt, device=device)
             self.mg_s2 = torch.empty(H, I, dtype=mgt, device=device)
+            self.mg_gate = torch.empty(H, dtype=mgt, device=device)
             if cfg.layout == "single":
                 self.mg_r1 = torch.empty(E, 2 * I, H, dtype=mgt, device=device)
                 self.mg_r2 = torch.empty(E, H, I, dtype=mgt, device=device)
@@ -152,11 +159,14 @@ class DeviceProblem:
                 *sh,
                 mk.grad(ld=H, row_offset=0, dtype=mgd, **g1), mk.grad(ld=H, row_offset=I, dtype=mgd, **g1),
                 mk.grad(ld=I, dtype=mgd, **g2))
+            if shared_gate:
+                self.main_grads.shared_out_gate = mk.grad(base=self.mg_gate, ld=H, dtype=mgd)
 
     # ------------------------------------------------------------------
     def reset_main_grads(self):
         """Every main_grad buffer starts from the exact pattern (expert e's phase = e)."""
         fill_main_grad_pattern(self.mg_s1, 0)
+        fill_main_grad_pattern(self.mg_gate, 0)
         fill_main_grad_pattern(self.mg_s2, 0)
         for e, (a, b) in enumerate(zip(self.mg_r1_list, self.mg_r2_list)):
             fill_main_grad_pattern(a, e)

@@ -23,6 +23,7 @@ MOE_BF16, MOE_FP32, MOE_MXFP8_E4M3 = 1, 2, 3
 MOE_FLAG_HAS_SHARED = 1
 MOE_FLAG_RECOMPUTE = 2
 MOE_FLAG_TOPK_ROUTING = 4
+MOE_FLAG_SHARED_GATE = 8
 
 EXPORTED = ("moe_saved_bytes", "moe_workspace_bytes", "moe_saved_view", "moe_forward",
             "moe_forward_topk", "moe_backward", "moe_status_str", "moe_kernel_timer_enable", "moe_kernel_timer_read")
@@ -47,7 +48,7 @@ class moe_weight(C.Structure):
 
 class moe_weights(C.Structure):
     _fields_ = [(n, moe_weight) for n in ("shared_gate", "shared_up", "shared_down",
-                                          "routed_gate", "routed_up", "routed_down")]
+                                          "routed_gate", "routed_up", "routed_down", "shared_out_gate")]
 
 
 class moe_grad(C.Structure):
@@ -57,7 +58,7 @@ class moe_grad(C.Structure):
 
 class moe_main_grads(C.Structure):
     _fields_ = [(n, moe_grad) for n in ("shared_gate", "shared_up", "shared_down",
-                                        "routed_gate", "routed_up", "routed_down")]
+                                        "routed_gate", "routed_up", "routed_down", "shared_out_gate")]
 
 
 class moe_saved_layout(C.Structure):

@@ -32,6 +32,7 @@ struct Dims {
   bool hs;           // the shared expert is fused in
   bool rc;           // recompute: saved holds the routing state only
   bool tk;           // routing given as the fixed-width [T][K] table
+  bool sg;           // the shared expert's output is gated
 };
 
 Dims dims_of(const moe_problem* p) {
@@ -44,6 +45,7 @@ Dims dims_of(const moe_problem* p) {
   d.mx = p->routed_dtype == MOE_MXFP8_E4M3;
   d.rc = (p->flags & MOE_FLAG_RECOMPUTE) != 0;
   d.tk = (p->flags & MOE_FLAG_TOPK_ROUTING) != 0;
+  d.sg = (p->flags & MOE_FLAG_SHARED_GATE) != 0;
   return d;
 }
 
@@ -68,7 +70,7 @@ ActLayout act_layout(const Dims& d, size_t o) {
 
 // Byte offsets inside `saved`.
 struct SavedLayout {
-  size_t top, rw, counts, offsets, slot_of, slot_token, status, slot_w, slot_t, tile_prefix, chunk_base,
+  size_t top, rw, counts, offsets, slot_of, slot_token, status, slot_w, slot_t, gate_s, tile_prefix, chunk_base,
       chunk_counts, chunk_status, total;
   ActLayout act;     // not in recompute mode
 };
@@ -86,6 +88,7 @@ SavedLayout saved_layout(const Dims& d) {
   L.status = take(4);
   L.slot_w = take(4 * d.SM);
   L.slot_t = take(4 * d.SM);
+  L.gate_s = take(d.sg ? 4 * d.T : 0);
   L.tile_prefix = take(4 * (d.E + 2));
   L.chunk_base = take(4 * d.nchunks * d.E);
   L.chunk_counts = take(4 * d.nchunks * d.E);
@@ -106,6 +109,7 @@ SavedLayout saved_layout(const Dims& d) {
 // first writer runs after the recomputed FC2 has consumed it.
 struct BwdLayout {
   size_t dyw, dfc1, dxp, dyq, dys, dfq, dfs, total;
+  size_t sdy, gdz, gpart;        // shared output gate: s dy [T][H] bf16, dz [T], partial sums
   ActLayout act;                 // recompute mode only
   size_t fxq, fxs, fhq, fhs;     // recompute mode, MXFP8 only
 };
@@ -130,6 +134,12 @@ BwdLayout bwd_layout(const Dims& d) {
     L.dfs = take(d.SM * 2 * d.I / 32);
   }
   L.fxq = L.dyq; L.fxs = L.dys; L.fhq = L.dfq; L.fhs = L.dfs;
+  L.sdy = L.gdz = L.gpart = 0;
+  if (d.sg) {
+    L.sdy = take(2 * d.T * d.H);
+    L.gdz = take(4 * d.T);
+    L.gpart = take(4 * (size_t)kGateChunks * d.H);
+  }
   L.total = o;
   return L;
 }
@@ -172,7 +182,9 @@ moe_status check_problem(const moe_problem* p) {
   if (p->topk < 1 || p->topk > kMaxTopk || p->topk > p->experts) return MOE_ERR_SHAPE;
   if (p->tokens * (int64_t)p->topk > (int64_t)1 << 30) return MOE_ERR_SHAPE;
   if (p->hidden > (1 << 20) || p->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
-  if (p->flags & ~(MOE_FLAG_HAS_SHARED | MOE_FLAG_RECOMPUTE | MOE_FLAG_TOPK_ROUTING)) return MOE_ERR_UNSUPPORTED;
+  if (p->flags & ~(MOE_FLAG_HAS_SHARED | MOE_FLAG_RECOMPUTE | MOE_FLAG_TOPK_ROUTING | MOE_FLAG_SHARED_GATE))
+    return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_SHARED_GATE) && !(p->flags & MOE_FLAG_HAS_SHARED)) return MOE_ERR_UNSUPPORTED;
   if (p->swiglu_limit != 0.0f) return MOE_ERR_UNSUPPORTED;
   if (p->routed_dtype != MOE_BF16 && p->routed_dtype != MOE_MXFP8_E4M3) return MOE_ERR_DTYPE;
   return MOE_OK;
@@ -229,6 +241,10 @@ moe_status check_weights(const moe_problem* p, const moe_weights* w, bool backwa
     if ((s = check_weight(w->shared_up, I, H, false, MOE_BF16)) != MOE_OK) return s;
     if ((s = check_weight(w->shared_down, H, I, false, MOE_BF16)) != MOE_OK) return s;
   }
+  if (p->flags & MOE_FLAG_SHARED_GATE) {   // [1][H] BF16, one grouped base
+    if ((s = check_weight(w->shared_out_gate, 1, H, false, MOE_BF16)) != MOE_OK) return s;
+    if (w->shared_out_gate.row_offset != 0) return MOE_ERR_LAYOUT;
+  }
   if ((s = check_weight(w->routed_gate, I, H, true, p->routed_dtype, backward)) != MOE_OK) return s;
   if ((s = check_weight(w->routed_up, I, H, true, p->routed_dtype, backward)) != MOE_OK) return s;
   if ((s = check_weight(w->routed_down, H, I, true, p->routed_dtype, backward)) != MOE_OK) return s;
@@ -265,6 +281,13 @@ moe_status check_grads(const moe_problem* p, const moe_main_grads* g) {
     if ((s = check_grad(g->shared_gate, H, false)) != MOE_OK) return s;
     if ((s = check_grad(g->shared_up, H, false)) != MOE_OK) return s;
     if ((s = check_grad(g->shared_down, I, false)) != MOE_OK) return s;
+  }
+  if (p->flags & MOE_FLAG_SHARED_GATE) {
+    const moe_grad& q = g->shared_out_gate;
+    if (q.dtype != 0 && q.dtype != MOE_FP32 && q.dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (grad_bf16(q) != grad_bf16(g->routed_gate)) return MOE_ERR_DTYPE;
+    if ((s = check_grad(q, H, false)) != MOE_OK) return s;
+    if (q.row_offset != 0) return MOE_ERR_LAYOUT;
   }
   if ((s = check_grad(g->routed_gate, H, true)) != MOE_OK) return s;
   if ((s = check_grad(g->routed_up, H, true)) != MOE_OK) return s;
@@ -585,7 +608,9 @@ moe_status forward_impl(bool table, const moe_problem* p, const void* hidden, co
   // F7 combine
   MOE_TRY(launch("combine", st, [&] {
     hipLaunchKernelGGL(k_combine, dim3(T), dim3(kRowThreads), 0, st, P.y, d.hs ? d.SM : -1, H, K,
-                       I32(L.slot_of), F32(L.rw), static_cast<uint16_t*>(out));
+                       I32(L.slot_of), F32(L.rw), static_cast<uint16_t*>(out), static_cast<const uint16_t*>(hidden),
+                       d.sg ? static_cast<const uint16_t*>(w->shared_out_gate.data.base) : (const uint16_t*)nullptr,
+                       d.sg ? F32(L.gate_s) : (float*)nullptr);
   }));
   return MOE_OK;
 }
@@ -647,16 +672,23 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
     MOE_TRY(experts_forward(d, P, x, w, st, true));
   }
 
+  // shared output gate: saved scores, the gated dy rows of the shared expert, dz
+  const float* gate_s = d.sg ? F32(L.gate_s) : nullptr;
+  float* gdz = d.sg ? reinterpret_cast<float*>(W + B.gdz) : nullptr;
+  uint16_t* sdy = d.sg ? WU16(B.sdy) : nullptr;
+  const uint16_t* gw = d.sg ? static_cast<const uint16_t*>(w->shared_out_gate.data.base) : nullptr;
+  const uint16_t* dy_shared = d.sg ? sdy : dy;   // the shared expert's upstream gradient
+
   // B1 weighted dy gather (+ Q) + B8 router-probability gradient (dense row, zeros off the map)
   MOE_TRY(launch("gather_dy_dprob", st, [&] {
     if (d.mx)
       hipLaunchKernelGGL(k_gather_dy_dprob<true>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(A.y), H, E, K,
                          I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, W + B.dyq, W + B.dys,
-                         d.tk ? 0 : 1);
+                         d.tk ? 0 : 1, d.SM, gate_s, gdz, sdy);
     else
       hipLaunchKernelGGL(k_gather_dy_dprob<false>, dim3(T), dim3(kRowThreads), 0, st, dy, U16(A.y), H, E, K,
                          I32(L.slot_of), I32(L.top), F32(L.rw), WU16(B.dyw), grad_probs, (uint8_t*)nullptr,
-                         (uint8_t*)nullptr, d.tk ? 0 : 1);
+                         (uint8_t*)nullptr, d.tk ? 0 : 1, d.SM, gate_s, gdz, sdy);
   }));
 
   gemm::TokArgs ta;
@@ -671,7 +703,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   gemm::DgradSwigluArgs a3;
   a3.t = ta;
   a3.a_r = WU16(B.dyw);
-  a3.a_s = dy;
+  a3.a_s = dy_shared;
   a3.wd = matref(w->routed_down, w->routed_down.data, 2);
   a3.sd = matref(w->shared_down, w->shared_down.data, 2);
   a3.ab = U16(A.ab);
@@ -727,7 +759,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   // B7 dx combine
   MOE_TRY(launch("dx_combine", st, [&] {
     hipLaunchKernelGGL(k_dx_combine, dim3(T), dim3(kRowThreads), 0, st, WU16(B.dxp), d.hs ? d.SM : -1, H, K,
-                       I32(L.slot_of), static_cast<uint16_t*>(grad_hidden));
+                       I32(L.slot_of), static_cast<uint16_t*>(grad_hidden), gw, (const float*)gdz);
   }));
 
   // B4 (+B6): FC2 weight gradient: main_grad_down[e] += dyw^T h
@@ -735,7 +767,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a5.counts = I32(L.counts);
   a5.offsets = I32(L.offsets);
   a5.T = T; a5.E = E; a5.has_shared = d.hs ? 1 : 0;
-  a5.a_r = WU16(B.dyw); a5.a_s = dy; a5.lda = H; a5.a_s_row0 = 0;
+  a5.a_r = WU16(B.dyw); a5.a_s = dy_shared; a5.lda = H; a5.a_s_row0 = 0;
   a5.b_r = U16(A.h); a5.b_s = U16(A.h); a5.ldb = I; a5.b_s_row0 = d.SM;
   a5.b_map = nullptr;
   a5.g_lo = gradref(mg->routed_down); a5.g_hi = a5.g_lo;
@@ -757,6 +789,17 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a6.parts = 2; a6.mpart = I;
   a6.N = H;
   MOE_TRY(launch("wgrad_fc1", st, [&] { launch_wgrad<1>(a6, d, grad_bf16(mg->routed_gate), st); }));
+
+  // shared output gate's weight: main_grad += sum_t dz[t] x[t]
+  if (d.sg) {
+    float* part = reinterpret_cast<float*>(W + B.gpart);
+    MOE_TRY(launch("gate_wgrad", st, [&] {
+      hipLaunchKernelGGL(k_gate_wgrad_partial, dim3((H + 511) / 512, kGateChunks), dim3(256), 0, st, x,
+                         (const float*)gdz, T, H, part);
+      hipLaunchKernelGGL(k_gate_wgrad_final, dim3((H + 255) / 256), dim3(256), 0, st, (const float*)part, H,
+                         static_cast<uint8_t*>(mg->shared_out_gate.base), grad_bf16(mg->routed_gate) ? 1 : 0);
+    }));
+  }
   return MOE_OK;
 }
 

@@ -69,12 +69,47 @@ __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
   }
 }
 
+// x[t] . g for the token's block (fixed order: pieces per thread, a wave butterfly, then
+// the waves in order); every thread gets the result.
+__device__ __forceinline__ float row_dot(const uint16_t* __restrict__ xr, const uint16_t* __restrict__ g, int H,
+                                        float* red /* LDS [kRowThreads / 64] */) {
+  const int nc = H / 8;
+  float v = 0.0f;
+  for (int c = threadIdx.x; c < nc; c += kRowThreads) {
+    float a[8], b[8];
+    unpack_bf16x8(reinterpret_cast<const uint4*>(xr)[c], a);
+    unpack_bf16x8(reinterpret_cast<const uint4*>(g)[c], b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += a[i] * b[i];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float z = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kRowThreads / 64; ++q) z += red[q];
+  return z;
+}
+
+// Shared output gate score sigmoid(z) (one scalar per token).
+__device__ __forceinline__ float gate_sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+
 // out[t] = y[shared_row0 + t] + sum_k w_tk * y[slot_of[t,k]], in float, fixed k order,
 // one rounding to bf16.  shared_row0 < 0: no shared row (the sum starts from zero).
+// With the shared output gate (gw non-null) the shared row is scaled by
+// sigmoid(x[t] . gw), which is also stored to gate_s[t] for the backward.
 __global__ __launch_bounds__(kRowThreads) void k_combine(
     const uint16_t* __restrict__ y, int64_t shared_row0, int H, int K,
-    const int32_t* __restrict__ slot_of, const float* __restrict__ rw, uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ slot_of, const float* __restrict__ rw, uint16_t* __restrict__ out,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gw, float* __restrict__ gate_s) {
+  __shared__ float red[kRowThreads / 64];
   const int t = blockIdx.x;
+  float gscale = 1.0f;
+  if (gw) {
+    gscale = gate_sigmoid(row_dot(x + (int64_t)t * H, gw, H, red));
+    if (threadIdx.x == 0) gate_s[t] = gscale;
+  }
   int s[kMaxTopk];
   load_slots(slot_of, t, K, s);
   float w[kMaxTopk];
@@ -100,6 +135,8 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
       float a[8];
       unpack_bf16x8(v[u], a);
 #pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] *= gscale;
+#pragma unroll
       for (int k = 0; k < kMaxTopk; ++k) {
         if (s[k] < 0) continue;
         float b[8];
@@ -116,18 +153,22 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
 // routed expert's upstream gradient), and the router-probability gradient
 // dprobs[t, e_tk] = dy[t] . y[slot] (y is the unweighted expert output), written
 // into the dense [T][E] row with zeros off the map, or (dense = 0, routing given as the
-// fixed-width table) into the [T][K] row of the table, 0 at -1 entries.  The dot products are
-// reduced per thread in a fixed order, then across each wave by a fixed butterfly,
-// then across the waves in order.  With Q, w_tk * dy[t] is also quantised to MXFP8
-// along H (the A operand of the scaled-FP8 data-gradient GEMM).  One block per token.
+// fixed-width table) into the [T][K] row of the table, 0 at -1 entries.  With the shared
+// output gate (gate_s non-null): dys[t] = s_t dy[t] (the shared expert's upstream
+// gradient) and dz[t] = s_t (1 - s_t) (dy[t] . y[shared_row0 + t]) (the gate logit's).
+// The dot products are reduced per thread in a fixed order, then across each wave by a
+// fixed butterfly, then across the waves in order.  With Q, w_tk * dy[t] is also
+// quantised to MXFP8 along H into dyq / dysc (the A operand of the scaled-FP8
+// data-gradient GEMM).  One block per token.
 template <bool Q>
 __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y, int H, int E, int K,
     const int32_t* __restrict__ slot_of, const int32_t* __restrict__ top,
     const float* __restrict__ rw, uint16_t* __restrict__ dyw, float* __restrict__ dprobs,
-    uint8_t* __restrict__ dyq, uint8_t* __restrict__ dys, int dense) {
-  __shared__ float red[kRowThreads / 64][kMaxTopk];
-  __shared__ float dp[kMaxTopk];
+    uint8_t* __restrict__ dyq, uint8_t* __restrict__ dysc, int dense, int64_t shared_row0,
+    const float* __restrict__ gate_s, float* __restrict__ dz, uint16_t* __restrict__ dys) {
+  __shared__ float red[kRowThreads / 64][kMaxTopk + 1];
+  __shared__ float dp[kMaxTopk + 1];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int s[kMaxTopk];
@@ -138,6 +179,10 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     w[k] = (s[k] >= 0) ? rw[(int64_t)t * K + k] : 0.0f;
     part[k] = 0.0f;
   }
+  const bool gated = gate_s != nullptr;
+  const float gs = gated ? gate_s[t] : 0.0f;
+  const uint4* ysh = gated ? reinterpret_cast<const uint4*>(y + (shared_row0 + t) * (int64_t)H) : nullptr;
+  float part_s = 0.0f;
   const uint4* src = reinterpret_cast<const uint4*>(dy + (int64_t)t * H);
   const int nc = H / 8;
   for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
@@ -157,6 +202,18 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
       if (c >= nc) break;
       float g[8];
       unpack_bf16x8(g4[u], g);
+      if (gated) {
+        float ys[8], sg[8];
+        unpack_bf16x8(ysh[c], ys);
+        float d = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          d += g[i] * ys[i];
+          sg[i] = gs * g[i];
+        }
+        part_s += d;
+        reinterpret_cast<uint4*>(dys + (int64_t)t * H)[c] = pack_bf8(sg);
+      }
 #pragma unroll
       for (int k = 0; k < kMaxTopk; ++k) {
         if (s[k] < 0) continue;
@@ -174,26 +231,27 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
           uint2 q;
           const uint32_t sc = mx_quantize8(wg, quad_max(absmax8(wg)), q);
           reinterpret_cast<uint2*>(dyq + (int64_t)s[k] * H)[c] = q;
-          if ((c & 3) == 0) dys[(int64_t)s[k] * (H / 32) + (c >> 2)] = (uint8_t)sc;
+          if ((c & 3) == 0) dysc[(int64_t)s[k] * (H / 32) + (c >> 2)] = (uint8_t)sc;
         }
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < kMaxTopk; ++k) {
-    float v = part[k];
+  for (int k = 0; k <= kMaxTopk; ++k) {
+    float v = k < kMaxTopk ? part[k] : part_s;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     if (lane == 0) red[wv][k] = v;
   }
   __syncthreads();
-  if (threadIdx.x < kMaxTopk) {
+  if (threadIdx.x <= kMaxTopk) {
     float v = 0.0f;
 #pragma unroll
     for (int q = 0; q < kRowThreads / 64; ++q) v += red[q][threadIdx.x];
     dp[threadIdx.x] = v;
   }
   __syncthreads();
+  if (gated && threadIdx.x == 0) dz[t] = gs * (1.0f - gs) * dp[kMaxTopk];
   if (!dense) {   // a route with no slot accumulated nothing: dp[k] = 0 there
     if (threadIdx.x < K) dprobs[(int64_t)t * K + threadIdx.x] = dp[threadIdx.x];
     return;
@@ -208,15 +266,18 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
 }
 
 // dx[t] = dxp[shared_row0 + t] + sum_k dxp[slot_of[t,k]] (float, fixed order, one rounding);
-// shared_row0 < 0: no shared row.
+// shared_row0 < 0: no shared row.  With the shared output gate, + dz[t] gw (the gate
+// logit's contribution).
 __global__ __launch_bounds__(kRowThreads) void k_dx_combine(
     const uint16_t* __restrict__ dxp, int64_t shared_row0, int H, int K,
-    const int32_t* __restrict__ slot_of, uint16_t* __restrict__ dx) {
+    const int32_t* __restrict__ slot_of, uint16_t* __restrict__ dx,
+    const uint16_t* __restrict__ gw, const float* __restrict__ dz) {
   const int t = blockIdx.x;
   int s[kMaxTopk];
   load_slots(slot_of, t, K, s);
   const uint4* src =
       shared_row0 >= 0 ? reinterpret_cast<const uint4*>(dxp + (shared_row0 + t) * (int64_t)H) : nullptr;
+  const float dzt = gw ? dz[t] : 0.0f;
   const int nc = H / 8;
   for (int c0 = threadIdx.x; c0 < nc; c0 += 2 * kRowThreads) {
     uint4 v[2], r[2][kMaxTopk];
@@ -243,8 +304,85 @@ __global__ __launch_bounds__(kRowThreads) void k_dx_combine(
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[i] += b[i];
       }
+      if (gw) {
+        float gv[8];
+        unpack_bf16x8(reinterpret_cast<const uint4*>(gw)[c], gv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] += dzt * gv[i];
+      }
       reinterpret_cast<uint4*>(dx + (int64_t)t * H)[c] = pack_bf8(a);
     }
+  }
+}
+
+// Gradient of the shared output gate's weight: main_grad_g += sum_t dz[t] x[t], in two
+// fixed-order passes.  Pass 1: block (column group b of 512, token chunk q) sums its
+// columns over the chunk's tokens: lane l owns columns 512 b + 8 l .. + 7 (one 16-byte
+// piece per row), wave v takes tokens q*TC + v, + 4, ... four at a time (their loads in
+// flight together, added in token order), and the 4 waves are added in order.
+constexpr int kGateChunks = 64;
+__global__ __launch_bounds__(256) void k_gate_wgrad_partial(
+    const uint16_t* __restrict__ x, const float* __restrict__ dz, int T, int H, float* __restrict__ part) {
+  __shared__ float red[4][64][9];   // [wave][lane][8 columns] (+1 pad)
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c8 = blockIdx.x * 64 + lane;              // 16-byte piece of the row
+  const bool in = 8 * c8 < H;
+  const int tc = (T + kGateChunks - 1) / kGateChunks;
+  const int t0 = blockIdx.y * tc, t1 = min(T, t0 + tc);
+  float acc[8] = {};
+  if (in) {
+    int t = t0 + wv;
+    for (; t + 12 < t1; t += 16) {
+      uint4 v[4];
+      float z[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = reinterpret_cast<const uint4*>(x + (int64_t)(t + 4 * u) * H)[c8];
+        z[u] = dz[t + 4 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float a[8];
+        unpack_bf16x8(v[u], a);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += z[u] * a[i];
+      }
+    }
+    for (; t < t1; t += 4) {
+      float a[8];
+      unpack_bf16x8(reinterpret_cast<const uint4*>(x + (int64_t)t * H)[c8], a);
+      const float z = dz[t];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += z * a[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[wv][lane][i] = acc[i];
+  __syncthreads();
+  if (wv == 0 && in) {
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = ((red[0][lane][i] + red[1][lane][i]) + red[2][lane][i]) + red[3][lane][i];
+    float* dst = part + (int64_t)blockIdx.y * H + 8 * c8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = o[i];
+  }
+}
+
+// Pass 2: chunks added in order, then the main_grad update (FP32, or BF16 with the
+// contribution rounded to BF16 first, as for the other weights).
+__global__ __launch_bounds__(256) void k_gate_wgrad_final(const float* __restrict__ part, int H,
+                                                           uint8_t* __restrict__ mg, int bf16_mg) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= H) return;
+  float v = 0.0f;
+  for (int q = 0; q < kGateChunks; ++q) v += part[(int64_t)q * H + col];
+  if (bf16_mg) {
+    uint16_t* m = reinterpret_cast<uint16_t*>(mg);
+    m[col] = f2bf(bf2f(m[col]) + bf2f(f2bf(v)));
+  } else {
+    float* m = reinterpret_cast<float*>(mg);
+    m[col] = m[col] + v;
   }
 }
 

@@ -24,7 +24,7 @@ def oracle_weights(dp) -> "O.Weights":
     cfg = dp.cfg
     shared = getattr(dp, "shared", True)
     return O.Weights.from_bits(cfg.inter, dp.np_s1 if shared else None, dp.np_s2 if shared else None,
-                               lambda e: dp.np_routed[e], cfg.routed)
+                               lambda e: dp.np_routed[e], cfg.routed, shared_gate=getattr(dp, "np_gate", None))
 
 
 def check_routing_state(dp):

@@ -235,3 +235,31 @@ def test_topk_routing_entry_point_validation():
     assert mk.moe_forward_topk(p, a, a, a, w, a, a, 0, 0, 0) == mk.MOE_ERR_WORKSPACE   # accepted so far
     assert mk.moe_saved_bytes(p) == mk.moe_saved_bytes(_ok_problem())
     assert "repeated" in mk.moe_status_str(mk.MOE_ERR_ROUTE_INVALID)
+
+
+def test_shared_gate_validation():
+    """MOE_FLAG_SHARED_GATE needs the shared expert, a [1][H] BF16 gate weight and a
+    seventh main_grad of the same dtype as the others."""
+    a = 1 << 41
+    p = _ok_problem()
+    H, I = p.hidden, p.intermediate
+    p.flags = mk.MOE_FLAG_SHARED_GATE                       # without the shared expert
+    assert mk.moe_forward(p, a, a, a, _fake_weights(_ok_problem()), a, a, a, 1 << 20, 0) == mk.MOE_ERR_UNSUPPORTED
+    p.flags = mk.MOE_FLAG_HAS_SHARED | mk.MOE_FLAG_SHARED_GATE
+    w = _fake_weights(p)
+    assert mk.moe_forward(p, a, a, a, w, a, a, a, 1 << 20, 0) == mk.MOE_ERR_DTYPE      # gate weight missing
+    w.shared_out_gate = mk.moe_weight(mk.MOE_BF16, 1, H, 0, mk.moe_mat(a, 0, 0, H))
+    assert mk.moe_forward(p, a, a, a, w, a, a, 0, 0, 0) == mk.MOE_ERR_WORKSPACE        # accepted
+    w.shared_out_gate.cols = H - 128
+    assert mk.moe_forward(p, a, a, a, w, a, a, a, 1 << 20, 0) == mk.MOE_ERR_SHAPE
+    w.shared_out_gate.cols = H
+    G = lambda ld, ro=0, dt=0: mk.moe_grad(a, 0, 0, ld, ro, dt)
+    g = mk.moe_main_grads(G(H), G(H, I), G(I), G(H), G(H, I), G(I))
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 1 << 30, 0) == mk.MOE_ERR_NULL    # gate grad missing
+    g.shared_out_gate = G(H, 0, mk.MOE_BF16)
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 1 << 30, 0) == mk.MOE_ERR_DTYPE
+    g.shared_out_gate = G(H)
+    assert mk.moe_backward(p, a, a, w, a, a, a, g, a, 16, 0) == mk.MOE_ERR_WORKSPACE     # accepted
+    q = _ok_problem()
+    assert mk.moe_workspace_bytes(p, 1) > mk.moe_workspace_bytes(q, 1)
+    assert mk.moe_saved_bytes(p) > mk.moe_saved_bytes(q)

@@ -59,6 +59,11 @@ def _check_backward(dp, W, tokens=None, experts=None, tol=BF16_TOL):
     else:   # routed-only: the shared main_grad buffers were not handed over and stay as they were
         assert "shared" not in g["dW"]
         assert np.all(s1 == 0) and np.all(s2 == 0)
+    gw = to_f64(dp.mg_gate) - dp.main_grad_start((cfg.hidden,), 0)
+    if getattr(dp, "gated", False):
+        errs["shared_out_gate"] = rel_err(gw, g["dW"]["shared_out_gate"])
+    else:
+        assert np.all(gw == 0), "the gate's main_grad must not be touched without the gate"
     worst = max(errs, key=lambda k: errs[k])
     print(f"[parity] dx {errs['dx']:.3e} dprobs {errs['dprobs']:.3e} worst {worst} {errs[worst]:.3e} "
           f"(tol {tol})", flush=True)
@@ -598,6 +603,52 @@ def test_bf16_main_grad_matches_oracle(gpu_lib, routed, layout, shape):
     print(f"[parity] bf16 main_grad = bf16(before + bf16(fp32 contribution)): exact fraction min "
           f"{min(match):.5f}", flush=True)
     assert min(match) >= 0.999
+
+
+# ----------------------------------------------------------------------------------
+# the shared expert's output gate
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("routed,layout,shape", [
+    ("bf16", "single", (777, 384, 13, 4, 256)),
+    ("mxfp8", "table", (300, 256, 6, 3, 128)),
+])
+def test_shared_output_gate_matches_oracle(gpu_lib, routed, layout, shape):
+    T, H, E, K, I = shape
+    cfg = gen.custom(T, H, E, K, I, routed=routed, layout=layout, short_frac=0.1 if routed == "bf16" else 0.05,
+                     short_max=max(1, K - 1), idx=(1000 if routed == "bf16" else 400) + T)
+    dp = _dp(cfg, shared_gate=True)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    assert W.shared_gate is not None
+    tol = BF16_TOL if routed == "bf16" else MXFP8_TOL
+    _check_forward(dp, W, tol=tol)
+    errs = _check_backward(dp, W, tol=tol)
+    print(f"[parity] gate weight gradient rel err {errs['shared_out_gate']:.3e}", flush=True)
+    # recompute mode: the same bits
+    rc = _dp(cfg, shared_gate=True, recompute=True)
+    rc.forward()
+    rc.layer.workspace.fill_(0xFF)
+    rc.backward()
+    torch.cuda.synchronize()
+    _assert_same_bits(dp, rc)
+    assert torch.equal(_bits(dp.mg_gate), _bits(rc.mg_gate))
+
+
+def test_shared_output_gate_full_size_sampled(gpu_lib):
+    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 with the shared output gate."""
+    cfg = gen.config(2)
+    dp = _dp(cfg, shared_gate=True)
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    W = oracle_weights(dp)
+    toks = sample_tokens(cfg.tokens, 32, seed=13)
+    _check_forward(dp, W, tokens=toks)
+    # the gate weight gradient sums over every token: compare it in full (experts sampled)
+    _check_backward(dp, W, tokens=toks, experts=[1, 90])
 
 
 # ----------------------------------------------------------------------------------
