@@ -50,7 +50,7 @@ __all__ = [
     "mxfp8_decode_colwise", "compact_routing", "dispatch_index", "silu", "dsilu",
     "swiglu_ffn", "Weights", "moe_forward", "moe_forward_f64", "moe_backward",
     "moe_backward_f64", "RouteOverflow", "RouteInvalid", "check_table", "moe_forward_table",
-    "moe_backward_table", "shared_gate_score",
+    "moe_backward_table", "shared_gate_score", "swiglu_clamped",
 ]
 
 
@@ -230,14 +230,33 @@ def dsilu(z):
     return s * (1.0 + z * (1.0 - s))
 
 
-def swiglu_ffn(X, Wg, Wu, Wd):
+def swiglu_ffn(X, Wg, Wu, Wd, limit=0.0):
     """Rows of X through one SwiGLU expert: a = X Wg^T, b = X Wu^T,
-    h = silu(a) * b, y = h Wd^T.  Returns (a, b, h, y)."""
+    h = silu(a) * b, y = h Wd^T (with a clamp limit L > 0: see swiglu_clamped).
+    Returns (a, b, h, y)."""
     a = X @ Wg.T
     b = X @ Wu.T
-    h = silu(a) * b
+    h, _, _ = swiglu_clamped(a, b, limit)
     y = h @ Wd.T
     return a, b, h, y
+
+
+def swiglu_clamped(a, b, limit=0.0):
+    """h = silu(a) b and its partial derivatives dh/da, dh/db.
+
+    With a clamp limit L > 0, the reading of the SwiGLU clamp (PR #8210 passes MCore's
+    activation_func_clamp_value to the backend as swiglu_limit; the pages give no
+    formula): the gate pre-activation is clamped from above and the linear one to
+    [-L, L] before the product, h = silu(min(a, L)) clamp(b, -L, L); a clamped input
+    passes no gradient (the bounds themselves pass it).  L = 0: no clamp."""
+    if limit and limit > 0:
+        ac = np.minimum(a, limit)
+        bc = np.clip(b, -limit, limit)
+        h = silu(ac) * bc
+        dha = bc * dsilu(a) * (a <= limit)
+        dhb = silu(ac) * ((b >= -limit) & (b <= limit))
+        return h, dha, dhb
+    return silu(a) * b, b * dsilu(a), silu(a)
 
 
 def shared_gate_score(x, g):
@@ -259,6 +278,7 @@ class Weights:
 
     shared      : (Wg [I,H], Wu [I,H], Wd [H,I]), or None in routed-only mode
     shared_gate : the shared expert's output gate weight g [H], or None (no gate)
+    swiglu_limit: the SwiGLU clamp limit L of every expert (0: none; swiglu_clamped)
     routed(e)   : (Wg, Wu, Wd) as used by the forward
     routed_t(e) : (Wg, Wu, Wd) as used by dgrad (columnwise decode for MXFP8)
 
@@ -266,8 +286,9 @@ class Weights:
     decoded on demand, one at a time.
     """
 
-    def __init__(self, shared, routed_fn, routed_dgrad_fn=None, shared_gate=None):
+    def __init__(self, shared, routed_fn, routed_dgrad_fn=None, shared_gate=None, swiglu_limit=0.0):
         self.shared = shared
+        self.swiglu_limit = float(swiglu_limit)
         self.shared_gate = None if shared_gate is None else np.asarray(shared_gate, dtype=np.float64)
         self._routed = routed_fn
         self._routed_t = routed_dgrad_fn or routed_fn
@@ -279,7 +300,8 @@ class Weights:
         return self._routed_t(e)
 
     @staticmethod
-    def from_bits(inter: int, shared_fc1, shared_fc2, routed_getter, routed_dtype: str, shared_gate=None):
+    def from_bits(inter: int, shared_fc1, shared_fc2, routed_getter, routed_dtype: str, shared_gate=None,
+                  swiglu_limit=0.0):
         """shared_fc1 u16 [2I, H], shared_fc2 u16 [H, I]; routed_getter(e) -> dict of
         bits (see moe_inputs.routed_expert).  Gate = FC1 rows [0, I), up = rows [I, 2I)
         (Megatron Core API docs, mok.runtime, _gate_up_weight_arguments: gate and up
@@ -297,7 +319,7 @@ class Weights:
                 d = routed_getter(e)
                 w1 = bf16_decode(d["fc1"])
                 return w1[:I], w1[I:2 * I], bf16_decode(d["fc2"])
-            return Weights(shared, fwd, shared_gate=gate)
+            return Weights(shared, fwd, shared_gate=gate, swiglu_limit=swiglu_limit)
 
         def fwd(e):
             d = routed_getter(e)
@@ -308,7 +330,7 @@ class Weights:
             d = routed_getter(e)
             w1 = mxfp8_decode_colwise(d["fc1_c"], d["fc1_cs"])
             return w1[:I], w1[I:2 * I], mxfp8_decode_colwise(d["fc2_c"], d["fc2_cs"])
-        return Weights(shared, fwd, bwd, shared_gate=gate)
+        return Weights(shared, fwd, bwd, shared_gate=gate, swiglu_limit=swiglu_limit)
 
 
 # ----------------------------------------------------------------------------------
@@ -364,7 +386,7 @@ def _forward_table_f64(x, top, rw, E, weights: Weights, tokens=None):
     x = np.asarray(x, dtype=np.float64)
     pos = {int(t): i for i, t in enumerate(tokens)}
     if weights.shared is not None:
-        _, _, _, out = swiglu_ffn(x, *weights.shared)
+        _, _, _, out = swiglu_ffn(x, *weights.shared, weights.swiglu_limit)
         if weights.shared_gate is not None:
             out = shared_gate_score(x, weights.shared_gate)[:, None] * out
     else:
@@ -374,7 +396,7 @@ def _forward_table_f64(x, top, rw, E, weights: Weights, tokens=None):
             continue
         rows = np.array([pos[t] for t, _, _ in lst])
         w = np.array([w for _, _, w in lst])
-        _, _, _, y = swiglu_ffn(x[rows], *weights.routed(e))
+        _, _, _, y = swiglu_ffn(x[rows], *weights.routed(e), weights.swiglu_limit)
         for j, r in enumerate(rows):     # fixed order; np.add.at would also do
             out[r] += w[j] * y[j]
     return out
@@ -456,7 +478,8 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
 
     if weights.shared is not None:
         Wg, Wu, Wd = weights.shared
-        a, b, h, ys = swiglu_ffn(x, Wg, Wu, Wd)
+        a, b, h, ys = swiglu_ffn(x, Wg, Wu, Wd, weights.swiglu_limit)
+        _, dha, dhb = swiglu_clamped(a, b, weights.swiglu_limit)
         gs = g
         if weights.shared_gate is not None:
             # out_t = s_t u_t: the shared expert sees s_t dy_t; s_t itself gets dy_t . u_t
@@ -465,8 +488,8 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
             dx += dz[:, None] * weights.shared_gate[None, :]
             gs = sc[:, None] * g
         gh = gs @ Wd
-        da = gh * b * dsilu(a)
-        db = gh * silu(a)
+        da = gh * dha
+        db = gh * dhb
         dx += da @ Wg + db @ Wu
 
     for e, lst in enumerate(_routes_by_expert(top, rw, tokens, E)):
@@ -475,12 +498,13 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
         rows = np.array([pos[t] for t, _, _ in lst])
         w = np.array([w for _, _, w in lst])
         Wg, Wu, Wd = weights.routed(e)
-        a, b, h, y = swiglu_ffn(x[rows], Wg, Wu, Wd)
+        a, b, h, y = swiglu_ffn(x[rows], Wg, Wu, Wd, weights.swiglu_limit)
+        _, dha, dhb = swiglu_clamped(a, b, weights.swiglu_limit)
         dprobs[rows, e] = np.sum(g[rows] * y, axis=1)
         Tg, Tu, Td = weights.routed_t(e)
         gh = w[:, None] * (g[rows] @ Td)
-        da = gh * b * dsilu(a)
-        db = gh * silu(a)
+        da = gh * dha
+        db = gh * dhb
         dxe = da @ Tg + db @ Tu
         for j, r in enumerate(rows):
             dx[r] += dxe[j]
@@ -500,24 +524,26 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
             w = np.array([w for _, _, w in lst])
             X = x_all[ts]
             G = dy_all[ts]
-            a, b, h, _ = swiglu_ffn(X, Wg, Wu, Wd)
+            a, b, h, _ = swiglu_ffn(X, Wg, Wu, Wd, weights.swiglu_limit)
+            _, dha, dhb = swiglu_clamped(a, b, weights.swiglu_limit)
             Tg, Tu, Td = weights.routed_t(e)
             gh = w[:, None] * (G @ Td)
-            da = gh * b * dsilu(a)
-            db = gh * silu(a)
+            da = gh * dha
+            db = gh * dhb
             dW[e] = (da.T @ X, db.T @ X, (w[:, None] * G).T @ h)
     if shared_grads and weights.shared is not None:
         X = x_all
         G = dy_all
         Wg, Wu, Wd = weights.shared
-        a, b, h, ys = swiglu_ffn(X, Wg, Wu, Wd)
+        a, b, h, ys = swiglu_ffn(X, Wg, Wu, Wd, weights.swiglu_limit)
+        _, dha, dhb = swiglu_clamped(a, b, weights.swiglu_limit)
         if weights.shared_gate is not None:
             sc = shared_gate_score(X, weights.shared_gate)
             dz = sc * (1.0 - sc) * np.sum(G * ys, axis=1)
             dW["shared_out_gate"] = dz @ X          # sum over all tokens of dz_t x_t
             G = sc[:, None] * G
         gh = G @ Wd
-        da = gh * b * dsilu(a)
-        db = gh * silu(a)
+        da = gh * dha
+        db = gh * dhb
         dW["shared"] = (da.T @ X, db.T @ X, G.T @ h)
     return {"dx": dx, "dprobs": dprobs, "dW": dW}

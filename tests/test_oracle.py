@@ -385,6 +385,48 @@ def test_shared_output_gate_zero_weight_halves_the_shared_expert():
     assert _rel(g["dW"]["shared_out_gate"], want) < 1e-12
 
 
+@pytest.mark.parametrize("limit", [0.05, 0.15])
+def test_swiglu_clamp_matches_dense_autograd(limit):
+    """SwiGLU clamp (gate pre-activation clamped above, linear one to [-L, L]) against the
+    dense autograd form with torch.clamp; the limits clamp a large share of both."""
+    cfg, probs, rmap, x, dy, W, d = _small_problem(24, 64, 5, 3, 32, seed=25, short=0.2)
+    Wc = O.Weights(W.shared, W.routed, swiglu_limit=limit)
+    xs = O.bf16_decode(x)
+    a = xs @ W.shared[0].T
+    b = xs @ W.shared[1].T
+    assert (a > limit).mean() > 0.05 and (np.abs(b) > limit).mean() > 0.05
+    out = O.moe_forward(x, probs, rmap, cfg.topk, Wc)
+    ref_out = dense_forward(d["x"], d["probs"], d["rmap"], d["shared"], d["routed"], limit=limit).numpy()
+    assert _rel(out, ref_out) < 1e-12
+    g = O.moe_backward(dy, x, probs, rmap, cfg.topk, Wc)
+    ref = dense_grads(d["x"], d["probs"], d["rmap"], d["shared"], d["routed"], d["dy"], limit=limit)
+    assert _rel(g["dx"], ref["dx"].numpy()) < 1e-12
+    assert _rel(g["dprobs"], ref["dprobs"].numpy()) < 1e-12
+    for e in range(cfg.experts):
+        dg, du, dd = g["dW"][e]
+        assert _rel(np.concatenate([dg, du]), ref["drouted1"][e].numpy()) < 1e-12
+        assert _rel(dd, ref["drouted2"][e].numpy()) < 1e-12
+    dg, du, dd = g["dW"]["shared"]
+    assert _rel(np.concatenate([dg, du]), ref["dshared1"].numpy()) < 1e-12
+
+
+def test_swiglu_clamp_limits_reduce_to_closed_forms():
+    """A limit above every pre-activation changes nothing; the clamped product itself is
+    silu(min(a, L)) clamp(b, -L, L) with derivatives that vanish where clamped."""
+    cfg, probs, rmap, x, dy, W, d = _small_problem(12, 32, 4, 2, 16, seed=26)
+    big = O.Weights(W.shared, W.routed, swiglu_limit=1e6)
+    assert np.array_equal(O.moe_forward(x, probs, rmap, cfg.topk, big), O.moe_forward(x, probs, rmap, cfg.topk, W))
+    a = np.array([-3.0, -0.5, 0.2, 0.5, 2.0])
+    b = np.array([-2.0, 0.4, -0.4, 1.5, 0.1])
+    h, dha, dhb = O.swiglu_clamped(a, b, 0.5)
+    sig = lambda v: 1.0 / (1.0 + np.exp(-v))
+    ac = np.array([-3.0, -0.5, 0.2, 0.5, 0.5])
+    bc = np.array([-0.5, 0.4, -0.4, 0.5, 0.1])
+    assert np.allclose(h, ac * sig(ac) * bc, rtol=0, atol=1e-15)
+    assert dha[4] == 0 and dha[3] != 0      # a = L still passes the gradient, a > L does not
+    assert dhb[0] == 0 and dhb[3] == 0 and dhb[1] != 0
+
+
 def test_sampled_rows_and_experts_equal_full_run():
     cfg, probs, rmap, x, dy, W, d = _small_problem(30, 32, 5, 2, 16, seed=13, short=0.2)
     full = O.moe_backward(dy, x, probs, rmap, cfg.topk, W)
