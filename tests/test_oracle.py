@@ -619,7 +619,7 @@ def test_mxfp8_weights_use_rowwise_forward_and_colwise_dgrad():
 # ----------------------------------------------------------------------------------
 # the pins catch planted mistakes (mutations applied to the oracle, on the CPU)
 # ----------------------------------------------------------------------------------
-def _swapped_gate_up(X, Wg, Wu, Wd):
+def _swapped_gate_up(X, Wg, Wu, Wd, limit=0.0):
     a = X @ Wu.T
     b = X @ Wg.T
     h = O.silu(a) * b
@@ -630,7 +630,7 @@ def _wrong_dsilu(z):
     return 1.0 / (1.0 + np.exp(-z))          # sigmoid instead of silu'
 
 
-def _transposed_down(X, Wg, Wu, Wd):
+def _transposed_down(X, Wg, Wu, Wd, limit=0.0):
     a = X @ Wg.T
     b = X @ Wu.T
     h = O.silu(a) * b
