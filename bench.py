@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--recompute", action="store_true",
                     help="MoE-layer recompute: saved holds the routing state only; the backward "
                          "regenerates the activations (same flops counted: the recomputation is overhead)")
+    ap.add_argument("--swiglu-limit", type=float, default=0.0, help="SwiGLU clamp limit (0: none)")
     ap.add_argument("--shared-gate", action="store_true",
                     help="the shared expert's output gate sigmoid(x . g) (its few flops are not counted)")
     ap.add_argument("--topk-input", action="store_true",
@@ -158,7 +159,7 @@ def main():
     dp = DeviceProblem(cfg, backward=True, main_grad_dtype=args.main_grad, shared=shared,
                        recompute=args.recompute,
                        routing_table=gen.routing_table(cfg) if args.topk_input else None,
-                       shared_gate=args.shared_gate)
+                       shared_gate=args.shared_gate, swiglu_limit=args.swiglu_limit)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s: {cfg.name}", file=sys.stderr, flush=True)
 
@@ -219,7 +220,7 @@ def main():
                    "routed_slots": slots, "routed_weights": cfg.routed, "layout": cfg.layout,
                    "routing": cfg.routing, "main_grad": args.main_grad, "shared_expert": shared,
                    "recompute": bool(args.recompute), "routing_input": "table" if args.topk_input else "map",
-                   "shared_gate": bool(args.shared_gate), "saved_bytes": int(dp.layer.saved.numel()),
+                   "shared_gate": bool(args.shared_gate), "swiglu_limit": args.swiglu_limit, "saved_bytes": int(dp.layer.saved.numel()),
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},

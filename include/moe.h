@@ -50,7 +50,8 @@ typedef enum {
   MOE_ERR_SHAPE = 2,           /* a size is out of range or not a multiple the kernels need */
   MOE_ERR_DTYPE = 3,           /* unsupported element type (e.g. non-BF16 shared expert)  */
   MOE_ERR_LAYOUT = 4,          /* inconsistent strides / both or neither of base and table */
-  MOE_ERR_UNSUPPORTED = 5,     /* a configuration not implemented (SwiGLU clamp)           */
+  MOE_ERR_UNSUPPORTED = 5,     /* a configuration not implemented (unknown flag bits, flag
+                                  combinations, swiglu_limit NaN / negative / infinite)    */
   MOE_ERR_WORKSPACE = 6,       /* saved / workspace buffer missing or too small            */
   MOE_ERR_ROUTE_OVERFLOW = 7,  /* device status word: a row had more than topk routes      */
   MOE_ERR_HIP = 8,             /* a HIP launch failed                                      */
@@ -102,7 +103,12 @@ typedef struct {
   int32_t routed_dtype;  /* MOE_BF16 or MOE_MXFP8_E4M3 (PR #6572, Supported configurations) */
   uint32_t flags;        /* MOE_FLAG_HAS_SHARED (else routed-only) | MOE_FLAG_RECOMPUTE
                             | MOE_FLAG_TOPK_ROUTING | MOE_FLAG_SHARED_GATE                 */
-  float swiglu_limit;    /* must be 0 (no clamp)                                          */
+  float swiglu_limit;    /* SwiGLU clamp L >= 0 of every expert (0: none).  The pages pass
+                            MCore's activation_func_clamp_value as swiglu_limit (PR #8210,
+                            review thread on the config port) without a formula; reading:
+                            h = silu(min(a, L)) clamp(b, -L, L), a = gate and b = up
+                            pre-activation, no gradient through a clamped input (the bounds
+                            themselves pass it).  NaN, negative or infinite: unsupported    */
 } moe_problem;
 
 /* One logical matrix per expert, [rows][cols], row-major.  Exactly one of

@@ -39,7 +39,8 @@ def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
 class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
                  routing=None, main_grad_dtype: str = "fp32", shared: bool = True,
-                 recompute: bool = False, routing_table=None, shared_gate: bool = False):
+                 recompute: bool = False, routing_table=None, shared_gate: bool = False,
+                 swiglu_limit: float = 0.0):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
         configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16".
         shared=False: routed-only mode; the shared weight and main_grad descriptors are
@@ -48,7 +49,7 @@ class DeviceProblem:
         activations).  routing_table: optional (top_experts [T,K] int32, router_weights
         [T,K] float32), the router's fixed-width table given to moe_forward_topk instead of
         the dense map; grad_probs is then [T,K].  shared_gate: the shared expert's output gate
-        (a seeded [H] weight and its main_grad)."""
+        (a seeded [H] weight and its main_grad).  swiglu_limit: the SwiGLU clamp (0: none)."""
         self.cfg = cfg
         self.device = device
         T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
@@ -82,7 +83,8 @@ class DeviceProblem:
         self.gated = shared_gate
         flags = ((mk.MOE_FLAG_HAS_SHARED if shared else 0) | (mk.MOE_FLAG_RECOMPUTE if recompute else 0)
                  | (mk.MOE_FLAG_TOPK_ROUTING if self.table else 0) | (mk.MOE_FLAG_SHARED_GATE if shared_gate else 0))
-        self.p = mk.problem(T, H, I, E, K, dt, flags=flags)
+        self.swiglu_limit = float(swiglu_limit)
+        self.p = mk.problem(T, H, I, E, K, dt, flags=flags, swiglu_limit=self.swiglu_limit)
 
         def routed_mat(key, rows, cols, conv, elem_cols):
             """moe_mat for a routed tensor stored [E][rows][cols] (single) or per expert (table)."""

@@ -640,6 +640,8 @@ struct Fc1Args {
   uint16_t* ab;
   uint16_t* h;
   int H, I;
+  float limit;   // SwiGLU clamp: h = silu(min(a, L)) clamp(b, -L, L) for L > 0, decided on
+                 // the BF16-rounded a and b (the values the backward reads)
 };
 
 template <bool MX>
@@ -691,6 +693,7 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int I = p.I;
+  const float L = p.limit;
 #pragma unroll
   for (int jp = 0; jp < TL::NJ / 2; ++jp) {
     const int jj = tt.nt * (TL::TN / 2) + (wn * TL::NJ / 2 + jp) * 32 + (lane & 31);
@@ -702,9 +705,14 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
         if (row >= tt.rows) continue;
         const float a = acc[i][2 * jp][r], b = acc[i][2 * jp + 1][r];
         const int64_t R = crow0 + row;
-        p.ab[R * 2 * I + jj] = (uint16_t)f2bf(a);
+        p.ab[R * 2 * I + jj] = (uint16_t)f2bf(a);       // stored unclamped
         p.ab[R * 2 * I + I + jj] = (uint16_t)f2bf(b);
-        p.h[R * I + jj] = (uint16_t)f2bf(a * sigmoidf_(a) * b);
+        // clamp decided on the stored (BF16) pre-activations, as the backward sees them
+        const bool a_hi = L > 0.0f && bf2f(f2bf(a)) > L;
+        const bool b_out = L > 0.0f && fabsf(bf2f(f2bf(b))) > L;
+        const float ac = a_hi ? L : a;
+        const float bc = b_out ? copysignf(L, b) : b;
+        p.h[R * I + jj] = (uint16_t)f2bf(ac * sigmoidf_(ac) * bc);
       }
   }
 }
@@ -805,7 +813,8 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::M
 
 // Data gradient of FC2 fused with the SwiGLU backward: gh = dyw W2 (contracting over H,
 // W2 [H][I] row-contiguous), then with the saved a, b:
-//   da = gh * b * silu'(a),  db = gh * silu(a)  -> dfc1 [rows][2I] (da at j, db at I + j).
+//   da = gh * b * silu'(a),  db = gh * silu(a)  -> dfc1 [rows][2I] (da at j, db at I + j)
+//   (with the clamp: a and b clamped first, and zero gradient through a clamped input).
 // MX: routed tiles take E4M3 dyw and the columnwise E4M3 copy of W2.
 struct DgradSwigluArgs {
   TokArgs t;
@@ -816,6 +825,7 @@ struct DgradSwigluArgs {
   const uint16_t* ab;
   uint16_t* dfc1;
   int H, I;
+  float limit;   // SwiGLU clamp limit (0: none); no gradient flows through a clamped input
 };
 
 template <bool MX>
@@ -871,9 +881,14 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
         const float a = bf2f(p.ab[R + n]);
         const float b = bf2f(p.ab[R + I + n]);
         const float gh = acc[i][j][r];
-        const float sg = sigmoidf_(a);
-        const float da = gh * b * (sg * (1.0f + a * (1.0f - sg)));
-        const float db = gh * (a * sg);
+        const float L = p.limit;
+        const bool a_hi = L > 0.0f && a > L;             // a, b: the stored BF16 values
+        const bool b_out = L > 0.0f && fabsf(b) > L;
+        const float ac = a_hi ? L : a;
+        const float bc = b_out ? copysignf(L, b) : b;
+        const float sg = sigmoidf_(ac);
+        const float da = a_hi ? 0.0f : gh * bc * (sg * (1.0f + ac * (1.0f - sg)));
+        const float db = b_out ? 0.0f : gh * (ac * sg);
         p.dfc1[R + n] = (uint16_t)f2bf(da);
         p.dfc1[R + I + n] = (uint16_t)f2bf(db);
       }

@@ -33,6 +33,7 @@ struct Dims {
   bool rc;           // recompute: saved holds the routing state only
   bool tk;           // routing given as the fixed-width [T][K] table
   bool sg;           // the shared expert's output is gated
+  float L;           // SwiGLU clamp limit (0: none)
 };
 
 Dims dims_of(const moe_problem* p) {
@@ -46,6 +47,7 @@ Dims dims_of(const moe_problem* p) {
   d.rc = (p->flags & MOE_FLAG_RECOMPUTE) != 0;
   d.tk = (p->flags & MOE_FLAG_TOPK_ROUTING) != 0;
   d.sg = (p->flags & MOE_FLAG_SHARED_GATE) != 0;
+  d.L = p->swiglu_limit;
   return d;
 }
 
@@ -185,7 +187,7 @@ moe_status check_problem(const moe_problem* p) {
   if (p->flags & ~(MOE_FLAG_HAS_SHARED | MOE_FLAG_RECOMPUTE | MOE_FLAG_TOPK_ROUTING | MOE_FLAG_SHARED_GATE))
     return MOE_ERR_UNSUPPORTED;
   if ((p->flags & MOE_FLAG_SHARED_GATE) && !(p->flags & MOE_FLAG_HAS_SHARED)) return MOE_ERR_UNSUPPORTED;
-  if (p->swiglu_limit != 0.0f) return MOE_ERR_UNSUPPORTED;
+  if (!(p->swiglu_limit >= 0.0f) || p->swiglu_limit > 3.0e38f) return MOE_ERR_UNSUPPORTED;   // NaN, < 0, inf
   if (p->routed_dtype != MOE_BF16 && p->routed_dtype != MOE_MXFP8_E4M3) return MOE_ERR_DTYPE;
   return MOE_OK;
 }
@@ -441,6 +443,7 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   a1.ab = P.ab;
   a1.h = P.h;
   a1.H = H; a1.I = I;
+  a1.limit = d.L;
   a1.mx = gemm::MxOperands{};
   if (d.mx) {
     a1.mx.aq = P.xq;
@@ -709,6 +712,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a3.ab = U16(A.ab);
   a3.dfc1 = WU16(B.dfc1);
   a3.H = H; a3.I = I;
+  a3.limit = d.L;
   a3.mx = gemm::MxOperands{};
   if (d.mx) {
     a3.mx.aq = W + B.dyq;

@@ -248,13 +248,20 @@ def swiglu_clamped(a, b, limit=0.0):
     activation_func_clamp_value to the backend as swiglu_limit; the pages give no
     formula): the gate pre-activation is clamped from above and the linear one to
     [-L, L] before the product, h = silu(min(a, L)) clamp(b, -L, L); a clamped input
-    passes no gradient (the bounds themselves pass it).  L = 0: no clamp."""
+    passes no gradient (the bounds themselves pass it).  L = 0: no clamp.
+
+    Whether an input is clamped is decided on its BF16 rounding, the precision in which
+    the layer keeps the pre-activations for its backward; the values themselves stay
+    exact.  (The gradient jumps at the bound, so the decision must be taken the same way
+    everywhere.)"""
     if limit and limit > 0:
-        ac = np.minimum(a, limit)
-        bc = np.clip(b, -limit, limit)
+        a_hi = bf16_round(a) > limit
+        b_out = np.abs(bf16_round(b)) > limit
+        ac = np.where(a_hi, limit, a)
+        bc = np.where(b_out, np.sign(b) * limit, b)
         h = silu(ac) * bc
-        dha = bc * dsilu(a) * (a <= limit)
-        dhb = silu(ac) * ((b >= -limit) & (b <= limit))
+        dha = bc * dsilu(ac) * ~a_hi
+        dhb = silu(ac) * ~b_out
         return h, dha, dhb
     return silu(a) * b, b * dsilu(a), silu(a)
 

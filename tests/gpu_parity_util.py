@@ -24,7 +24,8 @@ def oracle_weights(dp) -> "O.Weights":
     cfg = dp.cfg
     shared = getattr(dp, "shared", True)
     return O.Weights.from_bits(cfg.inter, dp.np_s1 if shared else None, dp.np_s2 if shared else None,
-                               lambda e: dp.np_routed[e], cfg.routed, shared_gate=getattr(dp, "np_gate", None))
+                               lambda e: dp.np_routed[e], cfg.routed, shared_gate=getattr(dp, "np_gate", None),
+                               swiglu_limit=getattr(dp, "swiglu_limit", 0.0))
 
 
 def check_routing_state(dp):

@@ -78,11 +78,15 @@ def test_invalid_problem_is_rejected(kw, status):
 
 def test_unsupported_configurations_are_rejected():
     p = _ok_problem()
-    p.flags = 4                                   # an unknown flag bit
+    p.flags = 16                                  # an unknown flag bit
     assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_UNSUPPORTED
+    for bad in (-1.0, float("nan"), float("inf")):   # SwiGLU clamp limit must be finite and >= 0
+        p = _ok_problem()
+        p.swiglu_limit = bad
+        assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_UNSUPPORTED
     p = _ok_problem()
-    p.swiglu_limit = 7.0                          # clamp not supported
-    assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_UNSUPPORTED
+    p.swiglu_limit = 7.0                          # a clamp is accepted (fails later on the weights)
+    assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_DTYPE
     p = _ok_problem()
     p.routed_dtype = 2                            # fp32 routed weights
     assert mk.moe_forward(p, 0, 0, 0, mk.moe_weights(), 0, 0, 0, 0, 0) == mk.MOE_ERR_DTYPE

@@ -424,6 +424,10 @@ def test_swiglu_clamp_limits_reduce_to_closed_forms():
     bc = np.array([-0.5, 0.4, -0.4, 0.5, 0.1])
     assert np.allclose(h, ac * sig(ac) * bc, rtol=0, atol=1e-15)
     assert dha[4] == 0 and dha[3] != 0      # a = L still passes the gradient, a > L does not
+    # the decision is taken on the BF16 rounding: just above L but rounding to L is not clamped
+    eps = 0.5 * 2.0 ** -9                   # below half a BF16 ulp of 0.5
+    h2, dha2, _ = O.swiglu_clamped(np.array([0.5 + eps]), np.array([0.1]), 0.5)
+    assert dha2[0] != 0 and np.isclose(h2[0], (0.5 + eps) * sig(0.5 + eps) * 0.1, rtol=1e-15, atol=0)
     assert dhb[0] == 0 and dhb[3] == 0 and dhb[1] != 0
 
 
