@@ -780,7 +780,7 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a5.N = I;
   MOE_TRY(launch("wgrad_fc2", st, [&] { launch_wgrad<2>(a5, d, grad_bf16(mg->routed_gate), st); }));
 
-  // B5 (+B6): FC1 weight gradient: main_grad_{gate,up}[e] += dfc1^T xp
+  // B5 (+B6): FC1 weight gradient: main_grad_{gate,up}[e] += dfc1^T x[slot_t]
   gemm::WgradArgs a6;
   a6.counts = I32(L.counts);
   a6.offsets = I32(L.offsets);
