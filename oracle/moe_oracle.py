@@ -46,7 +46,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_decode", "bf16_round", "main_grad_after", "e4m3_decode", "e8m0_decode", "mxfp8_decode_rowwise",
+    "bf16_decode", "bf16_round", "e4m3_round", "mx_block_exponent", "mx_quantize", "main_grad_after", "e4m3_decode", "e8m0_decode", "mxfp8_decode_rowwise",
     "mxfp8_decode_colwise", "compact_routing", "dispatch_index", "silu", "dsilu",
     "swiglu_ffn", "Weights", "moe_forward", "moe_forward_f64", "moe_backward",
     "moe_backward_f64", "RouteOverflow", "RouteInvalid", "check_table", "moe_forward_table",
@@ -119,6 +119,38 @@ def e8m0_decode(codes: np.ndarray) -> np.ndarray:
 
 _E4M3_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))   # the closed form above, tabulated
 _E8M0_TABLE = e8m0_decode(np.arange(256, dtype=np.uint8))
+
+
+def e4m3_round(u) -> np.ndarray:
+    """Round to the nearest E4M3 (OCP E4M3FN) value, ties to even, for |u| <= 448: 3
+    fraction bits, exponents down to -6, then subnormals spaced 2^-9."""
+    u = np.asarray(u, dtype=np.float64)
+    _, ex = np.frexp(u)                       # |u| = f 2^ex, f in [0.5, 1)
+    ulp = np.ldexp(1.0, np.maximum(ex - 4, -9))
+    return np.round(u / ulp) * ulp
+
+
+def mx_block_exponent(amax) -> np.ndarray:
+    """E8M0 exponent of an MX block: the smallest e in [-127, 127] with amax 2^-e <= 448,
+    E4M3's largest finite magnitude (-127 for an all-zero block)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    e = ex.astype(np.int64) - 9               # 2^(ex-1) <= amax < 2^ex, and 448 < 2^9
+    for _ in range(3):                        # the smallest e meeting the bound
+        e = np.where(np.ldexp(amax, -e) > 448.0, e + 1, e)
+        e = np.where(np.ldexp(amax, -(e - 1)) <= 448.0, e - 1, e)
+    e = np.where(amax > 0, e, -127)
+    return np.clip(e, -127, 127)
+
+
+def mx_quantize(v) -> np.ndarray:
+    """The MXFP8 value of v along its last axis (blocks of 32 sharing one E8M0 scale, each
+    element rounded to E4M3): quantise then decode, as the recipe does to the FP8
+    GEMMs' activation inputs (PR #6572, Supported configurations: MXFP8 routed experts)."""
+    v = np.asarray(v, dtype=np.float64)
+    b = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    e = mx_block_exponent(np.abs(b).max(axis=-1))[..., None]
+    return (e4m3_round(np.ldexp(b, -e)) * np.ldexp(1.0, e)).reshape(v.shape)
 
 
 def mxfp8_decode_rowwise(payload: np.ndarray, scale: np.ndarray) -> np.ndarray:
@@ -278,6 +310,25 @@ def shared_gate_score(x, g):
     return 1.0 / (1.0 + np.exp(-(np.asarray(x, dtype=np.float64) @ g)))
 
 
+def _routed_ffn(X, Wg, Wu, Wd, weights):
+    """One routed expert's forward on rows X: (a, b, h, y), with the MXFP8 activation
+    inputs when weights.mx_activations (FC1 reads MXFP8 x, FC2 MXFP8 of the BF16 h)."""
+    if not weights.mx_activations:
+        return swiglu_ffn(X, Wg, Wu, Wd, weights.swiglu_limit)
+    Xq = mx_quantize(X)
+    a = Xq @ Wg.T
+    b = Xq @ Wu.T
+    h, _, _ = swiglu_clamped(a, b, weights.swiglu_limit)
+    y = mx_quantize(bf16_round(h)) @ Wd.T
+    return a, b, h, y
+
+
+def _routed_dgrad_in(v, weights):
+    """A data-gradient GEMM's activation input (w dy, or dfc1 = [da | db]): MXFP8 of its
+    BF16 rounding when weights.mx_activations, else itself."""
+    return mx_quantize(bf16_round(v)) if weights.mx_activations else v
+
+
 class Weights:
     """Float64 views of the six weights, in the runtime's argument order
     (Megatron Core API docs, mok.runtime, _MoKWeightArguments: shared gate,
@@ -286,6 +337,10 @@ class Weights:
     shared      : (Wg [I,H], Wu [I,H], Wd [H,I]), or None in routed-only mode
     shared_gate : the shared expert's output gate weight g [H], or None (no gate)
     swiglu_limit: the SwiGLU clamp limit L of every expert (0: none; swiglu_clamped)
+    mx_activations: the routed experts' FP8 GEMMs also take their activation inputs in
+                  MXFP8 (x for FC1, the BF16 h for FC2, the BF16 w dy and dfc1 for the
+                  data gradients), as the MXFP8 recipe does; the weight gradients keep
+                  their operands in full precision
     routed(e)   : (Wg, Wu, Wd) as used by the forward
     routed_t(e) : (Wg, Wu, Wd) as used by dgrad (columnwise decode for MXFP8)
 
@@ -293,9 +348,11 @@ class Weights:
     decoded on demand, one at a time.
     """
 
-    def __init__(self, shared, routed_fn, routed_dgrad_fn=None, shared_gate=None, swiglu_limit=0.0):
+    def __init__(self, shared, routed_fn, routed_dgrad_fn=None, shared_gate=None, swiglu_limit=0.0,
+                 mx_activations=False):
         self.shared = shared
         self.swiglu_limit = float(swiglu_limit)
+        self.mx_activations = bool(mx_activations)
         self.shared_gate = None if shared_gate is None else np.asarray(shared_gate, dtype=np.float64)
         self._routed = routed_fn
         self._routed_t = routed_dgrad_fn or routed_fn
@@ -308,7 +365,7 @@ class Weights:
 
     @staticmethod
     def from_bits(inter: int, shared_fc1, shared_fc2, routed_getter, routed_dtype: str, shared_gate=None,
-                  swiglu_limit=0.0):
+                  swiglu_limit=0.0, mx_activations=False):
         """shared_fc1 u16 [2I, H], shared_fc2 u16 [H, I]; routed_getter(e) -> dict of
         bits (see moe_inputs.routed_expert).  Gate = FC1 rows [0, I), up = rows [I, 2I)
         (Megatron Core API docs, mok.runtime, _gate_up_weight_arguments: gate and up
@@ -337,7 +394,8 @@ class Weights:
             d = routed_getter(e)
             w1 = mxfp8_decode_colwise(d["fc1_c"], d["fc1_cs"])
             return w1[:I], w1[I:2 * I], mxfp8_decode_colwise(d["fc2_c"], d["fc2_cs"])
-        return Weights(shared, fwd, bwd, shared_gate=gate, swiglu_limit=swiglu_limit)
+        return Weights(shared, fwd, bwd, shared_gate=gate, swiglu_limit=swiglu_limit,
+                       mx_activations=mx_activations)
 
 
 # ----------------------------------------------------------------------------------
@@ -403,7 +461,7 @@ def _forward_table_f64(x, top, rw, E, weights: Weights, tokens=None):
             continue
         rows = np.array([pos[t] for t, _, _ in lst])
         w = np.array([w for _, _, w in lst])
-        _, _, _, y = swiglu_ffn(x[rows], *weights.routed(e), weights.swiglu_limit)
+        _, _, _, y = _routed_ffn(x[rows], *weights.routed(e), weights)
         for j, r in enumerate(rows):     # fixed order; np.add.at would also do
             out[r] += w[j] * y[j]
     return out
@@ -505,14 +563,15 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
         rows = np.array([pos[t] for t, _, _ in lst])
         w = np.array([w for _, _, w in lst])
         Wg, Wu, Wd = weights.routed(e)
-        a, b, h, y = swiglu_ffn(x[rows], Wg, Wu, Wd, weights.swiglu_limit)
+        a, b, h, y = _routed_ffn(x[rows], Wg, Wu, Wd, weights)
         _, dha, dhb = swiglu_clamped(a, b, weights.swiglu_limit)
         dprobs[rows, e] = np.sum(g[rows] * y, axis=1)
         Tg, Tu, Td = weights.routed_t(e)
-        gh = w[:, None] * (g[rows] @ Td)
+        gh = _routed_dgrad_in(w[:, None] * g[rows], weights) @ Td
         da = gh * dha
         db = gh * dhb
-        dxe = da @ Tg + db @ Tu
+        dq = _routed_dgrad_in(np.concatenate([da, db], axis=1), weights)
+        dxe = dq[:, :da.shape[1]] @ Tg + dq[:, da.shape[1]:] @ Tu
         for j, r in enumerate(rows):
             dx[r] += dxe[j]
 
@@ -531,10 +590,10 @@ def _backward_table_f64(dy_all, x_all, top, rw, E, weights: Weights, tokens=None
             w = np.array([w for _, _, w in lst])
             X = x_all[ts]
             G = dy_all[ts]
-            a, b, h, _ = swiglu_ffn(X, Wg, Wu, Wd, weights.swiglu_limit)
+            a, b, h, _ = _routed_ffn(X, Wg, Wu, Wd, weights)
             _, dha, dhb = swiglu_clamped(a, b, weights.swiglu_limit)
             Tg, Tu, Td = weights.routed_t(e)
-            gh = w[:, None] * (G @ Td)
+            gh = _routed_dgrad_in(w[:, None] * G, weights) @ Td
             da = gh * dha
             db = gh * dhb
             dW[e] = (da.T @ X, db.T @ X, (w[:, None] * G).T @ h)

@@ -431,6 +431,111 @@ def test_swiglu_clamp_limits_reduce_to_closed_forms():
     assert dhb[0] == 0 and dhb[3] == 0 and dhb[1] != 0
 
 
+def test_e4m3_round_matches_torch_cast():
+    """RNE to E4M3 against torch's float8_e4m3fn cast on values across every binade,
+    the subnormals, exact codes and their midpoints."""
+    rng = np.random.default_rng(31)
+    u = np.concatenate([rng.uniform(-448, 448, 20000),
+                        np.ldexp(rng.uniform(0.5, 1.0, 20000), rng.integers(-12, 9, 20000)) * rng.choice([-1, 1], 20000),
+                        O.e4m3_decode(np.arange(256, dtype=np.uint8))])
+    codes = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = np.sort(codes[np.isfinite(codes) & (codes >= 0)])
+    u = np.concatenate([u, 0.5 * (fin[1:] + fin[:-1]), -0.5 * (fin[1:] + fin[:-1])])
+    u = u[np.isfinite(u) & (np.abs(u) <= 448)].astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(u).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(O.e4m3_round(u), ref)
+
+
+def test_mx_block_exponent_and_quantize_closed_forms():
+    rng = np.random.default_rng(32)
+    amax = np.concatenate([np.ldexp(rng.uniform(0.5, 1.0, 5000), rng.integers(-120, 120, 5000)),
+                           [448.0, 448.0 * 2.0 ** 7, 449.0, 1.75, 1.75 * (1 + 2 ** -23), 0.0]])
+    e = O.mx_block_exponent(amax)
+    pos = amax > 0
+    assert np.all(np.ldexp(amax[pos], -e[pos]) <= 448.0)
+    assert np.all((np.ldexp(amax[pos], -(e[pos] - 1)) > 448.0) | (e[pos] == -127))
+    assert e[-1] == -127 and O.mx_block_exponent(448.0) == 0 and O.mx_block_exponent(449.0) == 1
+    v = rng.normal(0, 3, (4, 64))
+    q = O.mx_quantize(v)
+    for r in range(4):
+        for blk in range(2):
+            sl = slice(32 * blk, 32 * blk + 32)
+            sc = 2.0 ** O.mx_block_exponent(np.abs(v[r, sl]).max())
+            assert np.array_equal(q[r, sl], O.e4m3_round(v[r, sl] / sc) * sc)
+    assert np.max(np.abs(q - v) / np.abs(v).max()) < 2 ** -3     # 3 fraction bits
+
+
+def _torch_mx(v):
+    """MXFP8 quantise-dequantise along the last axis with torch's own float8_e4m3fn cast
+    (an implementation independent of the oracle's)."""
+    v = torch.as_tensor(v, dtype=torch.float64)
+    b = v.reshape(*v.shape[:-1], v.shape[-1] // 32, 32)
+    amax = b.abs().amax(dim=-1, keepdim=True)
+    # smallest e with amax 2^-e <= 448, searched over the exponent range
+    es = torch.arange(-127, 128, dtype=torch.float64)
+    ok = amax * torch.pow(2.0, -es) <= 448.0
+    e = torch.where(ok, es, torch.full_like(es, 1e9)).amin(dim=-1, keepdim=True)
+    e = torch.where(amax > 0, e, torch.full_like(e, -127.0))
+    q = (b * torch.pow(2.0, -e)).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64) * torch.pow(2.0, e)
+    return q.reshape(v.shape)
+
+
+def test_mx_activation_mode_matches_an_independent_recipe():
+    """The oracle's MXFP8-activation mode (x, the BF16 h, the BF16 w dy and dfc1 quantised
+    before the routed FP8 GEMMs) against the same recipe written with torch ops and torch's
+    E4M3 cast, for the forward, dprobs and dx."""
+    cfg = gen.custom(12, 64, 3, 2, 32, routed="mxfp8", idx=27)
+    probs, rmap = gen.routing(cfg)
+    x, dy = gen.hidden(cfg), gen.grad_out(cfg)
+    s1, s2 = gen.shared_weights(cfg)
+    routed = [gen.routed_expert(cfg, e) for e in range(3)]
+    W = O.Weights.from_bits(32, s1, s2, lambda e: routed[e], "mxfp8", mx_activations=True)
+    out = O.moe_forward(x, probs, rmap, 2, W)
+    g = O.moe_backward(dy, x, probs, rmap, 2, W)
+    xs = torch.from_numpy(O.bf16_decode(x))
+    dys = torch.from_numpy(O.bf16_decode(dy))
+    bf = lambda t: t.to(torch.bfloat16).to(torch.float64)
+    I = 32
+    ref = torch.zeros_like(xs)
+    dx = torch.zeros_like(xs)
+    dpr = torch.zeros(12, 3, dtype=torch.float64)
+    sh = [torch.from_numpy(m) for m in W.shared]
+    a = xs @ sh[0].T
+    b = xs @ sh[1].T
+    ref += (torch.nn.functional.silu(a) * b) @ sh[2].T
+    for t in range(12):
+        for e in range(3):
+            if not rmap[t, e]:
+                continue
+            wg, wu, wd = (torch.from_numpy(m) for m in W.routed(e))
+            tg, tu, td = (torch.from_numpy(m) for m in W.routed_t(e))
+            xq = _torch_mx(xs[t:t + 1])
+            a, b = xq @ wg.T, xq @ wu.T
+            sg = torch.sigmoid(a)
+            h = a * sg * b
+            y = _torch_mx(bf(h)) @ wd.T
+            w = float(probs[t, e])
+            ref[t] += w * y[0]
+            dpr[t, e] = (dys[t] * y[0]).sum()
+            gh = _torch_mx(bf(w * dys[t:t + 1])) @ td
+            da = gh * b * (sg * (1 + a * (1 - sg)))
+            db = gh * (a * sg)
+            dq = _torch_mx(bf(torch.cat([da, db], dim=1)))
+            dx[t] += (dq[:, :I] @ tg + dq[:, I:] @ tu)[0]
+    # the shared expert's data gradient (BF16, unquantised)
+    a = xs @ sh[0].T
+    b = xs @ sh[1].T
+    sg = torch.sigmoid(a)
+    gh = dys @ sh[2]
+    dx += (gh * b * (sg * (1 + a * (1 - sg)))) @ sh[0] + (gh * a * sg) @ sh[1]
+    assert _rel(out, ref.numpy()) < 1e-12
+    assert _rel(g["dprobs"], dpr.numpy()) < 1e-12
+    assert _rel(g["dx"], dx.numpy()) < 1e-12
+    # and it is a different function from the plain mode (the quantisation is visible)
+    Wp = O.Weights.from_bits(32, s1, s2, lambda e: routed[e], "mxfp8")
+    assert _rel(O.moe_forward(x, probs, rmap, 2, Wp), out) > 1e-4
+
+
 def test_sampled_rows_and_experts_equal_full_run():
     cfg, probs, rmap, x, dy, W, d = _small_problem(30, 32, 5, 2, 16, seed=13, short=0.2)
     full = O.moe_backward(dy, x, probs, rmap, cfg.topk, W)
