@@ -20,12 +20,12 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def oracle_weights(dp) -> "O.Weights":
+def oracle_weights(dp, mx_activations=False) -> "O.Weights":
     cfg = dp.cfg
     shared = getattr(dp, "shared", True)
     return O.Weights.from_bits(cfg.inter, dp.np_s1 if shared else None, dp.np_s2 if shared else None,
                                lambda e: dp.np_routed[e], cfg.routed, shared_gate=getattr(dp, "np_gate", None),
-                               swiglu_limit=getattr(dp, "swiglu_limit", 0.0))
+                               swiglu_limit=getattr(dp, "swiglu_limit", 0.0), mx_activations=mx_activations)
 
 
 def check_routing_state(dp):

@@ -72,6 +72,39 @@ def _check_backward(dp, W, tokens=None, experts=None, tol=BF16_TOL):
     return errs
 
 
+def _check_mx_aware(dp, tokens=None, experts=None, tol=BF16_TOL, tol_requant=2 * BF16_TOL):
+    """MXFP8 routed experts against the oracle that also quantises the FP8 GEMMs'
+    activation inputs as the recipe does: out, dprobs and the FC2 weight gradients to the
+    BF16 bound; dx and the FC1 weight gradients, whose FP8 GEMM input dfc1 is itself
+    quantised from values the two sides compute in different precision (an occasional
+    E4M3 code lands one step apart, an eighth of that element), to twice it.  Both are
+    well inside the plain MXFP8 bound (the shared expert is BF16, checked elsewhere)."""
+    cfg = dp.cfg
+    W = oracle_weights(dp, mx_activations=True)
+    I, H = cfg.inter, cfg.hidden
+    ref = O.moe_forward(dp.np_x, dp.np_probs, dp.np_rmap, cfg.topk, W, tokens=tokens)
+    sel = slice(None) if tokens is None else torch.as_tensor(tokens, device=dp.out.device)
+    errs = {"out": rel_err(to_f64(dp.out[sel]), ref)}
+    g = O.moe_backward(dp.np_dy, dp.np_x, dp.np_probs, dp.np_rmap, cfg.topk, W, tokens=tokens,
+                       experts=experts, shared_grads=False)
+    errs["dx"] = rel_err(to_f64(dp.dx[sel]), g["dx"])
+    errs["dprobs"] = rel_err(dp.dprobs[sel].cpu().numpy().astype(np.float64), g["dprobs"])
+    for e in (range(cfg.experts) if experts is None else experts):
+        dg, du, dd = g["dW"][e]
+        if np.abs(dd).max() == 0:
+            continue
+        d1 = to_f64(dp.mg_r1_list[e]) - dp.main_grad_start((2 * I, H), e)
+        d2 = to_f64(dp.mg_r2_list[e]) - dp.main_grad_start((H, I), e)
+        errs[f"w1_{e}"] = rel_err(d1, np.concatenate([dg, du]))
+        errs[f"w2_{e}"] = rel_err(d2, dd)
+    worst = max(errs, key=lambda k: errs[k])
+    print(f"[parity] MXFP8-activation oracle: out {errs['out']:.3e} dx {errs['dx']:.3e} dprobs "
+          f"{errs['dprobs']:.3e} worst {worst} {errs[worst]:.3e} (tol {tol})", flush=True)
+    lim = {k: (tol_requant if (k == "dx" or k.startswith("w1_")) else tol) for k in errs}
+    bad = {k: v for k, v in errs.items() if not (v <= lim[k])}
+    assert not bad, f"over tolerance: {bad}"
+
+
 def test_config0_forward_matches_oracle(gpu_lib):
     dp = _dp(gen.config(0))
     dp.forward()
@@ -227,6 +260,7 @@ def test_mxfp8_forward_backward_matches_oracle(gpu_lib, layout, shape):
     W = oracle_weights(dp)
     _check_forward(dp, W, tol=MXFP8_TOL)
     _check_backward(dp, W, tol=MXFP8_TOL)
+    _check_mx_aware(dp)
 
 
 @pytest.mark.parametrize("idx", [3, 4])
@@ -247,6 +281,7 @@ def test_full_size_mxfp8_config_sampled(gpu_lib, idx):
     counts = np.asarray(dp.layer.routing_state()["counts"].cpu())
     busiest = int(np.argmax(counts))
     _check_backward(dp, W, tokens=toks, experts=sorted({0, busiest, cfg.experts - 1}), tol=MXFP8_TOL)
+    _check_mx_aware(dp, tokens=toks, experts=sorted({0, busiest}))
 
 
 # ----------------------------------------------------------------------------------
