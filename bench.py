@@ -34,7 +34,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload index (2: 4096-token BF16 layer)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload index (2: 4096-token BF16 layer; 3: its MXFP8 form; 4: 8192-token "
+                         "MXFP8 layer; 5, 6: one GPU's 6-expert share of layer 2 / 3 under 16-way EP)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--main-grad", choices=("fp32", "bf16"), default="fp32",
@@ -65,6 +67,63 @@ def wgrad_fc1_bytes(cfg, slots, mg_bytes=4, shared=True):
     return (E + ns) * 2 * I * H * 2 * mg_bytes + (slots + ns * T) * (2 * I + H) * 2
 
 
+def gemm_work(cfg, slots, shared=True, mg_bytes=4):
+    """Algorithmic (flops, HBM bytes) per launch of each GEMM kernel of one step.  Rows are
+    the routed slots plus, with the shared expert, the tokens.  Weights are read once per
+    launch (MXFP8 routed: one E4M3 byte + 1/32 E8M0 byte per element, the copy the GEMM
+    contracts along), every gathered activation row once per slot (the routed FP8 GEMMs
+    read it quantised), every output row written once, main_grad read and written once."""
+    E, H, I, T = cfg.experts, cfg.hidden, cfg.inter, cfg.tokens
+    ns = 1 if shared else 0
+    Rr, Rs = slots, ns * T
+    R = Rr + Rs
+    q = 1 + 1 / 32 if cfg.routed == "mxfp8" else 2       # routed weight / FP8 GEMM input bytes
+    w1 = E * 2 * I * H * q + ns * 2 * I * H * 2
+    w2 = E * H * I * q + ns * H * I * 2
+    return {
+        "fc1_swiglu": (4 * H * I * R, w1 + Rr * H * q + Rs * H * 2 + R * 3 * I * 2),
+        "fc2": (2 * H * I * R, w2 + Rr * I * q + Rs * I * 2 + R * H * 2),
+        "dgrad_fc2_swiglu": (2 * H * I * R, w2 + Rr * H * q + Rs * H * 2 + R * 2 * I * 2 * 2),
+        "dgrad_fc1": (4 * H * I * R, w1 + Rr * 2 * I * q + Rs * 2 * I * 2 + R * H * 2),
+        "wgrad_fc1": (4 * H * I * R, wgrad_fc1_bytes(cfg, slots, mg_bytes, shared)),
+        "wgrad_fc2": (2 * H * I * R, (E + ns) * H * I * 2 * mg_bytes + R * (H + I) * 2),
+    }
+
+
+def mfma_peak(cfg, kernel, slots, shared=True):
+    """Dense MFMA peak (TFLOP/s) for a GEMM kernel: BF16, or for the routed FP8 GEMMs of
+    an MXFP8 layer the flop-weighted harmonic mix of the FP8 peak (routed rows) and the
+    BF16 peak (shared rows, which stay BF16).  Weight gradients run on BF16 operands."""
+    if cfg.routed != "mxfp8" or kernel.startswith("wgrad"):
+        return MFMA_PEAK["bf16"]
+    rr, rs = slots, (cfg.tokens if shared else 0)
+    return (rr + rs) / (rr / MFMA_PEAK["mxfp8"] + rs / MFMA_PEAK["bf16"])
+
+
+def kernel_roofline(cfg, slots, ktimes, shared=True, mg_bytes=4):
+    """Per GEMM kernel: the binding roofline (MFMA if its flops take longer at peak than
+    its bytes at the HBM peak, else HBM), the achieved rate from its live average launch
+    time, and the fraction of that peak."""
+    res = {}
+    for name, (fl, by) in gemm_work(cfg, slots, shared, mg_bytes).items():
+        n_l, tot = ktimes.get(name, (0, 0.0))
+        if n_l == 0:
+            continue
+        ms = tot / n_l
+        pk = mfma_peak(cfg, name, slots, shared)
+        if fl / (pk * 1e12) >= by / (HBM_PEAK_GBS * 1e9):
+            ach = fl / (ms * 1e-3) / 1e12
+            res[name] = {"bound": "mfma", "achieved": round(ach, 1), "peak": round(pk, 1), "unit": "TFLOP/s",
+                         "frac": round(ach / pk, 4), "avg_launch_ms": round(ms, 4), "alg_flops_per_launch": fl,
+                         "launches": n_l}
+        else:
+            ach = by / (ms * 1e-3) / 1e9
+            res[name] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "avg_launch_ms": round(ms, 4),
+                         "alg_bytes_per_launch": int(by), "launches": n_l}
+    return res
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "moe_megakernel_amd", "csrc")
@@ -74,9 +133,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel: str):
+def counter_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources; else None."""
+    on the current kernel sources and this workload; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(p) as f:
@@ -84,7 +143,7 @@ def counter_traffic(kernel: str):
     except (OSError, ValueError):
         return None
     ent = t.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash() or ent.get("workload") != workload:
         return None
     return ent.get("bytes_per_launch")
 
@@ -198,16 +257,13 @@ def main():
     shared_fl = 18.0 * cfg.hidden * cfg.inter * n_shared
     mfma_frac = (routed_fl / (MFMA_PEAK[dtype] * 1e12) + shared_fl / (MFMA_PEAK["bf16"] * 1e12)) / (ms * 1e-3)
 
-    dom = "wgrad_fc1"
-    n_l, tot_ms = ktimes.get(dom, (0, 0.0))
-    avg_ms = tot_ms / max(n_l, 1)
-    alg_bytes = wgrad_fc1_bytes(cfg, slots, 2 if args.main_grad == "bf16" else 4, shared)
-    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9 if avg_ms > 0 else 0.0
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": counter_traffic(dom) if args.main_grad == "fp32" and shared else None,
-                "avg_launch_ms": round(avg_ms, 4),
-                "alg_bytes_per_launch": alg_bytes}
+    # the dominant kernel: the GEMM kernel with the largest share of the step
+    krl = kernel_roofline(cfg, slots, ktimes, shared, 2 if args.main_grad == "bf16" else 4)
+    dom = max(krl, key=lambda k: krl[k]["avg_launch_ms"] * krl[k]["launches"])
+    plain = (args.main_grad == "fp32" and shared and not args.recompute and not args.topk_input
+             and not args.shared_gate and args.swiglu_limit == 0)
+    roofline = {"kernel": dom, **{k: v for k, v in krl[dom].items() if k != "launches"},
+                "traffic": counter_traffic(dom, cfg.name) if plain else None}
 
     line = {
         "metric": "MoE layer fwd+bwd TFLOPS and % of MFMA peak, 4096 tokens, 1 GPU",
@@ -224,6 +280,7 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},
+        "kernels_roofline": {k: {"bound": v["bound"], "frac": v["frac"]} for k, v in krl.items()},
     }
     line["hbm_calibration"] = hbm_calibration()
     if not args.no_cpu_baseline:

@@ -57,6 +57,10 @@ CONFIGS = {
     2: Config(2, "proxy-4096-bf16-balanced", 4096, 4096, 96, 4, 1024, "bf16", "single", "balanced", 0.0, 0.0, 0, True),
     3: Config(3, "proxy-4096-mxfp8-skewed-table", 4096, 4096, 96, 4, 1024, "mxfp8", "table", "softmax", 1.5, 0.0, 0, True),
     4: Config(4, "large-8192-mxfp8", 8192, 7168, 64, 6, 2048, "mxfp8", "single", "softmax", 1.0, 0.02, 5, True),
+    # one GPU's share of the 96-expert layer under 16-way expert parallelism: 6 local
+    # experts, each receiving about 2731 of the 16384 routed rows of 4096 tokens
+    5: Config(5, "ep16-share-4096-bf16", 4096, 4096, 6, 4, 1024, "bf16", "single", "balanced", 0.0, 0.0, 0, True),
+    6: Config(6, "ep16-share-4096-mxfp8", 4096, 4096, 6, 4, 1024, "mxfp8", "single", "balanced", 0.0, 0.0, 0, True),
 }
 
 

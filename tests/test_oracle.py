@@ -91,7 +91,7 @@ def test_generator_is_deterministic_per_expert():
     assert np.array_equal(p1, p2) and np.array_equal(m1, m2)
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4, 5, 6])
 def test_generator_routing_shapes(idx):
     cfg = gen.config(idx)
     probs, rmap = gen.routing(cfg)
