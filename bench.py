@@ -142,8 +142,8 @@ def counter_traffic(kernel: str, workload: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = t.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash() or ent.get("workload") != workload:
+    ent = t.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
 

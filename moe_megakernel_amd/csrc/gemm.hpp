@@ -516,10 +516,19 @@ __device__ __forceinline__ void zero_acc(Acc<TL>& acc) {
 // Token-dimension grouped tiles: group g < E is routed expert g with counts[g] rows
 // starting at offsets[g] of the permuted buffers; group E, when present, is the
 // shared expert with T rows.  tile_prefix[g] = sum of ceil(rows / BMT) over groups before g.  Linear
-// tiles (m-tile major, n-tile minor) are split into 8 contiguous chunks, chunk x
-// run by the blocks with blockIdx % 8 == x (the blocks one XCD receives), so the
-// n-tiles that share an A row panel run on one L2.
+// tiles are split into 8 contiguous chunks, chunk x run by the blocks with blockIdx % 8
+// == x (the blocks one XCD receives).  Inside a group the linear order walks bands of
+// kBandM m-tiles, column by column (m fastest), so the tiles resident on one XCD at a
+// time form a block of about kBandM m-tiles x (32 / kBandM) n-tiles: their A row panels
+// and B column panels are fetched into that XCD's L2 once per pass instead of the whole
+// weight being streamed again for every m-tile pair.  A group with one m-tile (at most
+// BMT rows) is walked along n as before.
 // ---------------------------------------------------------------------------------
+#ifndef MOE_BAND_M
+#define MOE_BAND_M 8
+#endif
+constexpr int kBandM = MOE_BAND_M;
+
 struct TokTile {
   int g, m0, rows, nt;
   bool ok;
@@ -538,14 +547,18 @@ __device__ __forceinline__ TokTile map_tok_tile(const int32_t* __restrict__ tile
   tt.ok = (j < c) && (L < total);
   if (!tt.ok) return tt;
   const int mt = L / ntn;
-  tt.nt = L - mt * ntn;
   int lo = 0, hi = groups - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (sp[mid] <= mt) lo = mid; else hi = mid - 1;
   }
   tt.g = lo;
-  tt.m0 = (mt - sp[lo]) * BMT;
+  const int li = L - sp[lo] * ntn;                 // tile inside the group
+  const int band = li / (kBandM * ntn);
+  const int r = li - band * kBandM * ntn;
+  const int h = min(kBandM, sp[lo + 1] - sp[lo] - band * kBandM);   // m-tiles in this band
+  tt.nt = r / h;
+  tt.m0 = (band * kBandM + r % h) * BMT;
   const int n = (lo < E) ? counts[lo] : T;
   tt.rows = min(BMT, n - tt.m0);
   return tt;
