@@ -639,6 +639,72 @@ __device__ __forceinline__ int wave_m() { return __builtin_amdgcn_readfirstlane(
 template <class TL>
 __device__ __forceinline__ int wave_n() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % TL::NWN; }
 
+// Token-dimension epilogue through LDS.  After the K loop the stage buffers are free: the
+// accumulators of one wave row (WMR tile rows x TN columns, fp32) are parked there per
+// round, then every thread takes pieces of 8 consecutive output columns of a row, so the
+// epilogue's global loads and stores move 16 bytes per lane instead of 2.  LDS row r holds
+// 16-byte chunk c at c ^ 8 ((r >> 2) & 1): the two row groups a wave writes at once fall
+// in disjoint banks.
+//  PAIR = false: f(tile_row, col, v) with v = tile columns col .. col + 7;
+//  PAIR = true (FC1's interleaved gate/up tile: columns 64 k .. 64 k + 31 are gate
+//  columns 32 k .. 32 k + 31 and the next 32 the matching up columns): f(tile_row, lc, g, u)
+//  with g, u = gate and up values of the tile's logical columns lc .. lc + 7.
+template <class TL, bool PAIR, class F>
+__device__ __forceinline__ void tok_epilogue(const Acc<TL>& acc, uint8_t* lds, int rows, int ncols, const F& f) {
+  constexpr int PPR = PAIR ? TL::TN / 16 : TL::TN / 8;   // pieces per row
+  constexpr int PPT = TL::WMR * PPR / TL::NTH;           // pieces per thread per round
+  static_assert(TL::WMR * TL::TN * 4 <= TL::LDS && (TL::WMR * PPR) % TL::NTH == 0, "epilogue round");
+  float* ct = reinterpret_cast<float*>(lds);
+  const int t = threadIdx.x, lane = t & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  auto sw = [](int r) { return ((r >> 2) & 1) << 3; };
+  auto get8 = [&](const float* rowp, int r, int c0, float* v) __attribute__((always_inline)) {
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(rowp + ((((c0 >> 2)) ^ sw(r)) << 2));
+    const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(rowp + ((((c0 >> 2) + 1) ^ sw(r)) << 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { v[k] = x0[k]; v[4 + k] = x1[k]; }
+  };
+#pragma unroll
+  for (int q = 0; q < TL::NWM; ++q) {
+    if (q * TL::WMR >= rows) break;
+    __syncthreads();   // the LDS is free (K loop or the previous round done)
+    if (wm == q) {
+#pragma unroll
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            const int col = acc_col<TL>(wn, j, lane);
+            ct[row * TL::TN + (((col >> 2) ^ sw(row)) << 2) + (col & 3)] = acc[i][j][r];
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pi = u * TL::NTH + t, row = pi / PPR, pc = pi % PPR;
+      const int trow = q * TL::WMR + row;
+      const float* rowp = ct + row * TL::TN;
+      if constexpr (PAIR) {
+        const int lc = 8 * pc, c0 = (lc >> 5) * 64 + (lc & 31);
+        if (trow < rows) {
+          float g[8], v[8];
+          get8(rowp, row, c0, g);
+          get8(rowp, row, c0 + 32, v);
+          f(trow, lc, g, v);
+        }
+      } else {
+        const int col = 8 * pc;
+        if (trow < rows && col < ncols) {
+          float v[8];
+          get8(rowp, row, col, v);
+          f(trow, col, v);
+        }
+      }
+    }
+  }
+}
+
 // FC1 + SwiGLU: [a | b] = A W1^T with gate rows -> a, up rows -> b; writes a, b
 // (bf16, [rows][2I]: a at column j, b at I + j) and h = silu(a) * b (bf16, [rows][I]).
 // The B tile interleaves 32 gate rows and 32 up rows, so a wave's accumulator blocks
@@ -707,27 +773,31 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int I = p.I;
   const float L = p.limit;
+  tok_epilogue<TL, true>(acc, lds, tt.rows, TL::TN, [&](int row, int lc, const float* ga, const float* ub) {
+    const int jj = tt.nt * (TL::TN / 2) + lc;
+    const int64_t R = crow0 + row;
+    uint32_t aw[4], bw[4], hw[4];
 #pragma unroll
-  for (int jp = 0; jp < TL::NJ / 2; ++jp) {
-    const int jj = tt.nt * (TL::TN / 2) + (wn * TL::NJ / 2 + jp) * 32 + (lane & 31);
+    for (int k = 0; k < 8; k += 2) {
+      float hv[2];
 #pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<TL>(wm, i, r, lane);
-        if (row >= tt.rows) continue;
-        const float a = acc[i][2 * jp][r], b = acc[i][2 * jp + 1][r];
-        const int64_t R = crow0 + row;
-        p.ab[R * 2 * I + jj] = (uint16_t)f2bf(a);       // stored unclamped
-        p.ab[R * 2 * I + I + jj] = (uint16_t)f2bf(b);
+      for (int e = 0; e < 2; ++e) {
+        const float a = ga[k + e], b = ub[k + e];
         // clamp decided on the stored (BF16) pre-activations, as the backward sees them
         const bool a_hi = L > 0.0f && bf2f(f2bf(a)) > L;
         const bool b_out = L > 0.0f && fabsf(bf2f(f2bf(b))) > L;
         const float ac = a_hi ? L : a;
         const float bc = b_out ? copysignf(L, b) : b;
-        p.h[R * I + jj] = (uint16_t)f2bf(ac * sigmoidf_(ac) * bc);
+        hv[e] = ac * sigmoidf_(ac) * bc;
       }
-  }
+      aw[k / 2] = pack_bf2(ga[k], ga[k + 1]);   // stored unclamped
+      bw[k / 2] = pack_bf2(ub[k], ub[k + 1]);
+      hw[k / 2] = pack_bf2(hv[0], hv[1]);
+    }
+    *reinterpret_cast<uint4*>(p.ab + R * 2 * I + jj) = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+    *reinterpret_cast<uint4*>(p.ab + R * 2 * I + I + jj) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+    *reinterpret_cast<uint4*>(p.h + R * I + jj) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  });
 }
 
 // Plain token-dim GEMM with bf16 store: C[rows][N] = A[rows][K] * B, where B is either
@@ -811,17 +881,10 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::M
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int N = p.N;
-  if (wn * TL::WNC >= ncols) return;
-#pragma unroll
-  for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < TL::NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<TL>(wm, i, r, lane);
-        if (row >= tt.rows || acc_col<TL>(wn, j, lane) >= ncols) continue;
-        p.c[(crow0 + row) * N + n0 + acc_col<TL>(wn, j, lane)] = (uint16_t)f2bf(acc[i][j][r]);
-      }
+  tok_epilogue<TL, false>(acc, lds, tt.rows, ncols, [&](int row, int col, const float* v) {
+    *reinterpret_cast<uint4*>(p.c + (crow0 + row) * N + n0 + col) =
+        make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+  });
 }
 
 // Data gradient of FC2 fused with the SwiGLU backward: gh = dyw W2 (contracting over H,
@@ -880,31 +943,30 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
   }
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
-  if (wn * TL::WNC >= ncols) return;
+  const float L = p.limit;
+  tok_epilogue<TL, false>(acc, lds, tt.rows, ncols, [&](int row, int col, const float* gv) {
+    const int n = n0 + col;
+    const int64_t R = (crow0 + row) * 2 * (int64_t)I;
+    float av[8], bv[8];
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.ab + R + n), av);   // the stored BF16 a, b
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.ab + R + I + n), bv);
+    float da[8], db[8];
 #pragma unroll
-  for (int i = 0; i < TL::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < TL::NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row<TL>(wm, i, r, lane);
-        if (row >= tt.rows || acc_col<TL>(wn, j, lane) >= ncols) continue;
-        const int n = n0 + acc_col<TL>(wn, j, lane);
-        const int64_t R = (crow0 + row) * 2 * (int64_t)I;
-        const float a = bf2f(p.ab[R + n]);
-        const float b = bf2f(p.ab[R + I + n]);
-        const float gh = acc[i][j][r];
-        const float L = p.limit;
-        const bool a_hi = L > 0.0f && a > L;             // a, b: the stored BF16 values
-        const bool b_out = L > 0.0f && fabsf(b) > L;
-        const float ac = a_hi ? L : a;
-        const float bc = b_out ? copysignf(L, b) : b;
-        const float sg = sigmoidf_(ac);
-        const float da = a_hi ? 0.0f : gh * bc * (sg * (1.0f + ac * (1.0f - sg)));
-        const float db = b_out ? 0.0f : gh * (ac * sg);
-        p.dfc1[R + n] = (uint16_t)f2bf(da);
-        p.dfc1[R + I + n] = (uint16_t)f2bf(db);
-      }
+    for (int k = 0; k < 8; ++k) {
+      const float a = av[k], b = bv[k], gh = gv[k];
+      const bool a_hi = L > 0.0f && a > L;
+      const bool b_out = L > 0.0f && fabsf(b) > L;
+      const float ac = a_hi ? L : a;
+      const float bc = b_out ? copysignf(L, b) : b;
+      const float sg = sigmoidf_(ac);
+      da[k] = a_hi ? 0.0f : gh * bc * (sg * (1.0f + ac * (1.0f - sg)));
+      db[k] = b_out ? 0.0f : gh * (ac * sg);
+    }
+    *reinterpret_cast<uint4*>(p.dfc1 + R + n) =
+        make_uint4(pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3]), pack_bf2(da[4], da[5]), pack_bf2(da[6], da[7]));
+    *reinterpret_cast<uint4*>(p.dfc1 + R + I + n) =
+        make_uint4(pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3]), pack_bf2(db[4], db[5]), pack_bf2(db[6], db[7]));
+  });
 }
 
 // ---------------------------------------------------------------------------------
