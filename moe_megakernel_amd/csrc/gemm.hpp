@@ -515,9 +515,13 @@ __device__ __forceinline__ void zero_acc(Acc<TL>& acc) {
 // ---------------------------------------------------------------------------------
 // Token-dimension grouped tiles: group g < E is routed expert g with counts[g] rows
 // starting at offsets[g] of the permuted buffers; group E, when present, is the
-// shared expert with T rows.  tile_prefix[g] = sum of ceil(rows / BMT) over groups before g.  Linear
-// tiles are split into 8 contiguous chunks, chunk x run by the blocks with blockIdx % 8
-// == x (the blocks one XCD receives).  Inside a group the linear order walks bands of
+// shared expert with T rows.  tile_prefix[g] = sum of ceil(rows / BMT) over groups before g.
+// The blocks with blockIdx % 8 == x (the blocks one XCD receives) run one contiguous eighth
+// of the shared expert's linear tiles, then one contiguous eighth of the routed tiles.
+// Splitting the two kinds separately keeps the XCDs' work equal when a shared tile is
+// longer than a routed one (BF16 shared next to MXFP8 routed weights: twice the K stages),
+// and the shared tiles start first.  The grid holds at least ceil(tiles / 8) + 1 blocks
+// per XCD.  Inside a group the linear order walks bands of
 // kBandM m-tiles, column by column (m fastest), so the tiles resident on one XCD at a
 // time form a block of about kBandM m-tiles x (32 / kBandM) n-tiles: their A row panels
 // and B column panels are fetched into that XCD's L2 once per pass instead of the whole
@@ -540,12 +544,14 @@ __device__ __forceinline__ TokTile map_tok_tile(const int32_t* __restrict__ tile
   for (int i = threadIdx.x; i <= groups; i += blockDim.x) sp[i] = tile_prefix[i];
   __syncthreads();
   TokTile tt;
-  const int total = sp[groups] * ntn;
-  const int c = (total + 7) >> 3;
+  const int rt = sp[min(E, groups)] * ntn;         // routed tiles
+  const int st = sp[groups] * ntn - rt;            // shared tiles (0 without the shared expert)
   const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int L = x * c + j;
-  tt.ok = (j < c) && (L < total);
+  const int s0 = (int)((int64_t)st * x / 8), ns = (int)((int64_t)st * (x + 1) / 8) - s0;
+  const int r0 = (int)((int64_t)rt * x / 8), nr = (int)((int64_t)rt * (x + 1) / 8) - r0;
+  tt.ok = j < ns + nr;
   if (!tt.ok) return tt;
+  const int L = j < ns ? rt + s0 + j : r0 + (j - ns);
   const int mt = L / ntn;
   int lo = 0, hi = groups - 1;
   while (lo < hi) {

@@ -384,6 +384,9 @@ int64_t max_mtiles(const Dims& d) {
   return (d.SM + bm - 1) / bm + d.E + (d.hs ? (d.T + bm - 1) / bm : 0);
 }
 unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
+// token-dimension GEMM grid for at most n tiles: each XCD may receive one tile more than
+// an even split (the shared and routed tiles are split separately)
+unsigned tok_grid(int64_t n) { return grid8(n) + 8; }
 
 // Weight-gradient launch: the shared expert's tiles first (when present), then E groups
 // of routed tiles rounded up to a multiple of 8 blocks (one chunk per XCD).
@@ -454,8 +457,8 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   MOE_TRY(launch(again ? "recompute_fc1_swiglu" : "fc1_swiglu", st, [&] {
     using S1 = gemm::Shapes<true>::FC1;
     using S0 = gemm::Shapes<false>::FC1;
-    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, dim3(grid8(mt * (2 * I / S1::TN))), dim3(S1::NTH), 0, st, a1);
-    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, dim3(grid8(mt * (2 * I / S0::TN))), dim3(S0::NTH), 0, st, a1);
+    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, dim3(tok_grid(mt * (2 * I / S1::TN))), dim3(S1::NTH), 0, st, a1);
+    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, dim3(tok_grid(mt * (2 * I / S0::TN))), dim3(S0::NTH), 0, st, a1);
   }));
   if (d.mx) {   // Q: MXFP8 codes of the routed FC2 input h
     MOE_TRY(launch(again ? "recompute_quantize_h" : "quantize_h", st, [&] {
@@ -487,8 +490,8 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   MOE_TRY(launch(again ? "recompute_fc2" : "fc2", st, [&] {
     using S1 = gemm::Shapes<true>::FC2;
     using S0 = gemm::Shapes<false>::FC2;
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), dim3(grid8(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a2);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), dim3(grid8(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a2);
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a2);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a2);
   }));
   return MOE_OK;
 }
@@ -723,8 +726,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   MOE_TRY(launch("dgrad_fc2_swiglu", st, [&] {
     using S1 = gemm::Shapes<true>::DG2;
     using S0 = gemm::Shapes<false>::DG2;
-    if (d.mx) hipLaunchKernelGGL(gemm::k_dgrad_swiglu<true>, dim3(grid8(mt * ((I + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a3);
-    else hipLaunchKernelGGL(gemm::k_dgrad_swiglu<false>, dim3(grid8(mt * ((I + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a3);
+    if (d.mx) hipLaunchKernelGGL(gemm::k_dgrad_swiglu<true>, dim3(tok_grid(mt * ((I + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a3);
+    else hipLaunchKernelGGL(gemm::k_dgrad_swiglu<false>, dim3(tok_grid(mt * ((I + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a3);
   }));
   if (d.mx) {   // Q: MXFP8 codes of the routed FC1 data-gradient input dfc1
     MOE_TRY(launch("quantize_dfc1", st, [&] {
@@ -756,8 +759,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   MOE_TRY(launch("dgrad_fc1", st, [&] {
     using S1 = gemm::Shapes<true>::DG1;
     using S0 = gemm::Shapes<false>::DG1;
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, true>), dim3(grid8(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a4);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, false>), dim3(grid8(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a4);
+    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, true>), dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a4);
+    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, false>), dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a4);
   }));
 
   // B7 dx combine
