@@ -35,6 +35,7 @@ namespace gemm {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
@@ -1070,7 +1071,9 @@ __global__ __launch_bounds__(TL_WG<MG16>::NTH, TL_WG<MG16>::MINB) void k_wgrad(W
   // main_grad += acc, one slice of SR rows per round: the waves of the wave row holding
   // them park those accumulators in LDS, then every thread adds pieces of 4 elements of
   // whole rows to main_grad (coalesced row reads and writes).  The main_grad loads of a
-  // round are issued before its LDS traffic.  LDS slice [SR][TN] fp32; 16-byte chunk c of row r
+  // round are issued before its LDS traffic.  main_grad is read and written once per
+  // step, so its loads and stores are non-temporal: the stream does not evict the token
+  // operands that neighbouring tiles re-read from L2.  LDS slice [SR][TN] fp32; 16-byte chunk c of row r
   // sits at c ^ 8 ((r >> 2) & 1), so the two row groups a wave writes at once use
   // disjoint banks.
   constexpr int CPRW = TL::TN / 4;                       // 16-byte chunks per row
@@ -1095,10 +1098,10 @@ __global__ __launch_bounds__(TL_WG<MG16>::NTH, TL_WG<MG16>::MINB) void k_wgrad(W
       const uint8_t* src = cb + grow * ldc + cc * 4 * ES;
       const bool in = grow < mrows && 4 * cc < ncols;
       if constexpr (MG16) {
-        const uint2 v = in ? *reinterpret_cast<const uint2*>(src) : make_uint2(0, 0);
-        mg[u] = f32x4_t{lo_bf(v.x), hi_bf(v.x), lo_bf(v.y), hi_bf(v.y)};
+        const u32x2_t v = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src)) : u32x2_t{};
+        mg[u] = f32x4_t{lo_bf(v[0]), hi_bf(v[0]), lo_bf(v[1]), hi_bf(v[1])};
       } else {
-        mg[u] = in ? *reinterpret_cast<const f32x4_t*>(src) : f32x4_t{};
+        mg[u] = in ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src)) : f32x4_t{};
       }
     }
     __syncthreads();   // the LDS slice is free (K loop or previous round done)
@@ -1130,9 +1133,9 @@ __global__ __launch_bounds__(TL_WG<MG16>::NTH, TL_WG<MG16>::MINB) void k_wgrad(W
           f32x4_t r;
 #pragma unroll
           for (int k = 0; k < 4; ++k) r[k] = mg[u][k] + bf2f(f2bf(v[k]));
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3]));
+          __builtin_nontemporal_store(u32x2_t{pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3])}, reinterpret_cast<u32x2_t*>(dst));
         } else {
-          *reinterpret_cast<f32x4_t*>(dst) = mg[u] + v;
+          __builtin_nontemporal_store(mg[u] + v, reinterpret_cast<f32x4_t*>(dst));
         }
       }
     }
