@@ -758,8 +758,15 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
     if (!shared) {
       auto fa = [&](int r) { return p.mx.aq + (int64_t)tok[min(r, last)] * H; };
       auto fas = [&](int r) { return p.mx.as + (int64_t)tok[min(r, last)] * (H / 32); };
-      auto fb = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).data.row(e, brow(rr)); };
-      auto fbs = [&](int rr) { return (((rr >> 5) & 1) ? p.mx.b1 : p.mx.b0).scale.row(e, brow(rr)); };
+      // per-tile bases of the gate and up weights and scales
+      const uint8_t* gd = p.mx.b0.data.row(e, 0);
+      const uint8_t* ud = p.mx.b1.data.row(e, 0);
+      const uint8_t* gs = p.mx.b0.scale.row(e, 0);
+      const uint8_t* us = p.mx.b1.scale.row(e, 0);
+      const int64_t gdl = p.mx.b0.data.ld_bytes, udl = p.mx.b1.data.ld_bytes;
+      const int64_t gsl = p.mx.b0.scale.ld_bytes, usl = p.mx.b1.scale.ld_bytes;
+      auto fb = [&](int rr) { return ((rr >> 5) & 1) ? ud + brow(rr) * udl : gd + brow(rr) * gdl; };
+      auto fbs = [&](int rr) { return ((rr >> 5) & 1) ? us + brow(rr) * usl : gs + brow(rr) * gsl; };
       tile_mma<TL, KC, KC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb);
       done = true;
     }
@@ -855,15 +862,23 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::M
     auto fa = [&](int r) { return p.mx.aq + (arow0 + min(r, last)) * K; };
     auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (K / 32); };
     if constexpr (BMODE == KC) {
-      auto fb = [&](int r) { return p.mx.b0.data.row(e, n0 + min(r, nlast)); };
-      auto fbs = [&](int r) { return p.mx.b0.scale.row(e, n0 + min(r, nlast)); };
+      const uint8_t* d0 = p.mx.b0.data.row(e, n0);     // per-tile bases
+      const uint8_t* s0 = p.mx.b0.scale.row(e, n0);
+      const int64_t dl = p.mx.b0.data.ld_bytes, sl = p.mx.b0.scale.ld_bytes;
+      auto fb = [&](int r) { return d0 + min(r, nlast) * dl; };
+      auto fbs = [&](int r) { return s0 + min(r, nlast) * sl; };
       tile_mma<TL, KC, KC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb);
     } else {
       const int kbsplit = ksplit / 32;
-      auto fb = [&](int q) { return (q < ksplit ? p.mx.b0.data.row(e, q) : p.mx.b1.data.row(e, q - ksplit)) + n0; };
-      auto fbs = [&](int kb) {
-        return (kb < kbsplit ? p.mx.b0.scale.row(e, kb) : p.mx.b1.scale.row(e, kb - kbsplit)) + n0;
-      };
+      // per-tile bases of the two weight parts, so the loaders only add row offsets
+      const uint8_t* d0 = p.mx.b0.data.row(e, 0) + n0;
+      const uint8_t* d1 = p.mx.b1.data.row(e, 0) + n0;
+      const uint8_t* s0 = p.mx.b0.scale.row(e, 0) + n0;
+      const uint8_t* s1 = p.mx.b1.scale.row(e, 0) + n0;
+      const int64_t dl0 = p.mx.b0.data.ld_bytes, dl1 = p.mx.b1.data.ld_bytes;
+      const int64_t sl0 = p.mx.b0.scale.ld_bytes, sl1 = p.mx.b1.scale.ld_bytes;
+      auto fb = [&](int q) { return q < ksplit ? d0 + (int64_t)q * dl0 : d1 + (int64_t)(q - ksplit) * dl1; };
+      auto fbs = [&](int kb) { return kb < kbsplit ? s0 + (int64_t)kb * sl0 : s1 + (int64_t)(kb - kbsplit) * sl1; };
       tile_mma<TL, KC, RC, true>(acc, K, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb, ncols);
     }
   }
@@ -936,8 +951,11 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
     done = true;
     auto fa = [&](int r) { return p.mx.aq + (arow0 + min(r, last)) * H; };
     auto fas = [&](int r) { return p.mx.as + (arow0 + min(r, last)) * (H / 32); };
-    auto fb = [&](int k) { return p.mx.b0.data.row(e, k) + n0; };
-    auto fbs = [&](int kb) { return p.mx.b0.scale.row(e, kb) + n0; };
+    const uint8_t* d0 = p.mx.b0.data.row(e, 0) + n0;     // per-tile bases
+    const uint8_t* s0 = p.mx.b0.scale.row(e, 0) + n0;
+    const int64_t dl = p.mx.b0.data.ld_bytes, sl = p.mx.b0.scale.ld_bytes;
+    auto fb = [&](int k) { return d0 + (int64_t)k * dl; };
+    auto fbs = [&](int kb) { return s0 + (int64_t)kb * sl; };
     tile_mma<TL, KC, RC, true>(acc, H, fa, fb, fas, fbs, lds, sc, active, tt.rows, pfb, ncols);
   }
   if (!done) {
