@@ -90,6 +90,42 @@ def gemm_work(cfg, slots, shared=True, mg_bytes=4):
     }
 
 
+def row_work(cfg, slots, shared=True, gate=False):
+    """Algorithmic HBM bytes per launch of the row kernels (permute-, combine- and
+    quantise-type work, all HBM-bound): every row they read or write touched once.
+    S = valid routed slots, T = tokens; the routing indices and weights are included."""
+    E, H, I, T, K = cfg.experts, cfg.hidden, cfg.inter, cfg.tokens, cfg.topk
+    S, Ts = slots, (T if shared else 0)
+    idx = T * K * 8                                     # slot_of + router weights
+    w = {
+        "combine": (S + Ts + T) * 2 * H + idx + (2 * T * H if gate else 0),
+        "dx_combine": (S + Ts + T) * 2 * H + idx,
+        "gather_dy_dprob": 2 * H * T + 4 * H * S + 4 * E * T + idx + (4 * H * T if gate else 0),
+    }
+    if cfg.routed == "mxfp8":
+        w["gather_dy_dprob"] += S * (H + H // 32)
+        w["quantize_x"] = T * (2 * H + H + H // 32)
+        w["quantize_h"] = S * (2 * I + I + I // 32)
+        w["quantize_dfc1"] = S * (4 * I + 2 * I + 2 * I // 32)
+    return w
+
+
+def row_roofline(cfg, slots, ktimes, shared=True, gate=False):
+    """Per row kernel: achieved algorithmic GB/s from its live average launch time and the
+    fraction of the HBM peak."""
+    res = {}
+    for name, by in row_work(cfg, slots, shared, gate).items():
+        n_l, tot = ktimes.get(name, (0, 0.0))
+        if n_l == 0:
+            continue
+        ms = tot / n_l
+        ach = by / (ms * 1e-3) / 1e9
+        res[name] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "avg_launch_ms": round(ms, 4),
+                     "alg_bytes_per_launch": int(by)}
+    return res
+
+
 def mfma_peak(cfg, kernel, slots, shared=True):
     """Dense MFMA peak (TFLOP/s) for a GEMM kernel: BF16, or for the routed FP8 GEMMs of
     an MXFP8 layer the flop-weighted harmonic mix of the FP8 peak (routed rows) and the
@@ -281,6 +317,8 @@ def main():
         "roofline": roofline,
         "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in ktimes.items()},
         "kernels_roofline": {k: {"bound": v["bound"], "frac": v["frac"]} for k, v in krl.items()},
+        "row_kernels_hbm": {k: {"achieved_GBps": v["achieved"], "frac": v["frac"]}
+                            for k, v in row_roofline(cfg, slots, ktimes, shared, args.shared_gate).items()},
     }
     line["hbm_calibration"] = hbm_calibration()
     if not args.no_cpu_baseline:
