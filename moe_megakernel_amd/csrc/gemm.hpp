@@ -665,7 +665,7 @@ __device__ __forceinline__ void tok_epilogue(const Acc<TL>& acc, uint8_t* lds, i
   const int t = threadIdx.x, lane = t & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
   auto sw = [](int r) { return ((r >> 2) & 1) << 3; };
   auto get8 = [&](const float* rowp, int r, int c0, float* v) __attribute__((always_inline)) {
-    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(rowp + ((((c0 >> 2)) ^ sw(r)) << 2));
+    const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(rowp + (((c0 >> 2) ^ sw(r)) << 2));
     const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(rowp + ((((c0 >> 2) + 1) ^ sw(r)) << 2));
 #pragma unroll
     for (int k = 0; k < 4; ++k) { v[k] = x0[k]; v[4 + k] = x1[k]; }
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
   for (int i = threadIdx.x; i < tt.rows; i += TL::NTH)
     tok[i] = shared ? tt.m0 + i : p.slot_t[arow0 + i];
   __syncthreads();
-  const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  const int wm = wave_m<TL>();
   auto brow = [&](int rr) { return tt.nt * (TL::TN / 2) + (rr >> 6) * 32 + (rr & 31); };   // logical column
   Acc<TL> acc;
   zero_acc<TL>(acc);
@@ -852,7 +852,7 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::M
   const int ncols = min(TL::TN, p.N - n0);   // the last N tile may be partial (a multiple of 128)
   const int nlast = ncols - 1;
   const int ksplit = p.ksplit;
-  const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  const int wm = wave_m<TL>();
   Acc<TL> acc;
   zero_acc<TL>(acc);
   const bool active = wm * TL::WMR < tt.rows;
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
   const int H = p.H, I = p.I, last = tt.rows - 1;
   const int n0 = tt.nt * TL::TN;
   const int ncols = min(TL::TN, I - n0);   // the last N tile may be partial (a multiple of 128)
-  const int lane = threadIdx.x & 63, wm = wave_m<TL>(), wn = wave_n<TL>();
+  const int wm = wave_m<TL>();
   Acc<TL> acc;
   zero_acc<TL>(acc);
   const bool active = wm * TL::WMR < tt.rows;
@@ -1091,9 +1091,9 @@ __global__ __launch_bounds__(TL_WG<MG16>::NTH, TL_WG<MG16>::MINB) void k_wgrad(W
   // whole rows to main_grad (coalesced row reads and writes).  The main_grad loads of a
   // round are issued before its LDS traffic.  main_grad is read and written once per
   // step, so its loads and stores are non-temporal: the stream does not evict the token
-  // operands that neighbouring tiles re-read from L2.  LDS slice [SR][TN] fp32; 16-byte chunk c of row r
-  // sits at c ^ 8 ((r >> 2) & 1), so the two row groups a wave writes at once use
-  // disjoint banks.
+  // operands that neighbouring tiles re-read from L2.  LDS slice [SR][TN] fp32; 16-byte
+  // chunk c of row r sits at c ^ 8 ((r >> 2) & 1), so the two row groups a wave writes at
+  // once use disjoint banks.
   constexpr int CPRW = TL::TN / 4;                       // 16-byte chunks per row
   // rows per round: a wave row, or (when its slice does not fit the LDS) the largest
   // multiple of 32 rows that does

@@ -416,7 +416,7 @@ struct FwdPtrs {
 // names differ).
 moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, const moe_weights* w,
                            hipStream_t st, bool again) {
-  const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
+  const int T = (int)d.T, E = (int)d.E, H = (int)d.H, I = (int)d.I;
   // Q: MXFP8 codes of x, one row per token (the routed FC1 input; F3's gather is the
   // FC1 kernel's row addressing)
   if (d.mx) {
@@ -576,7 +576,7 @@ moe_status forward_impl(bool table, const moe_problem* p, const void* hidden, co
   const ActLayout A = d.rc ? F.act : L.act;
   auto U16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(AB + off); };
 
-  const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H, I = (int)d.I;
+  const int T = (int)d.T, E = (int)d.E, K = (int)d.K, H = (int)d.H;
   const int nch = (int)d.nchunks;
 
   // F1 compaction (or validation of the router's table), F2 histogram + scan + stable rank
