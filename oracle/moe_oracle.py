@@ -95,7 +95,7 @@ def main_grad_after(before: np.ndarray, dW: np.ndarray, dtype: str) -> np.ndarra
 
 
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
-    """OCP FP8 E4M3FN codes -> float64 (BASELINE workload: "FP8 E4M3 payload").
+    """OCP FP8 E4M3FN codes -> float64 (the payload format of MXFP8 weights).
 
     sign s, exponent field f (4 bits, bias 7), mantissa m (3 bits):
       f >= 1 : (-1)^s * 2^(f-7) * (1 + m/8)
