@@ -280,15 +280,12 @@ def swiglu_clamped(a, b, limit=0.0):
     activation_func_clamp_value to the backend as swiglu_limit; the pages give no
     formula): the gate pre-activation is clamped from above and the linear one to
     [-L, L] before the product, h = silu(min(a, L)) clamp(b, -L, L); a clamped input
-    passes no gradient (the bounds themselves pass it).  L = 0: no clamp.
-
-    Whether an input is clamped is decided on its BF16 rounding, the precision in which
-    the layer keeps the pre-activations for its backward; the values themselves stay
-    exact.  (The gradient jumps at the bound, so the decision must be taken the same way
-    everywhere.)"""
+    passes no gradient, an input on a bound still passes it (the gradient of a clamp
+    inside its closed bounds).  Whether an input is clamped is decided on its exact
+    value.  L = 0: no clamp."""
     if limit and limit > 0:
-        a_hi = bf16_round(a) > limit
-        b_out = np.abs(bf16_round(b)) > limit
+        a_hi = a > limit
+        b_out = np.abs(b) > limit
         ac = np.where(a_hi, limit, a)
         bc = np.where(b_out, np.sign(b) * limit, b)
         h = silu(ac) * bc

@@ -16,19 +16,14 @@ import torch.nn.functional as F
 def dense_forward(x, probs, rmap, shared, routed, gate=None, limit=0.0):
     """x [T,H]; probs, rmap [T,E]; shared = (W1 [2I,H], W2 [H,I]); routed = (W1 [E,2I,H], W2 [E,H,I]);
     gate: optional [H] weight of the shared output gate, sigmoid(x @ gate) per token;
-    limit > 0: the gate pre-activation clamped above and the linear one to [-limit, limit],
-    where its BF16 rounding is past the bound (torch.where on a mask taken without
-    gradient, so a clamped input passes none)."""
+    limit > 0: the gate pre-activation clamped above and the linear one to [-limit, limit]
+    (torch.clamp, whose gradient passes inside the closed bounds)."""
     def ffn(xx, w1, w2):
         I = w2.shape[1]
         gu = xx @ w1.t()
         a, b = gu[:, :I], gu[:, I:]
         if limit > 0:
-            with torch.no_grad():
-                a_hi = a.to(torch.bfloat16).to(a.dtype) > limit
-                b_out = b.to(torch.bfloat16).to(b.dtype).abs() > limit
-            a = torch.where(a_hi, torch.full_like(a, limit), a)
-            b = torch.where(b_out, torch.sign(b.detach()) * limit, b)
+            a, b = a.clamp(max=limit), b.clamp(min=-limit, max=limit)
         return (F.silu(a) * b) @ w2.t()
 
     out = ffn(x, *shared) if shared is not None else torch.zeros_like(x)

@@ -424,11 +424,16 @@ def test_swiglu_clamp_limits_reduce_to_closed_forms():
     bc = np.array([-0.5, 0.4, -0.4, 0.5, 0.1])
     assert np.allclose(h, ac * sig(ac) * bc, rtol=0, atol=1e-15)
     assert dha[4] == 0 and dha[3] != 0      # a = L still passes the gradient, a > L does not
-    # the decision is taken on the BF16 rounding: just above L but rounding to L is not clamped
-    eps = 0.5 * 2.0 ** -9                   # below half a BF16 ulp of 0.5
-    h2, dha2, _ = O.swiglu_clamped(np.array([0.5 + eps]), np.array([0.1]), 0.5)
-    assert dha2[0] != 0 and np.isclose(h2[0], (0.5 + eps) * sig(0.5 + eps) * 0.1, rtol=1e-15, atol=0)
     assert dhb[0] == 0 and dhb[3] == 0 and dhb[1] != 0
+    # the decision is taken on the exact value: the smallest step past L is clamped, L itself
+    # is not (torch.clamp's gradient passes inside the closed bounds)
+    up, dn = np.nextafter(0.5, 1.0), np.nextafter(-0.5, -1.0)
+    h2, dha2, dhb2 = O.swiglu_clamped(np.array([up, 0.5]), np.array([dn, -0.5]), 0.5)
+    assert dha2[0] == 0 and dha2[1] != 0 and dhb2[0] == 0 and dhb2[1] != 0
+    assert h2[0] == h2[1] == 0.5 * sig(0.5) * -0.5
+    # derivatives of the unclamped region are those of silu(a) b
+    assert np.allclose(dha[:4], bc[:4] * O.dsilu(a[:4]), rtol=1e-15, atol=0)
+    assert np.allclose(dhb[1:3], a[1:3] * sig(a[1:3]), rtol=1e-15, atol=0)
 
 
 def test_e4m3_round_matches_torch_cast():
@@ -761,6 +766,48 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
         g = O.moe_backward(dy, x, probs, rmap, cfg.topk, W)
     except (ValueError, IndexError):
         return                                  # a shape error also exposes the mistake
+    errs = [_rel(out, ref["out"].numpy()), _rel(g["dx"], ref["dx"].numpy()),
+            _rel(g["dprobs"], ref["dprobs"].numpy())]
+    assert max(errs) > 1e-3, errs
+
+
+def _clamp_grad_leaks(a, b, limit=0.0):
+    h, _, dhb = _ORIG_CLAMP(a, b, limit)
+    return h, np.clip(b, -limit, limit) * O.dsilu(np.minimum(a, limit)), dhb   # no mask on a
+
+
+def _clamp_one_sided_b(a, b, limit=0.0):
+    ac = np.minimum(a, limit)
+    bc = np.minimum(b, limit)                   # the lower bound of the linear input dropped
+    return O.silu(ac) * bc, bc * O.dsilu(ac) * (a <= limit), O.silu(ac) * (b <= limit)
+
+
+def _clamp_ties_clamped(a, b, limit=0.0):
+    a_hi, b_out = a >= limit, np.abs(b) >= limit   # an input on a bound treated as clamped
+    ac = np.where(a_hi, limit, a)
+    bc = np.where(b_out, np.sign(b) * limit, b)
+    return O.silu(ac) * bc, bc * O.dsilu(ac) * ~a_hi, O.silu(ac) * ~b_out
+
+
+_ORIG_CLAMP = O.swiglu_clamped
+
+
+@pytest.mark.parametrize("mutant", ["grad_leaks", "one_sided_b", "ties_clamped"])
+def test_planted_clamp_mistakes_are_caught(monkeypatch, mutant):
+    """Each plausible mistake in the clamp fails its pins: the dense autograd form with
+    torch.clamp, or (for the decision at the bound itself) the closed forms."""
+    if mutant == "ties_clamped":
+        monkeypatch.setattr(O, "swiglu_clamped", _clamp_ties_clamped)
+        _, dha, dhb = O.swiglu_clamped(np.array([0.5]), np.array([-0.5]), 0.5)
+        assert dha[0] == 0 and dhb[0] == 0     # what the closed-form pin rejects
+        return
+    limit = 0.15
+    cfg, probs, rmap, x, dy, W, d = _small_problem(24, 64, 5, 3, 32, seed=25, short=0.2)
+    Wc = O.Weights(W.shared, W.routed, swiglu_limit=limit)
+    monkeypatch.setattr(O, "swiglu_clamped", _clamp_grad_leaks if mutant == "grad_leaks" else _clamp_one_sided_b)
+    out = O.moe_forward(x, probs, rmap, cfg.topk, Wc)
+    g = O.moe_backward(dy, x, probs, rmap, cfg.topk, Wc)
+    ref = dense_grads(d["x"], d["probs"], d["rmap"], d["shared"], d["routed"], d["dy"], limit=limit)
     errs = [_rel(out, ref["out"].numpy()), _rel(g["dx"], ref["dx"].numpy()),
             _rel(g["dprobs"], ref["dprobs"].numpy())]
     assert max(errs) > 1e-3, errs
