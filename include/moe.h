@@ -108,7 +108,9 @@ typedef struct {
                             review thread on the config port) without a formula; reading:
                             h = silu(min(a, L)) clamp(b, -L, L), a = gate and b = up
                             pre-activation, no gradient through a clamped input (the bounds
-                            themselves pass it).  NaN, negative or infinite: unsupported    */
+                            themselves pass it).  Whether an input is clamped is decided on
+                            its FP32 value in the forward.  NaN, negative or infinite:
+                            unsupported                                                      */
 } moe_problem;
 
 /* One logical matrix per expert, [rows][cols], row-major.  Exactly one of

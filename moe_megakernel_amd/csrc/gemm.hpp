@@ -727,7 +727,8 @@ struct Fc1Args {
   uint16_t* h;
   int H, I;
   float limit;   // SwiGLU clamp: h = silu(min(a, L)) clamp(b, -L, L) for L > 0, decided on
-                 // the BF16-rounded a and b (the values the backward reads)
+                 // the FP32 accumulator; a clamped input is stored as +-infinity in ab, which
+                 // tells the backward it was clamped
 };
 
 template <bool MX>
@@ -793,19 +794,23 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
     uint32_t aw[4], bw[4], hw[4];
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
-      float hv[2];
+      float hv[2], as[2], bs[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float a = ga[k + e], b = ub[k + e];
-        // clamp decided on the stored (BF16) pre-activations, as the backward sees them
-        const bool a_hi = L > 0.0f && bf2f(f2bf(a)) > L;
-        const bool b_out = L > 0.0f && fabsf(bf2f(f2bf(b))) > L;
+        // the clamp is decided here, on the FP32 accumulator; a clamped input is stored as
+        // +-infinity, so the backward reads the decision instead of taking it again on a
+        // rounded value
+        const bool a_hi = L > 0.0f && a > L;
+        const bool b_out = L > 0.0f && fabsf(b) > L;
         const float ac = a_hi ? L : a;
         const float bc = b_out ? copysignf(L, b) : b;
         hv[e] = ac * sigmoidf_(ac) * bc;
+        as[e] = a_hi ? __builtin_inff() : a;
+        bs[e] = b_out ? copysignf(__builtin_inff(), b) : b;
       }
-      aw[k / 2] = pack_bf2(ga[k], ga[k + 1]);   // stored unclamped
-      bw[k / 2] = pack_bf2(ub[k], ub[k + 1]);
+      aw[k / 2] = pack_bf2(as[0], as[1]);
+      bw[k / 2] = pack_bf2(bs[0], bs[1]);
       hw[k / 2] = pack_bf2(hv[0], hv[1]);
     }
     *reinterpret_cast<uint4*>(p.ab + R * 2 * I + jj) = make_uint4(aw[0], aw[1], aw[2], aw[3]);
@@ -912,7 +917,8 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::M
 // Data gradient of FC2 fused with the SwiGLU backward: gh = dyw W2 (contracting over H,
 // W2 [H][I] row-contiguous), then with the saved a, b:
 //   da = gh * b * silu'(a),  db = gh * silu(a)  -> dfc1 [rows][2I] (da at j, db at I + j)
-//   (with the clamp: a and b clamped first, and zero gradient through a clamped input).
+//   (with the clamp: a and b clamped first, and zero gradient through a clamped input;
+//   the forward stored each clamped input as +-infinity).
 // MX: routed tiles take E4M3 dyw and the columnwise E4M3 copy of W2.
 struct DgradSwigluArgs {
   TokArgs t;
@@ -923,7 +929,8 @@ struct DgradSwigluArgs {
   const uint16_t* ab;
   uint16_t* dfc1;
   int H, I;
-  float limit;   // SwiGLU clamp limit (0: none); no gradient flows through a clamped input
+  float limit;   // SwiGLU clamp limit (0: none); no gradient flows through a clamped input,
+                 // which the forward stored as +-infinity
 };
 
 template <bool MX>
@@ -979,8 +986,9 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float a = av[k], b = bv[k], gh = gv[k];
-      const bool a_hi = L > 0.0f && a > L;
-      const bool b_out = L > 0.0f && fabsf(b) > L;
+      // the forward's clamp decisions: a clamped input was stored as +-infinity
+      const bool a_hi = L > 0.0f && a == __builtin_inff();
+      const bool b_out = L > 0.0f && __builtin_isinf(b);
       const float ac = a_hi ? L : a;
       const float bc = b_out ? copysignf(L, b) : b;
       const float sg = sigmoidf_(ac);
