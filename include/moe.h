@@ -240,6 +240,31 @@ moe_status moe_forward_topk(const moe_problem* p, const void* hidden, const int3
                             const float* router_weights, const moe_weights* w, void* out,
                             void* saved, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Forward that allocates nothing and takes no workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Arguments and results as for moe_forward (the dense routing map; with
+ * MOE_FLAG_TOPK_ROUTING it returns MOE_ERR_UNSUPPORTED), computed by the same kernels, so
+ * `out` and `saved` are bit-identical to moe_forward's.  The forward's scratch (the MXFP8
+ * codes and scales of the routed GEMM inputs, and in recompute mode the forward's
+ * activations: moe_workspace_bytes(p, 0) bytes) lives instead in one static device array
+ * of MOE_NOALLOC_SCRATCH_BYTES per GPU, which the library holds from its load until the
+ * process ends.
+ *  Limit: a problem whose forward workspace exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ *  MOE_ERR_WORKSPACE with nothing enqueued.  BF16 routed weights without recompute need no
+ *  scratch at any size; MXFP8 routed weights at 4096 tokens, hidden 4096, 96 experts,
+ *  top-4, intermediate 1024 need 35 MB.
+ *  Sharing: the array used is the current device's, on which `stream` must run.  Every call
+ *  on one GPU uses the same array, which keeps the last call's contents; nothing in it has
+ *  to start at zero (a kernel reads only bytes written earlier in the same call).  Calls
+ *  that overlap on one GPU (several streams or host threads) race on it: the caller
+ *  serialises them.
+ *  The first call on a device, once its arguments are valid, looks up the array's device
+ *  address (hipGetSymbolAddress) and keeps it; no call allocates or frees device memory. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_problem* p, const void* hidden, const float* probs,
+                               const uint8_t* routing_map, const moe_weights* w, void* out,
+                               void* saved, void* stream);
+
 /* Backward of sum(grad_out * out).
  *  grad_out     bf16  [T][H]
  *  hidden       the same bf16 [T][H] tensor given to moe_forward

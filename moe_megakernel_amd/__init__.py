@@ -26,7 +26,9 @@ MOE_FLAG_TOPK_ROUTING = 4
 MOE_FLAG_SHARED_GATE = 8
 
 EXPORTED = ("moe_saved_bytes", "moe_workspace_bytes", "moe_saved_view", "moe_forward",
-            "moe_forward_topk", "moe_backward", "moe_status_str", "moe_kernel_timer_enable", "moe_kernel_timer_read")
+            "moe_forward_topk", "moe_forward_noalloc", "moe_backward", "moe_status_str",
+            "moe_kernel_timer_enable", "moe_kernel_timer_read")
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class moe_problem(C.Structure):
@@ -90,6 +92,9 @@ def load(path: str | None = None):
     lib.moe_forward.restype = C.c_int
     lib.moe_forward_topk.argtypes = lib.moe_forward.argtypes
     lib.moe_forward_topk.restype = C.c_int
+    lib.moe_forward_noalloc.argtypes = [P(moe_problem), C.c_void_p, C.c_void_p, C.c_void_p, P(moe_weights),
+                                        C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.moe_forward_noalloc.restype = C.c_int
     lib.moe_backward.argtypes = [P(moe_problem), C.c_void_p, C.c_void_p, P(moe_weights), C.c_void_p,
                                  C.c_void_p, C.c_void_p, P(moe_main_grads), C.c_void_p, C.c_size_t,
                                  C.c_void_p]
@@ -136,6 +141,13 @@ def moe_forward(p, hidden, probs, routing_map, weights, out, saved, workspace, w
     """Raw call with integer device addresses; returns the status code."""
     return load().moe_forward(C.byref(p), hidden, probs, routing_map, C.byref(weights), out, saved,
                               workspace, workspace_bytes, stream)
+
+
+def moe_forward_noalloc(p, hidden, probs, routing_map, weights, out, saved, stream) -> int:
+    """Raw call of the allocation-free forward (its scratch is the library's static per-GPU
+    array); returns the status code."""
+    return load().moe_forward_noalloc(C.byref(p), hidden, probs, routing_map, C.byref(weights), out, saved,
+                                      stream)
 
 
 def moe_forward_topk(p, hidden, top_experts, router_weights, weights, out, saved, workspace, workspace_bytes,
@@ -223,6 +235,14 @@ class Layer:
                          _ptr(self.saved), _ptr(self.workspace), self.ws_bytes, current_stream())
         if st != MOE_OK:
             raise MoeError(st, "moe_forward")
+        return out
+
+    def forward_noalloc(self, hidden, probs, routing_map, weights: moe_weights, out):
+        """moe_forward_noalloc into this layer's `saved` (no workspace is passed)."""
+        st = moe_forward_noalloc(self.p, _ptr(hidden), _ptr(probs), _ptr(routing_map), weights, _ptr(out),
+                                 _ptr(self.saved), current_stream())
+        if st != MOE_OK:
+            raise MoeError(st, "moe_forward_noalloc")
         return out
 
     def forward_topk(self, hidden, top_experts, router_weights, weights: moe_weights, out):

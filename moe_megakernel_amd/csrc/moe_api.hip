@@ -499,6 +499,35 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
 
 }  // namespace
 
+// Scratch of the allocation-free forward (moe_forward_noalloc): one array per GPU, held
+// by that GPU from the library's load until the process ends.  In host code this name is
+// only a stand-in for the symbol, not a device address: host code reaches the memory
+// through the address scratch_address() looks up per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxScratchDevices] = {};
+
+// The device address of the current GPU's `scratch` array, looked up on the first call on
+// that GPU (with it current) and kept: every GPU holds its own copy at its own address.
+moe_status scratch_address(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    g_scratch[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
 // ================================================================== C ABI
 extern "C" {
 
@@ -548,11 +577,13 @@ moe_status moe_saved_view(const moe_problem* p, moe_saved_layout* out) {
 namespace {
 
 // Both forward entry points: the routing is the dense map + probabilities (rmap, probs),
-// or the router's fixed-width table (top_in, rw_in).
+// or the router's fixed-width table (top_in, rw_in).  noalloc: the workspace arguments are
+// unused and the forward's scratch is this GPU's static `scratch` array (looked up only
+// once every argument has passed validation).
 moe_status forward_impl(bool table, const moe_problem* p, const void* hidden, const float* probs,
                         const uint8_t* routing_map, const int32_t* top_in, const float* rw_in,
                         const moe_weights* w, void* out, void* saved, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool noalloc = false) {
   MOE_TRY(check_problem(p));
   if (((p->flags & MOE_FLAG_TOPK_ROUTING) != 0) != table) return MOE_ERR_UNSUPPORTED;
   MOE_TRY(check_weights(p, w));
@@ -561,10 +592,19 @@ moe_status forward_impl(bool table, const moe_problem* p, const void* hidden, co
   if (d.T > 0 && (!hidden || !have_routing || !out)) return MOE_ERR_NULL;
   if (!saved) return MOE_ERR_WORKSPACE;
   const FwdLayout F = fwd_layout(d);
-  if (workspace_bytes < F.total || !workspace) return MOE_ERR_WORKSPACE;
+  if (noalloc) {
+    if (F.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  } else if (workspace_bytes < F.total || !workspace) {
+    return MOE_ERR_WORKSPACE;
+  }
   if ((hidden && !aligned16(hidden)) || (out && !aligned16(out)) || !aligned16(saved) ||
-      !aligned16(workspace))
+      (!noalloc && !aligned16(workspace)))
     return MOE_ERR_LAYOUT;
+  if (noalloc) {
+    uint8_t* sp = nullptr;
+    MOE_TRY(scratch_address(&sp));
+    workspace = sp;
+  }
   uint8_t* WS = static_cast<uint8_t*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const SavedLayout L = saved_layout(d);
@@ -630,6 +670,13 @@ moe_status moe_forward(const moe_problem* p, const void* hidden, const float* pr
                        void* workspace, size_t workspace_bytes, void* stream) {
   return forward_impl(false, p, hidden, probs, routing_map, nullptr, nullptr, w, out, saved, workspace,
                       workspace_bytes, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_problem* p, const void* hidden, const float* probs,
+                               const uint8_t* routing_map, const moe_weights* w, void* out, void* saved,
+                               void* stream) {
+  return forward_impl(false, p, hidden, probs, routing_map, nullptr, nullptr, w, out, saved, nullptr, 0,
+                      stream, true);
 }
 
 moe_status moe_forward_topk(const moe_problem* p, const void* hidden, const int32_t* top_experts,

@@ -267,3 +267,23 @@ def test_shared_gate_validation():
     q = _ok_problem()
     assert mk.moe_workspace_bytes(p, 1) > mk.moe_workspace_bytes(q, 1)
     assert mk.moe_saved_bytes(p) > mk.moe_saved_bytes(q)
+
+
+def test_noalloc_forward_validation():
+    """moe_forward_noalloc validates like moe_forward and rejects a problem whose forward
+    scratch exceeds its static array, all on the host before any HIP call."""
+    a = 1 << 41
+    p = _ok_problem()
+    w = _fake_weights(p)
+    assert mk.moe_forward_noalloc(p, 0, a, a, w, a, a, 0) == mk.MOE_ERR_NULL
+    assert mk.moe_forward_noalloc(p, a, a, a, w, a, 0, 0) == mk.MOE_ERR_WORKSPACE      # no saved buffer
+    q = _ok_problem()
+    q.flags |= mk.MOE_FLAG_TOPK_ROUTING
+    assert mk.moe_forward_noalloc(q, a, a, a, w, a, a, 0) == mk.MOE_ERR_UNSUPPORTED
+    big = _ok_problem(tokens=1 << 16)
+    big.flags |= mk.MOE_FLAG_RECOMPUTE                       # activations in the forward scratch
+    assert mk.moe_workspace_bytes(big, 0) > mk.MOE_NOALLOC_SCRATCH_BYTES
+    assert mk.moe_forward_noalloc(big, a, a, a, _fake_weights(big), a, a, 0) == mk.MOE_ERR_WORKSPACE
+    assert mk.moe_forward_noalloc(_ok_problem(hidden=100), a, a, a, w, a, a, 0) == mk.MOE_ERR_SHAPE
+    mx = mk.problem(4096, 4096, 1024, 96, 4, mk.MOE_MXFP8_E4M3)   # the 4096-token MXFP8 layer fits
+    assert mk.moe_workspace_bytes(mx, 0) <= mk.MOE_NOALLOC_SCRATCH_BYTES
