@@ -8,10 +8,13 @@ One step = moe_forward + moe_backward over one batch of seeded synthetic input
 backward with FP32 main_grad accumulation and the dense probability gradient).
 Inputs are resident in HBM before the timed region.  Prints one JSON line.
 
-Throughput is algorithmic TFLOPS: 18 * H * I * (S + T) flops per step, S = valid
-routed slots, T = tokens (shared expert; 0 with --routed-only).  The roofline object describes the
-dominant kernel, timed live with HIP events on the stream it runs on; the
-cpu_baseline object times the CPU oracle on a bounded sample of the same workload.
+The step time is the median of K per-step times (HIP events on the layer's stream between
+consecutive steps, after W warm-up steps; 50 and 10 by default).  Throughput is
+algorithmic TFLOPS: 18 * H * I * (S + T) flops per step, S = valid routed slots, T =
+tokens (shared expert; 0 with --routed-only).  Per-kernel times come from a second timed
+pass of K steps with the library's kernel timer on; the roofline object describes the
+dominant kernel from them.  The cpu_baseline object times the CPU oracle on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -32,8 +35,8 @@ MFMA_PEAK = {"bf16": 2516.6, "mxfp8": 5033.2}   # dense TFLOP/s, MI355X
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2,
                     help="workload index (2: 4096-token BF16 layer; 3: its MXFP8 form; 4: 8192-token "
                          "MXFP8 layer; 5, 6: one GPU's 6-expert share of layer 2 / 3 under 16-way EP)")
@@ -206,6 +209,17 @@ def hbm_calibration():
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, dp, n_tokens, shared=True):
     """The oracle, as it stands, on the first n_tokens tokens of the same workload
     (forward + backward incl. every routed expert's and the shared expert's weight
@@ -227,7 +241,7 @@ def cpu_baseline(cfg, dp, n_tokens, shared=True):
     flops = 18.0 * cfg.hidden * cfg.inter * (s + (n if shared else 0))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOPS", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus_visible": len(os.sched_getaffinity(0)),
             "sample": f"first {n} of {cfg.tokens} tokens ({s} routed slots), fp64 numpy oracle, "
                       f"forward+backward incl. all weight gradients; {dt:.1f} s"}
 
@@ -272,18 +286,33 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    mk.moe_kernel_timer_read()                      # drop warmup records
-    mk.moe_kernel_timer_enable(True)
+    # Headline: K steps, synchronised on both sides, an event on the layer's stream between
+    # consecutive steps; the step time is the median of the K per-step times.  No per-kernel
+    # event is recorded in this region.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    for i in range(args.steps):
+        evs[i].record()
+        step()
+    evs[-1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms = float(np.median(per_step))
+    # Per-kernel times: a second timed pass of K steps with the library's kernel timer (HIP
+    # events around every launch, on the stream the kernels run on).
+    mk.moe_kernel_timer_read()                      # drop earlier records
+    mk.moe_kernel_timer_enable(True)
+    torch.cuda.synchronize()
+    t_k = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+    elapsed_k = time.perf_counter() - t_k
     mk.moe_kernel_timer_enable(False)
     ktimes = mk.moe_kernel_timer_read()
 
-    ms = elapsed / args.steps * 1e3
     slots = dp.slots
     n_shared = cfg.tokens if shared else 0
     flops = 18.0 * cfg.hidden * cfg.inter * (slots + n_shared)
@@ -305,6 +334,9 @@ def main():
         "metric": "MoE layer fwd+bwd TFLOPS and % of MFMA peak, 4096 tokens, 1 GPU",
         "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "ms_per_step_stats": {"median": round(ms, 4), "mean": round(elapsed / args.steps * 1e3, 4),
+                              "min": round(per_step[0], 4), "max": round(per_step[-1], 4),
+                              "kernel_timer_pass_mean": round(elapsed_k / args.steps * 1e3, 4)},
         "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "mfma_peak_frac": round(mfma_frac, 4),
         "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden,

@@ -78,14 +78,14 @@ typedef enum { MOE_BF16 = 1, MOE_FP32 = 2, MOE_MXFP8_E4M3 = 3 } moe_dtype;
 #define MOE_FLAG_RECOMPUTE 2u
 /* Set: the routing arrives as the router's fixed-width table (top_experts and
  * router_weights, [T][K]), the form the runtime consumes (Megatron Core API docs,
- * mok.runtime, _MoKFunction.forward), through moe_forward_topk; moe_backward then writes
+ * mok.runtime, _MoKAutograd.forward), through moe_forward_topk; moe_backward then writes
  * grad_probs as [T][K].  Clear: the dense routing map and probabilities through
  * moe_forward. */
 #define MOE_FLAG_TOPK_ROUTING 4u
 /* Set (with MOE_FLAG_HAS_SHARED): the shared expert's output gate, MCore's optional
  * shared-expert output gate (PR #6572, Supported configurations) and the runtime's
  * shared_output_gate_weight argument (Megatron Core API docs, mok.runtime,
- * _MoKFunction.forward).  The pages give no formula; the reading implemented: a BF16
+ * _MoKAutograd.forward).  The pages give no formula; the reading implemented: a BF16
  * weight g [1][H] (moe_weights.shared_out_gate) and one score per token,
  * s_t = sigmoid(x_t . g), multiplying the shared expert's output:
  *     out[t] = s_t shared(x_t) + sum_k w_tk expert_{e_tk}(x_t)
@@ -199,8 +199,25 @@ typedef struct {
   size_t offsets;         /* int32 [E+1], exclusive prefix sum of counts                     */
   size_t slot_of;         /* int32 [T][K], slot of route (t,k) in expert-major order, -1 pad */
   size_t slot_token;      /* int32 [T*K], t*K+k of the route at each slot (first S valid)    */
-  size_t status_word;     /* int32, 0 or MOE_ERR_ROUTE_OVERFLOW                              */
+  size_t status_word;     /* int32: 0, MOE_ERR_ROUTE_OVERFLOW, or (moe_forward_topk)
+                             MOE_ERR_ROUTE_INVALID                                          */
 } moe_saved_layout;
+
+/* Byte offsets of the MXFP8 activation codes and E8M0 scales inside the workspaces, the
+ * inputs the routed FP8 GEMMs are given (for tests that read them back).  Forward workspace
+ * (moe_workspace_bytes(p, 0)): x_codes [T][H] and x_scales [T][H/32] (one row per token),
+ * h_codes [T*K][I] and h_scales [T*K][I/32] (one row per slot).  Backward workspace:
+ * dy_codes [T*K][H] and dy_scales [T*K][H/32] (the BF16 w_tk dy[t] of each slot),
+ * dfc1_codes [T*K][2I] and dfc1_scales [T*K][2I/32].  Slot rows at or past the number of
+ * valid slots hold nothing.  Blocks of 32 run along the rows; each code is the E4M3
+ * rounding (to nearest even) of value * 2^-e, e the smallest exponent in [-127, 127] that
+ * brings the block's largest magnitude to at most 448, stored as e + 127.  Returns
+ * MOE_ERR_UNSUPPORTED for BF16 routed weights (no staging exists). */
+typedef struct {
+  size_t x_codes, x_scales, h_codes, h_scales;
+  size_t dy_codes, dy_scales, dfc1_codes, dfc1_scales;
+} moe_mx_staging_layout;
+moe_status moe_mx_staging_view(const moe_problem* p, moe_mx_staging_layout* layout);
 
 /* Bytes of the forward->backward context for this problem (0 on invalid input). */
 size_t moe_saved_bytes(const moe_problem* p);

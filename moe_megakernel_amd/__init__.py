@@ -27,7 +27,7 @@ MOE_FLAG_SHARED_GATE = 8
 
 EXPORTED = ("moe_saved_bytes", "moe_workspace_bytes", "moe_saved_view", "moe_forward",
             "moe_forward_topk", "moe_forward_noalloc", "moe_backward", "moe_status_str",
-            "moe_kernel_timer_enable", "moe_kernel_timer_read")
+            "moe_kernel_timer_enable", "moe_kernel_timer_read", "moe_mx_staging_view")
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -68,6 +68,11 @@ class moe_saved_layout(C.Structure):
                                           "slot_of", "slot_token", "status_word")]
 
 
+class moe_mx_staging_layout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in ("x_codes", "x_scales", "h_codes", "h_scales",
+                                          "dy_codes", "dy_scales", "dfc1_codes", "dfc1_scales")]
+
+
 _lib = None
 
 
@@ -105,6 +110,8 @@ def load(path: str | None = None):
     lib.moe_kernel_timer_enable.restype = None
     lib.moe_kernel_timer_read.argtypes = [P(C.c_char_p), P(C.c_int), P(C.c_double), C.c_int]
     lib.moe_kernel_timer_read.restype = C.c_int
+    lib.moe_mx_staging_view.argtypes = [P(moe_problem), P(moe_mx_staging_layout)]
+    lib.moe_mx_staging_view.restype = C.c_int
     if path is None:
         _lib = lib
     return lib
@@ -134,6 +141,14 @@ def moe_saved_view(p: moe_problem) -> moe_saved_layout:
     st = load().moe_saved_view(C.byref(p), C.byref(out))
     if st != MOE_OK:
         raise MoeError(st, "moe_saved_view")
+    return out
+
+
+def moe_mx_staging_view(p: moe_problem) -> moe_mx_staging_layout:
+    out = moe_mx_staging_layout()
+    st = load().moe_mx_staging_view(C.byref(p), C.byref(out))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_mx_staging_view")
     return out
 
 

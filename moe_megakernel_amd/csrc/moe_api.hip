@@ -572,6 +572,18 @@ moe_status moe_saved_view(const moe_problem* p, moe_saved_layout* out) {
   return MOE_OK;
 }
 
+moe_status moe_mx_staging_view(const moe_problem* p, moe_mx_staging_layout* out) {
+  MOE_TRY(check_problem(p));
+  if (!out) return MOE_ERR_NULL;
+  const Dims d = dims_of(p);
+  if (!d.mx) return MOE_ERR_UNSUPPORTED;
+  const FwdLayout F = fwd_layout(d);
+  const BwdLayout B = bwd_layout(d);
+  out->x_codes = F.xq; out->x_scales = F.xs; out->h_codes = F.hq; out->h_scales = F.hs;
+  out->dy_codes = B.dyq; out->dy_scales = B.dys; out->dfc1_codes = B.dfq; out->dfc1_scales = B.dfs;
+  return MOE_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void k_route_compact(
 }
 
 // Kernel 1 for a router that already produced the fixed-width table (the form the
-// runtime consumes: Megatron Core API docs, mok.runtime, _MoKFunction.forward takes
+// runtime consumes: Megatron Core API docs, mok.runtime, _MoKAutograd.forward takes
 // router_weights and top_experts): validation and the chunk histogram in one pass.
 // Thread (i, k) for the chunk's token i and route k.  An ID outside [-1, E) or an ID a
 // row lists twice marks the chunk invalid and is stored as -1 (weight 0), so every later

@@ -157,9 +157,10 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
 // output gate (gate_s non-null): dys[t] = s_t dy[t] (the shared expert's upstream
 // gradient) and dz[t] = s_t (1 - s_t) (dy[t] . y[shared_row0 + t]) (the gate logit's).
 // The dot products are reduced per thread in a fixed order, then across each wave by a
-// fixed butterfly, then across the waves in order.  With Q, w_tk * dy[t] is also
+// fixed butterfly, then across the waves in order.  With Q, the BF16 w_tk * dy[t] is also
 // quantised to MXFP8 along H into dyq / dysc (the A operand of the scaled-FP8
-// data-gradient GEMM).  One block per token.
+// data-gradient GEMM), as every other FP8 GEMM input is quantised from its BF16 tensor.
+// One block per token.
 template <bool Q>
 __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
     const uint16_t* __restrict__ dy, const uint16_t* __restrict__ y, int H, int E, int K,
@@ -227,9 +228,12 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_dy_dprob(
 #pragma unroll
         for (int i = 0; i < 8; ++i) wg[i] = w[k] * g[i];
         reinterpret_cast<uint4*>(dyw + (int64_t)s[k] * H)[c] = pack_bf8(wg);
-        if constexpr (Q) {
+        if constexpr (Q) {   // the MXFP8 codes of the BF16 values just stored
+          float wb[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wb[i] = bf2f(f2bf(wg[i]));
           uint2 q;
-          const uint32_t sc = mx_quantize8(wg, quad_max(absmax8(wg)), q);
+          const uint32_t sc = mx_quantize8(wb, quad_max(absmax8(wb)), q);
           reinterpret_cast<uint2*>(dyq + (int64_t)s[k] * H)[c] = q;
           if ((c & 3) == 0) dysc[(int64_t)s[k] * (H / 32) + (c >> 2)] = (uint8_t)sc;
         }

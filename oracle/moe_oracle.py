@@ -202,7 +202,7 @@ def compact_routing(routing_map: np.ndarray, probs: np.ndarray, topk: int):
 
 def check_table(top_experts: np.ndarray, num_experts: int) -> None:
     """A router's fixed-width table as the runtime consumes it (Megatron Core API docs,
-    mok.runtime, _MoKFunction.forward takes top_experts and router_weights): every entry
+    mok.runtime, _MoKAutograd.forward takes top_experts and router_weights): every entry
     is an expert ID in [0, E) or -1 for a missing route, and a row names an expert at
     most once (a token has one decision per expert, as in the dense map)."""
     for t, row in enumerate(np.asarray(top_experts)):
@@ -301,7 +301,7 @@ def shared_gate_score(x, g):
     Reading of the shared-output gate (named on the pages as MCore's optional
     shared-expert output gate, PR #6572 Supported configurations, and as the runtime's
     shared_output_gate_weight argument, Megatron Core API docs, mok.runtime,
-    _MoKFunction.forward; its formula is not given there): a weight vector g [H] whose
+    _MoKAutograd.forward; its formula is not given there): a weight vector g [H] whose
     sigmoid score per token scales the shared expert's output.
     """
     return 1.0 / (1.0 + np.exp(-(np.asarray(x, dtype=np.float64) @ g)))
