@@ -80,13 +80,18 @@ def gemm_work(cfg, slots, shared=True, mg_bytes=4):
     ns = 1 if shared else 0
     Rr, Rs = slots, ns * T
     R = Rr + Rs
-    q = 1 + 1 / 32 if cfg.routed == "mxfp8" else 2       # routed weight / FP8 GEMM input bytes
+    mx = cfg.routed == "mxfp8"
+    q = 1 + 1 / 32 if mx else 2                          # routed weight / FP8 GEMM input bytes
     w1 = E * 2 * I * H * q + ns * 2 * I * H * 2
     w2 = E * H * I * q + ns * H * I * 2
+    # MXFP8: FC1 also writes the routed rows' h codes + scales, the FC2 data gradient the
+    # routed rows' dfc1 codes + scales (the quantisation is fused into their epilogues)
+    hq = Rr * I * (1 + 1 / 32) if mx else 0
+    dfq = Rr * 2 * I * (1 + 1 / 32) if mx else 0
     return {
-        "fc1_swiglu": (4 * H * I * R, w1 + Rr * H * q + Rs * H * 2 + R * 3 * I * 2),
+        "fc1_swiglu": (4 * H * I * R, w1 + Rr * H * q + Rs * H * 2 + R * 3 * I * 2 + hq),
         "fc2": (2 * H * I * R, w2 + Rr * I * q + Rs * I * 2 + R * H * 2),
-        "dgrad_fc2_swiglu": (2 * H * I * R, w2 + Rr * H * q + Rs * H * 2 + R * 2 * I * 2 * 2),
+        "dgrad_fc2_swiglu": (2 * H * I * R, w2 + Rr * H * q + Rs * H * 2 + R * 2 * I * 2 * 2 + dfq),
         "dgrad_fc1": (4 * H * I * R, w1 + Rr * 2 * I * q + Rs * 2 * I * 2 + R * H * 2),
         "wgrad_fc1": (4 * H * I * R, wgrad_fc1_bytes(cfg, slots, mg_bytes, shared)),
         "wgrad_fc2": (2 * H * I * R, (E + ns) * H * I * 2 * mg_bytes + R * (H + I) * 2),
@@ -108,8 +113,6 @@ def row_work(cfg, slots, shared=True, gate=False):
     if cfg.routed == "mxfp8":
         w["gather_dy_dprob"] += S * (H + H // 32)
         w["quantize_x"] = T * (2 * H + H + H // 32)
-        w["quantize_h"] = S * (2 * I + I + I // 32)
-        w["quantize_dfc1"] = S * (4 * I + 2 * I + 2 * I // 32)
     return w
 
 

@@ -50,6 +50,28 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)w;
 }
 
+// Max over the 4 lanes 4q .. 4q + 3 (one 32-element MX block held as 4 pieces of 8).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  return fmaxf(v, __shfl_xor(v, 2));
+}
+
+// 8 floats of a 32-element block whose |max| is amax -> 8 E4M3 codes; returns the E8M0 byte.
+__device__ __forceinline__ uint32_t mx_quantize8(const float (&v)[8], float amax, uint2& q) {
+  const int e = mx_block_exp(amax);
+  const float inv = ldexpf(1.0f, -e);
+  q.x = pack_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  q.y = pack_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  return (uint32_t)(e + 127);
+}
+
+__device__ __forceinline__ float absmax8(const float (&v)[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
 __device__ __forceinline__ void unpack_bf16x8(const uint4& v, float* f) {
   f[0] = lo_bf(v.x); f[1] = hi_bf(v.x); f[2] = lo_bf(v.y); f[3] = hi_bf(v.y);
   f[4] = lo_bf(v.z); f[5] = hi_bf(v.z); f[6] = lo_bf(v.w); f[7] = hi_bf(v.w);

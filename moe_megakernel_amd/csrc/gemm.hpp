@@ -725,6 +725,8 @@ struct Fc1Args {
   MxOperands mx;        // b0 = gate, b1 = up
   uint16_t* ab;
   uint16_t* h;
+  uint8_t* hq;   // MXFP8 routed tiles: E4M3 codes [rows][I] and E8M0 scales [rows][I/32] of the
+  uint8_t* hs;   // BF16 h just stored (blocks of 32 along I), the FC2 input
   int H, I;
   float limit;   // SwiGLU clamp: h = silu(min(a, L)) clamp(b, -L, L) for L > 0, decided on
                  // the FP32 accumulator; a clamped input is stored as +-infinity in ab, which
@@ -816,6 +818,18 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
     *reinterpret_cast<uint4*>(p.ab + R * 2 * I + jj) = make_uint4(aw[0], aw[1], aw[2], aw[3]);
     *reinterpret_cast<uint4*>(p.ab + R * 2 * I + I + jj) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
     *reinterpret_cast<uint4*>(p.h + R * I + jj) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    if constexpr (MX) {
+      if (!shared) {   // the routed FC2 input: MXFP8 codes of the BF16 h of these 8 columns; the
+                       // 4 lanes holding one 32-column block are adjacent (8 columns per lane)
+        float hb[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { hb[2 * k] = lo_bf(hw[k]); hb[2 * k + 1] = hi_bf(hw[k]); }
+        uint2 q;
+        const uint32_t sc = mx_quantize8(hb, quad_max(absmax8(hb)), q);
+        *reinterpret_cast<uint2*>(p.hq + R * I + jj) = q;
+        if ((jj & 31) == 0) p.hs[R * (I / 32) + jj / 32] = (uint8_t)sc;
+      }
+    }
   });
 }
 
@@ -928,6 +942,8 @@ struct DgradSwigluArgs {
   MxOperands mx;         // b0 = columnwise W2
   const uint16_t* ab;
   uint16_t* dfc1;
+  uint8_t* dfq;  // MXFP8 routed tiles: E4M3 codes [rows][2I] and E8M0 scales [rows][2I/32] of the
+  uint8_t* dfs;  // BF16 dfc1 just stored (blocks of 32 along 2I), the FC1 data-gradient input
   int H, I;
   float limit;   // SwiGLU clamp limit (0: none); no gradient flows through a clamped input,
                  // which the forward stored as +-infinity
@@ -995,10 +1011,29 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
       da[k] = a_hi ? 0.0f : gh * bc * (sg * (1.0f + ac * (1.0f - sg)));
       db[k] = b_out ? 0.0f : gh * (ac * sg);
     }
-    *reinterpret_cast<uint4*>(p.dfc1 + R + n) =
-        make_uint4(pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3]), pack_bf2(da[4], da[5]), pack_bf2(da[6], da[7]));
-    *reinterpret_cast<uint4*>(p.dfc1 + R + I + n) =
-        make_uint4(pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3]), pack_bf2(db[4], db[5]), pack_bf2(db[6], db[7]));
+    const uint4 dav = make_uint4(pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3]), pack_bf2(da[4], da[5]),
+                                 pack_bf2(da[6], da[7]));
+    const uint4 dbv = make_uint4(pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3]), pack_bf2(db[4], db[5]),
+                                 pack_bf2(db[6], db[7]));
+    *reinterpret_cast<uint4*>(p.dfc1 + R + n) = dav;
+    *reinterpret_cast<uint4*>(p.dfc1 + R + I + n) = dbv;
+    if constexpr (MX) {
+      if (!shared) {   // the routed FC1 data-gradient input: MXFP8 codes of the BF16 da and db
+                       // (the 4 lanes holding one 32-column block are adjacent)
+        float fa[8], fb[8];
+        unpack_bf16x8(dav, fa);
+        unpack_bf16x8(dbv, fb);
+        uint2 qa, qb;
+        const uint32_t sa = mx_quantize8(fa, quad_max(absmax8(fa)), qa);
+        const uint32_t sb = mx_quantize8(fb, quad_max(absmax8(fb)), qb);
+        *reinterpret_cast<uint2*>(p.dfq + R + n) = qa;
+        *reinterpret_cast<uint2*>(p.dfq + R + I + n) = qb;
+        if ((n & 31) == 0) {
+          p.dfs[R / 32 + n / 32] = (uint8_t)sa;
+          p.dfs[R / 32 + (I + n) / 32] = (uint8_t)sb;
+        }
+      }
+    }
   });
 }
 

@@ -421,8 +421,7 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   // FC1 kernel's row addressing)
   if (d.mx) {
     MOE_TRY(launch(again ? "recompute_quantize_x" : "quantize_x", st, [&] {
-      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, x, d.T, H, (const int32_t*)nullptr,
-                         P.xq, P.xs);
+      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, x, d.T, H, P.xq, P.xs);
     }));
   }
 
@@ -445,6 +444,8 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   a1.su = matref(w->shared_up, w->shared_up.data, 2);
   a1.ab = P.ab;
   a1.h = P.h;
+  a1.hq = P.hq;   // MXFP8: the epilogue also writes the FC2 input's codes (quantise step Q for h)
+  a1.hs = P.hs;
   a1.H = H; a1.I = I;
   a1.limit = d.L;
   a1.mx = gemm::MxOperands{};
@@ -460,12 +461,6 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
     if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, dim3(tok_grid(mt * (2 * I / S1::TN))), dim3(S1::NTH), 0, st, a1);
     else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, dim3(tok_grid(mt * (2 * I / S0::TN))), dim3(S0::NTH), 0, st, a1);
   }));
-  if (d.mx) {   // Q: MXFP8 codes of the routed FC2 input h
-    MOE_TRY(launch(again ? "recompute_quantize_h" : "quantize_h", st, [&] {
-      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, P.h, d.SM, I, P.offsets + E, P.hq,
-                         P.hs);
-    }));
-  }
 
   // F5 + F6: routed and shared FC2 -> y (unweighted)
   gemm::PlainArgs a2;
@@ -773,6 +768,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   a3.sd = matref(w->shared_down, w->shared_down.data, 2);
   a3.ab = U16(A.ab);
   a3.dfc1 = WU16(B.dfc1);
+  a3.dfq = W + B.dfq;   // MXFP8: the epilogue also writes the FC1 data-gradient input's codes (Q)
+  a3.dfs = W + B.dfs;
   a3.H = H; a3.I = I;
   a3.limit = d.L;
   a3.mx = gemm::MxOperands{};
@@ -788,12 +785,6 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
     if (d.mx) hipLaunchKernelGGL(gemm::k_dgrad_swiglu<true>, dim3(tok_grid(mt * ((I + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a3);
     else hipLaunchKernelGGL(gemm::k_dgrad_swiglu<false>, dim3(tok_grid(mt * ((I + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a3);
   }));
-  if (d.mx) {   // Q: MXFP8 codes of the routed FC1 data-gradient input dfc1
-    MOE_TRY(launch("quantize_dfc1", st, [&] {
-      hipLaunchKernelGGL(k_quantize_rows, dim3(2048), dim3(kRowThreads), 0, st, WU16(B.dfc1), d.SM, 2 * I,
-                         I32(L.offsets) + E, W + B.dfq, W + B.dfs);
-    }));
-  }
 
   // B3 (+B6): FC1 data gradient -> dxp (routed rows) and the shared rows
   gemm::PlainArgs a4;

@@ -19,28 +19,6 @@ __device__ __forceinline__ void load_slots(const int32_t* __restrict__ slot_of, 
   for (int k = 0; k < kMaxTopk; ++k) s[k] = (k < K) ? slot_of[(int64_t)t * K + k] : -1;
 }
 
-// Max over the 4 lanes 4q .. 4q + 3 (one 32-element MX block).
-__device__ __forceinline__ float quad_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  return fmaxf(v, __shfl_xor(v, 2));
-}
-
-// 8 floats of a 32-element block whose |max| is amax -> 8 E4M3 codes; returns the E8M0 byte.
-__device__ __forceinline__ uint32_t mx_quantize8(const float (&v)[8], float amax, uint2& q) {
-  const int e = mx_block_exp(amax);
-  const float inv = ldexpf(1.0f, -e);
-  q.x = pack_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-  q.y = pack_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-  return (uint32_t)(e + 127);
-}
-
-__device__ __forceinline__ float absmax8(const float (&v)[8]) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-  return m;
-}
-
 __device__ __forceinline__ uint4 pack_bf8(const float (&a)[8]) {
   uint4 o;
   o.x = pack_bf2(a[0], a[1]); o.y = pack_bf2(a[2], a[3]);
@@ -48,15 +26,13 @@ __device__ __forceinline__ uint4 pack_bf8(const float (&a)[8]) {
   return o;
 }
 
-// MXFP8 quantisation of bf16 rows along their length: payload [rows][cols] E4M3 and
-// scales [rows][cols/32] E8M0.  Rows at or beyond *row_limit (when given) are skipped:
-// the routed buffers hold offsets[E] valid rows.  One thread per 16-byte piece.
+// MXFP8 quantisation of bf16 rows along their length (the hidden states, the routed FC1
+// input): payload [rows][cols] E4M3 and scales [rows][cols/32] E8M0.  One thread per
+// 16-byte piece.  (h and dfc1 are quantised in the epilogues of the GEMMs that produce them.)
 __global__ __launch_bounds__(kRowThreads) void k_quantize_rows(
-    const uint16_t* __restrict__ in, int64_t rows, int cols, const int32_t* __restrict__ row_limit,
-    uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+    const uint16_t* __restrict__ in, int64_t rows, int cols, uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
   const int64_t nc = (int64_t)cols / 8;
-  const int64_t lim = row_limit ? (int64_t)*row_limit : rows;
-  const int64_t total = (lim < rows ? lim : rows) * nc;
+  const int64_t total = rows * nc;
   // the stride is a multiple of 4 pieces, so a block's 4 pieces stay on 4 adjacent lanes
   for (int64_t b = (int64_t)blockIdx.x * kRowThreads + threadIdx.x; b < total;
        b += (int64_t)gridDim.x * kRowThreads) {

@@ -46,7 +46,15 @@ def test_row_kernel_bytes_closed_form():
     assert "quantize_x" not in w
     mx = bench.row_work(gen.config(3), S)
     assert mx["gather_dy_dprob"] == w["gather_dy_dprob"] + S * (H + H // 32)
-    assert mx["quantize_h"] == S * (3 * cfg.inter + cfg.inter // 32)
+    assert mx["quantize_x"] == T * (3 * H + H // 32)
+    assert "quantize_h" not in mx and "quantize_dfc1" not in mx      # fused into the GEMM epilogues
+    g, g3 = bench.gemm_work(cfg, S), bench.gemm_work(gen.config(3), S)
+    I = cfg.inter
+    # the MXFP8 epilogues also write the routed rows' codes and scales of h and dfc1
+    assert g3["fc1_swiglu"][1] - g["fc1_swiglu"][1] == pytest.approx(
+        -(E * 2 * I * H + S * H) * (2 - 33 / 32) + S * I * 33 / 32)
+    assert g3["dgrad_fc2_swiglu"][1] - g["dgrad_fc2_swiglu"][1] == pytest.approx(
+        -(E * H * I + S * H) * (2 - 33 / 32) + S * 2 * I * 33 / 32)
 
 
 def test_roofline_picks_the_binding_bound():
