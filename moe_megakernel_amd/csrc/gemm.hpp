@@ -41,11 +41,14 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 
 
-template <int TM_, int TN_, int NWM_, int NWN_, int NS_, int MINB_, int PF_ = 0, int KB_ = 128>
+template <int TM_, int TN_, int NWM_, int NWN_, int NS_, int MINB_, int PF_ = 0, int KB_ = 128, int NSB_ = 0>
 struct Tile {
   static constexpr int TM = TM_, TN = TN_, NWM = NWM_, NWN = NWN_, NS = NS_, MINB = MINB_;
   static constexpr int PF = PF_;   // L2 prefetch distance in stages past the newest DMA stage (0: off)
   static constexpr int KB = KB_;   // K bytes per row per stage: 128, or 64 (BF16 only)
+  // Stages of the B operand in LDS: NS, or (BF16, NS = 2) three, so the B DMAs run one stage
+  // further ahead than the A DMAs.  The two operands have separate rings, A first.
+  static constexpr int NSB = NSB_ ? NSB_ : NS;
   static constexpr int NW = NWM * NWN, NTH = 64 * NW;
   static constexpr int WMR = TM / NWM, WNC = TN / NWN;   // rows / columns per wave
   static constexpr int MI = WMR / 32, NJ = WNC / 32;     // 32x32 blocks per wave
@@ -60,13 +63,14 @@ struct Tile {
   static constexpr int SCG = 8;                           // stages per scale group
   static constexpr int SCG_A = TM * 4 * SCG, SCG_B = TN * 4 * SCG;   // group buffer parts
   static constexpr int SC_RCB = 4 * TN;                   // RC B scales of one stage
-  static constexpr int LDS = NS * STAGE;
+  static constexpr int LDS = NS * A_BYTES + NSB * B_BYTES;
   static constexpr int SC_LDS = 2 * (SCG_A + SCG_B) + NS * SC_RCB;
   // L2 prefetch: one dword per 128-byte line of a stage (TM + TN lines), PF_N per wave
   static constexpr int PF_N = PF ? (TM + TN + NTH - 1) / NTH : 0;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
   static_assert(WMR % 32 == 0 && WNC % 32 == 0 && NS >= 2, "tile shape");
   static_assert(KB == 128 || (KB == 64 && PF == 0), "64-byte stages take no L2 prefetch");
+  static_assert(NSB == NS || (NSB == 3 && NS == 2 && PF == 0), "B ring one stage deeper than A");
 };
 
 template <class TL>
@@ -262,8 +266,9 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     }
   };
 
-  auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
-    const uint32_t sa = lds0 + slot * TL::STAGE, sb = sa + TL::A_BYTES;
+  // stage kt's A tile sits in A slot kt % NS, its B tile in B slot kt % NSB
+  auto issue_a = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t sa = lds0 + (kt % TL::NS) * TL::A_BYTES;
     const int k0 = kt * KST;
 #pragma unroll
     for (int i = 0; i < TL::A_DMA; ++i) {
@@ -275,6 +280,10 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
         dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fa(k)) + ca[i] : zp, m0v);
       }
     }
+  };
+  auto issue_b = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t sb = lds0 + TL::NS * TL::A_BYTES + (kt % TL::NSB) * TL::B_BYTES;
+    const int k0 = kt * KST;
 #pragma unroll
     for (int i = 0; i < TL::B_DMA; ++i) {
       const uint32_t m0v = sb + (w * TL::B_DMA + i) * 1024;
@@ -289,6 +298,12 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
         dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fb(row)) + cb[i] : zp, m0v);
       }
     }
+  };
+  // one whole stage (equal rings): A, B, then the stage's map, scale and prefetch loads
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const int slot = kt % TL::NS;
+    issue_a(kt);
+    issue_b(kt);
     if constexpr (BMAP) {
       if (bmap) map_issue(kt + 1);
     }
@@ -315,8 +330,8 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
   // ---- fragment reads and MFMAs of one stage
   auto compute = [&](int kt) __attribute__((always_inline)) {
     const int slot = kt % TL::NS;
-    const uint8_t* As = lds + slot * TL::STAGE;
-    const uint8_t* Bs = As + TL::A_BYTES;
+    const uint8_t* As = lds + slot * TL::A_BYTES;
+    const uint8_t* Bs = lds + TL::NS * TL::A_BYTES + (kt % TL::NSB) * TL::B_BYTES;
     const int g = lane >> 5, grp = lane >> 4, j16 = lane & 15;
     // Small wave tiles read all fragments of the stage first, so the LDS reads of later K
     // steps overlap the MFMAs of earlier ones; large ones (whose fragments would not fit
@@ -458,6 +473,9 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
   // ---- NS-stage pipeline, one barrier per stage.  At the top of step kt the wave's
   // DMAs of stage kt must have landed; those of the up to NS - 2 later stages may fly
   // (with PF, each stage's group of loads ends with its prefetch, which may fly too).
+  // With the deeper B ring, step kt issues A(kt + 1) and then B(kt + 2), so B's loads
+  // (the weight panel, the HBM-bound operand of the token GEMMs) get one more stage of
+  // lead than A's.
   if constexpr (BMAP) {
     if (bmap && nk > 0) {
       map_issue(0);
@@ -465,29 +483,51 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       __syncthreads();
     }
   }
+  static_assert(TL::NSB == TL::NS || (!FP8 && !BMAP), "deeper B ring: BF16 token GEMMs");
+  if constexpr (TL::NSB == TL::NS) {
 #pragma unroll
-  for (int s = 0; s < TL::NS - 1; ++s)
-    if (s < nk) issue(s, s);
+    for (int s = 0; s < TL::NS - 1; ++s)
+      if (s < nk) issue(s);
+  } else {
+    // B(0), A(0), B(1): at the top of step kt the newest loads are A(kt) and then B(kt + 1)
+    if (nk > 0) {
+      issue_b(0);
+      issue_a(0);
+    }
+    if (nk > 1) issue_b(1);
+  }
   // Two copies of the loop, so that skipping the MFMAs of an idle wave is not a branch
   // inside it (a conditional update would make the accumulators flow through a join
   // and cost a copy of every accumulator register per stage).
   auto run = [&](auto act) __attribute__((always_inline)) {
-    for (int kt = 0; kt < nk; ++kt) {
-      const int ahead = min(TL::NS - 2, nk - 1 - kt);
-      constexpr int TAIL = TL::PF_N;   // the prefetch that follows stage kt's DMAs
-      if constexpr (TL::NS >= 4) {
-        if (ahead >= 2) wait_vm<2 * LPS + TAIL>();
-        else if (ahead == 1) wait_vm<LPS + TAIL>();
-        else wait_vm<TAIL>();
-      } else if constexpr (TL::NS == 3) {
-        if (ahead >= 1) wait_vm<LPS + TAIL>();
-        else wait_vm<TAIL>();
-      } else {
-        wait_vm<TAIL>();
+    if constexpr (TL::NSB != TL::NS) {
+      for (int kt = 0; kt < nk; ++kt) {
+        // A(kt) and B(kt) must have landed; B(kt + 1), issued after A(kt), may fly
+        if (kt + 1 < nk) wait_vm<TL::B_DMA>();
+        else wait_vm<0>();
+        __syncthreads();
+        if (kt + 1 < nk) issue_a(kt + 1);
+        if (kt + 2 < nk) issue_b(kt + 2);
+        if constexpr (decltype(act)::value) compute(kt);
       }
-      __syncthreads();
-      if (kt + TL::NS - 1 < nk) issue(kt + TL::NS - 1, (kt + TL::NS - 1) % TL::NS);
-      if constexpr (decltype(act)::value) compute(kt);
+    } else {
+      for (int kt = 0; kt < nk; ++kt) {
+        const int ahead = min(TL::NS - 2, nk - 1 - kt);
+        constexpr int TAIL = TL::PF_N;   // the prefetch that follows stage kt's DMAs
+        if constexpr (TL::NS >= 4) {
+          if (ahead >= 2) wait_vm<2 * LPS + TAIL>();
+          else if (ahead == 1) wait_vm<LPS + TAIL>();
+          else wait_vm<TAIL>();
+        } else if constexpr (TL::NS == 3) {
+          if (ahead >= 1) wait_vm<LPS + TAIL>();
+          else wait_vm<TAIL>();
+        } else {
+          wait_vm<TAIL>();
+        }
+        __syncthreads();
+        if (kt + TL::NS - 1 < nk) issue(kt + TL::NS - 1);
+        if constexpr (decltype(act)::value) compute(kt);
+      }
     }
   };
   if (wave_active) run(std::true_type{});
@@ -588,17 +628,21 @@ struct MxOperands {
 
 // Tile shapes per kernel: TM, TN, waves along M, waves along N, LDS stages, the
 // workgroups per CU the register budget targets, L2 prefetch distance, K bytes per
-// stage.  BF16 and MXFP8 routed weights take separate shapes; within one of the two,
+// stage, LDS stages of the B operand (default: as many as A).  BF16 and MXFP8 routed weights take separate shapes; within one of the two,
 // every token-dimension GEMM has the same M tile (the routing scan builds one tile
 // prefix for it).
+// BF16 FC1, FC2 and FC2 data gradient: the weight panel gets a third LDS stage (at 4096
+// tokens over 96 experts each panel is read once, from HBM, and the extra stage of lead
+// hides more of its latency: 3-4% per kernel there, 1-3% slower with 2731 tokens per
+// expert, where the panels are L2 hits).
 #ifndef MOE_TL_FC1
-#define MOE_TL_FC1 192, 256, 2, 4, 2, 1
+#define MOE_TL_FC1 192, 256, 2, 4, 2, 1, 0, 128, 3
 #endif
 #ifndef MOE_TL_FC2
-#define MOE_TL_FC2 192, 256, 2, 4, 2, 1
+#define MOE_TL_FC2 192, 256, 2, 4, 2, 1, 0, 128, 3
 #endif
 #ifndef MOE_TL_DG2
-#define MOE_TL_DG2 192, 256, 2, 4, 2, 1
+#define MOE_TL_DG2 192, 256, 2, 4, 2, 1, 0, 128, 3
 #endif
 #ifndef MOE_TL_DG1
 #define MOE_TL_DG1 192, 256, 2, 4, 2, 1
