@@ -54,6 +54,9 @@ def parse():
                     help="the shared expert's output gate sigmoid(x . g) (its few flops are not counted)")
     ap.add_argument("--topk-input", action="store_true",
                     help="routing given as the router's fixed-width [T][K] table (moe_forward_topk)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="BF16 layers: also time the vendor BLAS (torch.mm / torch.bmm, hipBLASLt) on "
+                         "the same token-GEMM shapes with uniform expert batches, as a yardstick")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device-to-device copy before the steps (a known-size "
                          "reference for the HBM byte counters)")
@@ -249,6 +252,59 @@ def cpu_baseline(cfg, dp, n_tokens, shared=True):
                       f"forward+backward incl. all weight gradients; {dt:.1f} s"}
 
 
+def blas_shapes(cfg, slots, shared=True):
+    """The token GEMMs of one step as plain library GEMMs: per kernel a list of
+    (batch, M, K, N) products A[M,K] B[K,N], the routed experts as one batch of E products
+    of round(slots / E) rows each (uniform batches: the library has no grouped form with a
+    row map), the shared expert as one product of T rows.  No gather, no epilogue."""
+    E, H, I, T = cfg.experts, cfg.hidden, cfg.inter, cfg.tokens
+    m = max(1, round(slots / E))
+    kn = {"fc1_swiglu": (H, 2 * I), "fc2": (I, H), "dgrad_fc2_swiglu": (H, I), "dgrad_fc1": (2 * I, H)}
+    out = {}
+    for k, (K, N) in kn.items():
+        out[k] = [(E, m, K, N)] + ([(1, T, K, N)] if shared else [])
+    return out
+
+
+def blas_reference(cfg, slots, shared=True, reps=20):
+    """Median time of each token GEMM's library form (torch.bmm for the routed batch,
+    torch.mm for the shared rows; BF16, contiguous operands, FP32 accumulation inside the
+    library).  A yardstick for the grouped kernels, not part of the layer."""
+    import numpy as np
+    import torch
+    res = {}
+    for k, gemms in blas_shapes(cfg, slots, shared).items():
+        tot_ms, tot_fl, parts = 0.0, 0.0, []
+        for (B, M, K, N) in gemms:
+            a = torch.randn(B, M, K, device="cuda", dtype=torch.bfloat16)
+            b = torch.randn(B, K, N, device="cuda", dtype=torch.bfloat16)
+            if B == 1:
+                a2, b2 = a[0], b[0]
+                f = lambda: torch.mm(a2, b2)
+            else:
+                f = lambda: torch.bmm(a, b)
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                f()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = float(np.median(ts))
+            fl = 2.0 * B * M * K * N
+            parts.append({"batch": B, "M": M, "K": K, "N": N, "ms": round(ms, 4)})
+            tot_ms += ms
+            tot_fl += fl
+            del a, b
+        res[k] = {"ms": round(tot_ms, 4), "TFLOPS": round(tot_fl / (tot_ms * 1e-3) / 1e12, 1), "gemms": parts}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -356,6 +412,8 @@ def main():
                             for k, v in row_roofline(cfg, slots, ktimes, shared, args.shared_gate).items()},
     }
     line["hbm_calibration"] = hbm_calibration()
+    if args.blas_reference and cfg.routed == "bf16":
+        line["blas_reference"] = blas_reference(cfg, slots, shared)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, dp, args.cpu_sample_tokens, shared)
     print(json.dumps(line), flush=True)

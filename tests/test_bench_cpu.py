@@ -24,6 +24,21 @@ def test_gemm_flops_sum_to_the_layer_total():
     assert sum(f for f, _ in w0.values()) == 18 * cfg.hidden * cfg.inter * S
 
 
+@pytest.mark.parametrize("shared", [True, False])
+def test_blas_reference_shapes_carry_the_kernels_flops(shared):
+    # with S a multiple of E (every expert the same rows), the library GEMMs of each token
+    # kernel multiply exactly the flops the kernel is credited with
+    cfg = gen.config(5)
+    S = 16380                                # 6 experts x 2730 rows
+    shapes = bench.blas_shapes(cfg, S, shared)
+    w = bench.gemm_work(cfg, S, shared)
+    assert set(shapes) == {"fc1_swiglu", "fc2", "dgrad_fc2_swiglu", "dgrad_fc1"}
+    for k, gemms in shapes.items():
+        assert sum(2 * B * M * K * N for B, M, K, N in gemms) == w[k][0], k
+    # the 4096-token layer: 96 uniform products of round(16384 / 96) = 171 rows
+    assert bench.blas_shapes(gen.config(2), 16384)["fc1_swiglu"][0] == (96, 171, 4096, 2048)
+
+
 def test_wgrad_bytes_closed_form():
     # every FC1 main_grad element (E + 1 experts, 2I x H) read and written in FP32, plus the
     # bf16 dfc1 (2I) and input (H) rows of every slot and token read once
