@@ -52,7 +52,7 @@ struct Tile {
   static constexpr int NW = NWM * NWN, NTH = 64 * NW;
   static constexpr int WMR = TM / NWM, WNC = TN / NWN;   // rows / columns per wave
   static constexpr int MI = WMR / 32, NJ = WNC / 32;     // 32x32 blocks per wave
-  static constexpr int A_BYTES = TM * KB, B_BYTES = TN * KB, STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_BYTES = TM * KB, B_BYTES = TN * KB;
   static constexpr int A_DMA = A_BYTES / 1024 / NW;      // 1 KB DMA instructions per wave per stage
   static constexpr int B_DMA = B_BYTES / 1024 / NW;
   // MXFP8 scales (one E8M0 byte per 32 codes; a stage of 128 codes has 4 per row).  The
@@ -628,9 +628,9 @@ struct MxOperands {
 
 // Tile shapes per kernel: TM, TN, waves along M, waves along N, LDS stages, the
 // workgroups per CU the register budget targets, L2 prefetch distance, K bytes per
-// stage, LDS stages of the B operand (default: as many as A).  BF16 and MXFP8 routed weights take separate shapes; within one of the two,
-// every token-dimension GEMM has the same M tile (the routing scan builds one tile
-// prefix for it).
+// stage, LDS stages of the B operand (default: as many as A).  BF16 and MXFP8 routed
+// weights take separate shapes; within one of the two, every token-dimension GEMM has
+// the same M tile (the routing scan builds one tile prefix for it).
 // BF16 FC1, FC2 and FC2 data gradient: the weight panel gets a third LDS stage (at 4096
 // tokens over 96 experts each panel is read once, from HBM, and the extra stage of lead
 // hides more of its latency: 3-4% per kernel there, 1-3% slower with 2731 tokens per
