@@ -38,5 +38,26 @@ def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
     return out
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_caller", "moe_c_caller.c")
+C_CALLER = os.path.join(ROOT, "tests", "c_caller", "moe_c_caller")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_caller(lib: str = LIB, out: str = C_CALLER) -> str:
+    """The plain C test caller of the library (host code only, gcc): it links
+    libmoe_mi355x.so and the HIP runtime, and finds both through its run path."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
+           C_CALLER_SRC, "-o", out + ".tmp",
+           "-L", os.path.dirname(lib), "-lmoe_mi355x", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../moe_megakernel_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_caller())
