@@ -150,10 +150,16 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
   constexpr int LPS = TL::A_DMA + TL::B_DMA + TL::PF_N;
   static_assert(!FP8 || TL::NS == 2, "MXFP8 tiles use two stages");
   // BMAP: a row-contiguous B whose k-th row is source row bmap[k] (bmap null: row k).
-  // Stage kt's KST map entries are DMA'd into map_lds[(kt & 1) * 64 ..] by wave 0 with the
-  // stage before (two stages: every wait drains all loads, so the map has landed when the
-  // next issue reads it behind the barrier).
-  static_assert(!BMAP || (BMODE == RC && TL::NS == 2 && !FP8), "row-mapped B");
+  // Stage j's KST map entries go to map_lds[(j % MS) * 64 ..], MS = 2 NS - 2 slots, DMA'd
+  // by wave 0 as the last load of stage j - (NS - 1)'s group (maps 0 .. NS - 2 before the
+  // ring starts).  Stage j is issued at step j - (NS - 1), after that step's wait has
+  // drained stage j - (NS - 1)'s group and its barrier, so the map has landed and is
+  // visible.  The prologue's NS - 1 stage issues write maps NS - 1 .. 2 NS - 3 while other
+  // waves may still read maps 0 .. NS - 2 (no barrier between them), hence 2 NS - 2 slots;
+  // in the ring, step kt writes map kt + 2 NS - 2 over map kt, which the issue of step
+  // kt - NS + 1 read, before this step's barrier.
+  constexpr int MS = 2 * TL::NS - 2;
+  static_assert(!BMAP || (BMODE == RC && !FP8 && TL::KB / 2 <= 64), "row-mapped B");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w / TL::NWN, wn = w % TL::NWN;
@@ -262,7 +268,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       const int k = kt * KST + lane;
       const uint8_t* src = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
       if (lane < KST && k < kdim) src = reinterpret_cast<const uint8_t*>(bmap + k);
-      dma4(src, map0 + (kt & 1) * 256);
+      dma4(src, map0 + (kt % MS) * 256);
     }
   };
 
@@ -293,7 +299,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
         const int k = k0 + kb[i];
         int row = k;
         if constexpr (BMAP) {
-          if (bmap) row = map_lds[(kt & 1) * 64 + kb[i]];
+          if (bmap) row = map_lds[(kt % MS) * 64 + kb[i]];
         }
         dma16(k < kdim ? reinterpret_cast<const uint8_t*>(fb(row)) + cb[i] : zp, m0v);
       }
@@ -305,7 +311,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     issue_a(kt);
     issue_b(kt);
     if constexpr (BMAP) {
-      if (bmap) map_issue(kt + 1);
+      if (bmap) map_issue(kt + TL::NS - 1);
     }
     if constexpr (FP8) {
       if constexpr (BMODE == RC) {   // this stage's [4][TN] block of B scales
@@ -478,7 +484,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
   // lead than A's.
   if constexpr (BMAP) {
     if (bmap && nk > 0) {
-      map_issue(0);
+      for (int s = 0; s < TL::NS - 1; ++s) map_issue(s);
       wait_vm<0>();
       __syncthreads();
     }
@@ -662,6 +668,13 @@ struct MxOperands {
 #ifndef MOE_TL_WG
 #define MOE_TL_WG 128, 256, 2, 4, 2, 2, 0, 64
 #endif
+// FP32 main_grad, FC1, short token loops (few tokens per expert): a third 64-byte stage.
+// Two 72 KB workgroups still share a CU; 3% faster at 171 tokens per expert, where the
+// main_grad stream binds, 3-5% slower at 768 or 2731, hence only there.  (The FC2 kernel
+// with three stages needs 134 VGPRs and drops to one workgroup per CU.)
+#ifndef MOE_TL_WG_SHORT
+#define MOE_TL_WG_SHORT 128, 256, 2, 4, 3, 2, 0, 64
+#endif
 #ifndef MOE_TL_WG16
 #define MOE_TL_WG16 128, 128, 2, 2, 2, 4, 0, 64
 #endif
@@ -674,10 +687,12 @@ template <> struct Shapes<true> {
   using FC1 = Tile<MOE_TL_FC1_MX>; using FC2 = Tile<MOE_TL_FC2_MX>;
   using DG2 = Tile<MOE_TL_DG2_MX>; using DG1 = Tile<MOE_TL_DG1_MX>;
 };
-// weight gradients: FP32 main_grad (MG16 = false) and BF16 main_grad (true; half the
-// read-modify-write bytes per tile, so smaller tiles at higher occupancy win there)
-template <bool MG16>
-using TL_WG = typename std::conditional<MG16, Tile<MOE_TL_WG16>, Tile<MOE_TL_WG>>::type;
+// weight gradients: FP32 main_grad (MG16 = false; SHORT: the short-token-loop FC1 shape)
+// and BF16 main_grad (true; half the read-modify-write bytes per tile, so smaller tiles at
+// higher occupancy win there)
+template <bool MG16, bool SHORT = false>
+using TL_WG = typename std::conditional<
+    MG16, Tile<MOE_TL_WG16>, typename std::conditional<SHORT, Tile<MOE_TL_WG_SHORT>, Tile<MOE_TL_WG>>::type>::type;
 template <bool MX>
 constexpr int bm_of() { return Shapes<MX>::FC1::TM; }
 static_assert(Shapes<false>::FC2::TM == bm_of<false>() && Shapes<false>::DG2::TM == bm_of<false>() &&
@@ -1104,21 +1119,21 @@ struct WgradArgs {
   int N;
 };
 
-template <bool MG16>
+template <bool MG16, bool SHORT>
 __host__ __device__ inline int wgrad_tiles_per_group(int parts, int mpart, int N) {
-  using TL = TL_WG<MG16>;
+  using TL = TL_WG<MG16, SHORT>;
   return parts * ((mpart + TL::TM - 1) / TL::TM) * ((N + TL::TN - 1) / TL::TN);
 }
 
 // FC is 1 or 2 (which projection's gradient); it only names the kernel symbol apart.
 // MG16: BF16 main_grad (the contribution is rounded to BF16, then added with one BF16
 // rounding), else FP32.
-template <int FC, bool MG16>
-__global__ __launch_bounds__(TL_WG<MG16>::NTH, TL_WG<MG16>::MINB) void k_wgrad(WgradArgs p) {
-  using TL = TL_WG<MG16>;
+template <int FC, bool MG16, bool SHORT>
+__global__ __launch_bounds__((TL_WG<MG16, SHORT>::NTH), (TL_WG<MG16, SHORT>::MINB)) void k_wgrad(WgradArgs p) {
+  using TL = TL_WG<MG16, SHORT>;
   __shared__ __align__(16) uint8_t lds[TL::LDS];
   __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
-  __shared__ __align__(16) int32_t bmap_lds[FC == 1 ? 128 : 4];
+  __shared__ __align__(16) int32_t bmap_lds[FC == 1 ? 64 * (2 * TL::NS - 2) : 4];   // the map ring
   const int mtp = (p.mpart + TL::TM - 1) / TL::TM, ntn = (p.N + TL::TN - 1) / TL::TN;
   const int per = p.parts * mtp * ntn;
   const int nshared = p.has_shared ? per : 0;

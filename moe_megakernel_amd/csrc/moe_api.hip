@@ -390,16 +390,29 @@ unsigned tok_grid(int64_t n) { return grid8(n) + 8; }
 
 // Weight-gradient launch: the shared expert's tiles first (when present), then E groups
 // of routed tiles rounded up to a multiple of 8 blocks (one chunk per XCD).
-template <int FC, bool MG16>
+template <int FC, bool MG16, bool SHORT>
 void launch_wgrad_t(const gemm::WgradArgs& a, const Dims& d, hipStream_t st) {
-  const int per = gemm::wgrad_tiles_per_group<MG16>(a.parts, a.mpart, a.N);
+  const int per = gemm::wgrad_tiles_per_group<MG16, SHORT>(a.parts, a.mpart, a.N);
   const dim3 g((d.hs ? per : 0) + grid8((int64_t)d.E * per));
-  hipLaunchKernelGGL((gemm::k_wgrad<FC, MG16>), g, dim3(gemm::TL_WG<MG16>::NTH), 0, st, a);
+  constexpr unsigned nth = gemm::TL_WG<MG16, SHORT>::NTH;
+  hipLaunchKernelGGL((gemm::k_wgrad<FC, MG16, SHORT>), g, dim3(nth), 0, st, a);
 }
+// The FP32-main_grad FC1 weight gradient takes its short-token-loop shape when the routed
+// experts average at most this many slots (T K / E).
+constexpr int64_t kWgradShortSlots = 256;
 template <int FC>
 void launch_wgrad(const gemm::WgradArgs& a, const Dims& d, bool mg16, hipStream_t st) {
-  if (mg16) launch_wgrad_t<FC, true>(a, d, st);
-  else launch_wgrad_t<FC, false>(a, d, st);
+  if (mg16) {
+    launch_wgrad_t<FC, true, false>(a, d, st);
+    return;
+  }
+  if constexpr (FC == 1) {
+    if (d.SM <= kWgradShortSlots * d.E) {
+      launch_wgrad_t<FC, false, true>(a, d, st);
+      return;
+    }
+  }
+  launch_wgrad_t<FC, false, false>(a, d, st);
 }
 
 // Pointers of one run of the routed + shared expert forward (F3-F6).
