@@ -345,8 +345,9 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
     if constexpr (!FP8) {
       constexpr int NKS = KB / 32;   // 16-element K steps per stage
       // (the row-mapped instantiation sits at its register cap: reading every fragment of
-      // the stage ahead there spills)
-      constexpr bool PRE = NKS * (TL::MI + TL::NJ) * 4 <= 64 && !BMAP;
+      // the stage ahead there spills; a three-stage ring reads one K step at a time too, so
+      // that the weight gradients keep 128 VGPRs and two workgroups per CU)
+      constexpr bool PRE = NKS * (TL::MI + TL::NJ) * 4 <= 64 && !BMAP && TL::NS < 3;
       bf16x8_t a[NKS][TL::MI], b[NKS][TL::NJ];
       auto load = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
@@ -668,10 +669,9 @@ struct MxOperands {
 #ifndef MOE_TL_WG
 #define MOE_TL_WG 128, 256, 2, 4, 2, 2, 0, 64
 #endif
-// FP32 main_grad, FC1, short token loops (few tokens per expert): a third 64-byte stage.
-// Two 72 KB workgroups still share a CU; 3% faster at 171 tokens per expert, where the
-// main_grad stream binds, 3-5% slower at 768 or 2731, hence only there.  (The FC2 kernel
-// with three stages needs 134 VGPRs and drops to one workgroup per CU.)
+// FP32 main_grad, short token loops (few tokens per expert): a third 64-byte stage.  Two
+// 72 KB workgroups still share a CU; 3-5% faster at 171 tokens per expert, where the
+// main_grad stream binds, 3-5% slower at 768 or 2731, hence only there.
 #ifndef MOE_TL_WG_SHORT
 #define MOE_TL_WG_SHORT 128, 256, 2, 4, 3, 2, 0, 64
 #endif
@@ -687,7 +687,7 @@ template <> struct Shapes<true> {
   using FC1 = Tile<MOE_TL_FC1_MX>; using FC2 = Tile<MOE_TL_FC2_MX>;
   using DG2 = Tile<MOE_TL_DG2_MX>; using DG1 = Tile<MOE_TL_DG1_MX>;
 };
-// weight gradients: FP32 main_grad (MG16 = false; SHORT: the short-token-loop FC1 shape)
+// weight gradients: FP32 main_grad (MG16 = false; SHORT: the short-token-loop shape)
 // and BF16 main_grad (true; half the read-modify-write bytes per tile, so smaller tiles at
 // higher occupancy win there)
 template <bool MG16, bool SHORT = false>

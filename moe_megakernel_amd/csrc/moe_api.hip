@@ -397,22 +397,14 @@ void launch_wgrad_t(const gemm::WgradArgs& a, const Dims& d, hipStream_t st) {
   constexpr unsigned nth = gemm::TL_WG<MG16, SHORT>::NTH;
   hipLaunchKernelGGL((gemm::k_wgrad<FC, MG16, SHORT>), g, dim3(nth), 0, st, a);
 }
-// The FP32-main_grad FC1 weight gradient takes its short-token-loop shape when the routed
+// The FP32-main_grad weight gradients take their short-token-loop shape when the routed
 // experts average at most this many slots (T K / E).
 constexpr int64_t kWgradShortSlots = 256;
 template <int FC>
 void launch_wgrad(const gemm::WgradArgs& a, const Dims& d, bool mg16, hipStream_t st) {
-  if (mg16) {
-    launch_wgrad_t<FC, true, false>(a, d, st);
-    return;
-  }
-  if constexpr (FC == 1) {
-    if (d.SM <= kWgradShortSlots * d.E) {
-      launch_wgrad_t<FC, false, true>(a, d, st);
-      return;
-    }
-  }
-  launch_wgrad_t<FC, false, false>(a, d, st);
+  if (mg16) launch_wgrad_t<FC, true, false>(a, d, st);
+  else if (d.SM <= kWgradShortSlots * d.E) launch_wgrad_t<FC, false, true>(a, d, st);
+  else launch_wgrad_t<FC, false, false>(a, d, st);
 }
 
 // Pointers of one run of the routed + shared expert forward (F3-F6).
