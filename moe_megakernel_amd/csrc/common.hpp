@@ -15,20 +15,22 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> packed bfloat16 bits (lo in bits 0-15), round to nearest even, NaN stays
+// NaN: one v_cvt_pk_bf16_f32.  Over every float bit pattern (FP32 denormals preserved,
+// the compiler's default) it gives the same bits as rounding the float's bits by hand
+// (add 0x7fff plus the kept LSB, keep the top half), and a NaN for every NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
-
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack_bf2(f, 0.0f) & 0xffffu; }
 
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + __expf(-a)); }
+// logistic function with the hardware reciprocal (1 ulp) instead of an IEEE division
+__device__ __forceinline__ float sigmoidf_(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 // ----------------------------------------------------------------------------- MXFP8
 // Block exponent of a 32-element MX block: the smallest e in [-127, 127] with
