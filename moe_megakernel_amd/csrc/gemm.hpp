@@ -849,6 +849,9 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const int I = p.I;
   const float L = p.limit;
+  // two copies of the epilogue, so that a layer without a clamp runs none of its selects
+  auto epilogue = [&](auto clamp) __attribute__((always_inline)) {
+  constexpr bool CL = decltype(clamp)::value;
   tok_epilogue<TL, true>(acc, lds, tt.rows, TL::TN, [&](int row, int lc, const float* ga, const float* ub) {
     const int jj = tt.nt * (TL::TN / 2) + lc;
     const int64_t R = crow0 + row;
@@ -862,8 +865,8 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
         // the clamp is decided here, on the FP32 accumulator; a clamped input is stored as
         // +-infinity, so the backward reads the decision instead of taking it again on a
         // rounded value
-        const bool a_hi = L > 0.0f && a > L;
-        const bool b_out = L > 0.0f && fabsf(b) > L;
+        const bool a_hi = CL && a > L;
+        const bool b_out = CL && fabsf(b) > L;
         const float ac = a_hi ? L : a;
         const float bc = b_out ? copysignf(L, b) : b;
         hv[e] = ac * sigmoidf_(ac) * bc;
@@ -890,6 +893,9 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
       }
     }
   });
+  };
+  if (L > 0.0f) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // Plain token-dim GEMM with bf16 store: C[rows][N] = A[rows][K] * B, where B is either
@@ -1051,6 +1057,8 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
 
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const float L = p.limit;
+  auto epilogue = [&](auto clamp) __attribute__((always_inline)) {   // as in the FC1 kernel
+  constexpr bool CL = decltype(clamp)::value;
   tok_epilogue<TL, false>(acc, lds, tt.rows, ncols, [&](int row, int col, const float* gv) {
     const int n = n0 + col;
     const int64_t R = (crow0 + row) * 2 * (int64_t)I;
@@ -1062,8 +1070,8 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
     for (int k = 0; k < 8; ++k) {
       const float a = av[k], b = bv[k], gh = gv[k];
       // the forward's clamp decisions: a clamped input was stored as +-infinity
-      const bool a_hi = L > 0.0f && a == __builtin_inff();
-      const bool b_out = L > 0.0f && __builtin_isinf(b);
+      const bool a_hi = CL && a == __builtin_inff();
+      const bool b_out = CL && __builtin_isinf(b);
       const float ac = a_hi ? L : a;
       const float bc = b_out ? copysignf(L, b) : b;
       const float sg = sigmoidf_(ac);
@@ -1094,6 +1102,9 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
       }
     }
   });
+  };
+  if (L > 0.0f) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------------
