@@ -38,6 +38,11 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+// global-memory views, so that main_grad's accesses compile to global (not flat)
+// instructions: a flat access counts against the LDS wait counter too, and would hold up
+// every LDS wait behind the outstanding main_grad loads
+typedef __attribute__((address_space(1))) f32x4_t glb_f32x4;
+typedef __attribute__((address_space(1))) u32x2_t glb_u32x2;
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 
 
@@ -1229,10 +1234,10 @@ __global__ __launch_bounds__((TL_WG<MG16, SHORT>::NTH), (TL_WG<MG16, SHORT>::MIN
       const uint8_t* src = cb + grow * ldc + cc * 4 * ES;
       const bool in = grow < mrows && 4 * cc < ncols;
       if constexpr (MG16) {
-        const u32x2_t v = in ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src)) : u32x2_t{};
+        const u32x2_t v = in ? __builtin_nontemporal_load(((const glb_u32x2*)(src))) : u32x2_t{};
         mg[u] = f32x4_t{lo_bf(v[0]), hi_bf(v[0]), lo_bf(v[1]), hi_bf(v[1])};
       } else {
-        mg[u] = in ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src)) : f32x4_t{};
+        mg[u] = in ? __builtin_nontemporal_load(((const glb_f32x4*)(src))) : f32x4_t{};
       }
     }
     __syncthreads();   // the LDS slice is free (K loop or previous round done)
@@ -1264,9 +1269,9 @@ __global__ __launch_bounds__((TL_WG<MG16, SHORT>::NTH), (TL_WG<MG16, SHORT>::MIN
           f32x4_t r;
 #pragma unroll
           for (int k = 0; k < 4; ++k) r[k] = mg[u][k] + bf2f(f2bf(v[k]));
-          __builtin_nontemporal_store(u32x2_t{pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3])}, reinterpret_cast<u32x2_t*>(dst));
+          __builtin_nontemporal_store(u32x2_t{pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3])}, ((glb_u32x2*)(dst)));
         } else {
-          __builtin_nontemporal_store(mg[u] + v, reinterpret_cast<f32x4_t*>(dst));
+          __builtin_nontemporal_store(mg[u] + v, ((glb_f32x4*)(dst)));
         }
       }
     }
