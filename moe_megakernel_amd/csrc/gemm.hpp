@@ -856,48 +856,48 @@ __global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k
   const float L = p.limit;
   // two copies of the epilogue, so that a layer without a clamp runs none of its selects
   auto epilogue = [&](auto clamp) __attribute__((always_inline)) {
-  constexpr bool CL = decltype(clamp)::value;
-  tok_epilogue<TL, true>(acc, lds, tt.rows, TL::TN, [&](int row, int lc, const float* ga, const float* ub) {
-    const int jj = tt.nt * (TL::TN / 2) + lc;
-    const int64_t R = crow0 + row;
-    uint32_t aw[4], bw[4], hw[4];
+    constexpr bool CL = decltype(clamp)::value;
+    tok_epilogue<TL, true>(acc, lds, tt.rows, TL::TN, [&](int row, int lc, const float* ga, const float* ub) {
+      const int jj = tt.nt * (TL::TN / 2) + lc;
+      const int64_t R = crow0 + row;
+      uint32_t aw[4], bw[4], hw[4];
 #pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-      float hv[2], as[2], bs[2];
+      for (int k = 0; k < 8; k += 2) {
+        float hv[2], as[2], bs[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float a = ga[k + e], b = ub[k + e];
-        // the clamp is decided here, on the FP32 accumulator; a clamped input is stored as
-        // +-infinity, so the backward reads the decision instead of taking it again on a
-        // rounded value
-        const bool a_hi = CL && a > L;
-        const bool b_out = CL && fabsf(b) > L;
-        const float ac = a_hi ? L : a;
-        const float bc = b_out ? copysignf(L, b) : b;
-        hv[e] = ac * sigmoidf_(ac) * bc;
-        as[e] = a_hi ? __builtin_inff() : a;
-        bs[e] = b_out ? copysignf(__builtin_inff(), b) : b;
+        for (int e = 0; e < 2; ++e) {
+          const float a = ga[k + e], b = ub[k + e];
+          // the clamp is decided here, on the FP32 accumulator; a clamped input is stored as
+          // +-infinity, so the backward reads the decision instead of taking it again on a
+          // rounded value
+          const bool a_hi = CL && a > L;
+          const bool b_out = CL && fabsf(b) > L;
+          const float ac = a_hi ? L : a;
+          const float bc = b_out ? copysignf(L, b) : b;
+          hv[e] = ac * sigmoidf_(ac) * bc;
+          as[e] = a_hi ? __builtin_inff() : a;
+          bs[e] = b_out ? copysignf(__builtin_inff(), b) : b;
+        }
+        aw[k / 2] = pack_bf2(as[0], as[1]);
+        bw[k / 2] = pack_bf2(bs[0], bs[1]);
+        hw[k / 2] = pack_bf2(hv[0], hv[1]);
       }
-      aw[k / 2] = pack_bf2(as[0], as[1]);
-      bw[k / 2] = pack_bf2(bs[0], bs[1]);
-      hw[k / 2] = pack_bf2(hv[0], hv[1]);
-    }
-    *reinterpret_cast<uint4*>(p.ab + R * 2 * I + jj) = make_uint4(aw[0], aw[1], aw[2], aw[3]);
-    *reinterpret_cast<uint4*>(p.ab + R * 2 * I + I + jj) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-    *reinterpret_cast<uint4*>(p.h + R * I + jj) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    if constexpr (MX) {
-      if (!shared) {   // the routed FC2 input: MXFP8 codes of the BF16 h of these 8 columns; the
-                       // 4 lanes holding one 32-column block are adjacent (8 columns per lane)
-        float hb[8];
+      *reinterpret_cast<uint4*>(p.ab + R * 2 * I + jj) = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+      *reinterpret_cast<uint4*>(p.ab + R * 2 * I + I + jj) = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+      *reinterpret_cast<uint4*>(p.h + R * I + jj) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      if constexpr (MX) {
+        if (!shared) {   // the routed FC2 input: MXFP8 codes of the BF16 h of these 8 columns; the
+                         // 4 lanes holding one 32-column block are adjacent (8 columns per lane)
+          float hb[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) { hb[2 * k] = lo_bf(hw[k]); hb[2 * k + 1] = hi_bf(hw[k]); }
-        uint2 q;
-        const uint32_t sc = mx_quantize8(hb, quad_max(absmax8(hb)), q);
-        *reinterpret_cast<uint2*>(p.hq + R * I + jj) = q;
-        if ((jj & 31) == 0) p.hs[R * (I / 32) + jj / 32] = (uint8_t)sc;
+          for (int k = 0; k < 4; ++k) { hb[2 * k] = lo_bf(hw[k]); hb[2 * k + 1] = hi_bf(hw[k]); }
+          uint2 q;
+          const uint32_t sc = mx_quantize8(hb, quad_max(absmax8(hb)), q);
+          *reinterpret_cast<uint2*>(p.hq + R * I + jj) = q;
+          if ((jj & 31) == 0) p.hs[R * (I / 32) + jj / 32] = (uint8_t)sc;
+        }
       }
-    }
-  });
+    });
   };
   if (L > 0.0f) epilogue(std::true_type{});
   else epilogue(std::false_type{});
@@ -1063,50 +1063,50 @@ __global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k
   const int64_t crow0 = shared ? p.t.shared_row0 + tt.m0 : (int64_t)p.t.offsets[tt.g] + tt.m0;
   const float L = p.limit;
   auto epilogue = [&](auto clamp) __attribute__((always_inline)) {   // as in the FC1 kernel
-  constexpr bool CL = decltype(clamp)::value;
-  tok_epilogue<TL, false>(acc, lds, tt.rows, ncols, [&](int row, int col, const float* gv) {
-    const int n = n0 + col;
-    const int64_t R = (crow0 + row) * 2 * (int64_t)I;
-    float av[8], bv[8];
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.ab + R + n), av);   // the stored BF16 a, b
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.ab + R + I + n), bv);
-    float da[8], db[8];
+    constexpr bool CL = decltype(clamp)::value;
+    tok_epilogue<TL, false>(acc, lds, tt.rows, ncols, [&](int row, int col, const float* gv) {
+      const int n = n0 + col;
+      const int64_t R = (crow0 + row) * 2 * (int64_t)I;
+      float av[8], bv[8];
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(p.ab + R + n), av);   // the stored BF16 a, b
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(p.ab + R + I + n), bv);
+      float da[8], db[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float a = av[k], b = bv[k], gh = gv[k];
-      // the forward's clamp decisions: a clamped input was stored as +-infinity
-      const bool a_hi = CL && a == __builtin_inff();
-      const bool b_out = CL && __builtin_isinf(b);
-      const float ac = a_hi ? L : a;
-      const float bc = b_out ? copysignf(L, b) : b;
-      const float sg = sigmoidf_(ac);
-      da[k] = a_hi ? 0.0f : gh * bc * (sg * (1.0f + ac * (1.0f - sg)));
-      db[k] = b_out ? 0.0f : gh * (ac * sg);
-    }
-    const uint4 dav = make_uint4(pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3]), pack_bf2(da[4], da[5]),
-                                 pack_bf2(da[6], da[7]));
-    const uint4 dbv = make_uint4(pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3]), pack_bf2(db[4], db[5]),
-                                 pack_bf2(db[6], db[7]));
-    *reinterpret_cast<uint4*>(p.dfc1 + R + n) = dav;
-    *reinterpret_cast<uint4*>(p.dfc1 + R + I + n) = dbv;
-    if constexpr (MX) {
-      if (!shared) {   // the routed FC1 data-gradient input: MXFP8 codes of the BF16 da and db
-                       // (the 4 lanes holding one 32-column block are adjacent)
-        float fa[8], fb[8];
-        unpack_bf16x8(dav, fa);
-        unpack_bf16x8(dbv, fb);
-        uint2 qa, qb;
-        const uint32_t sa = mx_quantize8(fa, quad_max(absmax8(fa)), qa);
-        const uint32_t sb = mx_quantize8(fb, quad_max(absmax8(fb)), qb);
-        *reinterpret_cast<uint2*>(p.dfq + R + n) = qa;
-        *reinterpret_cast<uint2*>(p.dfq + R + I + n) = qb;
-        if ((n & 31) == 0) {
-          p.dfs[R / 32 + n / 32] = (uint8_t)sa;
-          p.dfs[R / 32 + (I + n) / 32] = (uint8_t)sb;
+      for (int k = 0; k < 8; ++k) {
+        const float a = av[k], b = bv[k], gh = gv[k];
+        // the forward's clamp decisions: a clamped input was stored as +-infinity
+        const bool a_hi = CL && a == __builtin_inff();
+        const bool b_out = CL && __builtin_isinf(b);
+        const float ac = a_hi ? L : a;
+        const float bc = b_out ? copysignf(L, b) : b;
+        const float sg = sigmoidf_(ac);
+        da[k] = a_hi ? 0.0f : gh * bc * (sg * (1.0f + ac * (1.0f - sg)));
+        db[k] = b_out ? 0.0f : gh * (ac * sg);
+      }
+      const uint4 dav = make_uint4(pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3]), pack_bf2(da[4], da[5]),
+                                   pack_bf2(da[6], da[7]));
+      const uint4 dbv = make_uint4(pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3]), pack_bf2(db[4], db[5]),
+                                   pack_bf2(db[6], db[7]));
+      *reinterpret_cast<uint4*>(p.dfc1 + R + n) = dav;
+      *reinterpret_cast<uint4*>(p.dfc1 + R + I + n) = dbv;
+      if constexpr (MX) {
+        if (!shared) {   // the routed FC1 data-gradient input: MXFP8 codes of the BF16 da and db
+                         // (the 4 lanes holding one 32-column block are adjacent)
+          float fa[8], fb[8];
+          unpack_bf16x8(dav, fa);
+          unpack_bf16x8(dbv, fb);
+          uint2 qa, qb;
+          const uint32_t sa = mx_quantize8(fa, quad_max(absmax8(fa)), qa);
+          const uint32_t sb = mx_quantize8(fb, quad_max(absmax8(fb)), qb);
+          *reinterpret_cast<uint2*>(p.dfq + R + n) = qa;
+          *reinterpret_cast<uint2*>(p.dfq + R + I + n) = qb;
+          if ((n & 31) == 0) {
+            p.dfs[R / 32 + n / 32] = (uint8_t)sa;
+            p.dfs[R / 32 + (I + n) / 32] = (uint8_t)sb;
+          }
         }
       }
-    }
-  });
+    });
   };
   if (L > 0.0f) epilogue(std::true_type{});
   else epilogue(std::false_type{});
