@@ -81,8 +81,9 @@ struct Tile {
 template <class TL>
 using Acc = f32x16_t[TL::MI][TL::NJ];
 
-// Zero page: the source of row-contiguous k rows past the end of K.
-__device__ __align__(16) uint4 g_zero_page[64];
+// Zero page: the source of row-contiguous k rows past the end of K.  Internal linkage:
+// each translation unit that launches kernels holds its own copy.
+static __device__ __align__(16) uint4 g_zero_page[64];
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_u8*)p;
@@ -1277,6 +1278,20 @@ __global__ __launch_bounds__((TL_WG<MG16, SHORT>::NTH), (TL_WG<MG16, SHORT>::MIN
     }
   }
 }
+
+// ---------------------------------------------------------------------------------
+// Launchers, defined in translation units of their own (gemm_tok.hip: the token-dimension
+// GEMMs; gemm_wgrad.hip: the weight gradients), so that each family can take its own
+// instruction-scheduling strategy.
+// ---------------------------------------------------------------------------------
+template <bool MX>
+void launch_fc1(dim3 grid, hipStream_t st, const Fc1Args& a);
+template <int BMODE, bool MX>
+void launch_plain(dim3 grid, hipStream_t st, const PlainArgs& a);
+template <bool MX>
+void launch_dgrad_swiglu(dim3 grid, hipStream_t st, const DgradSwigluArgs& a);
+template <int FC, bool MG16, bool SHORT>
+void launch_wgrad(dim3 grid, hipStream_t st, const WgradArgs& a);
 
 }  // namespace gemm
 }  // namespace moe

@@ -394,8 +394,7 @@ template <int FC, bool MG16, bool SHORT>
 void launch_wgrad_t(const gemm::WgradArgs& a, const Dims& d, hipStream_t st) {
   const int per = gemm::wgrad_tiles_per_group<MG16, SHORT>(a.parts, a.mpart, a.N);
   const dim3 g((d.hs ? per : 0) + grid8((int64_t)d.E * per));
-  constexpr unsigned nth = gemm::TL_WG<MG16, SHORT>::NTH;
-  hipLaunchKernelGGL((gemm::k_wgrad<FC, MG16, SHORT>), g, dim3(nth), 0, st, a);
+  gemm::launch_wgrad<FC, MG16, SHORT>(g, st, a);
 }
 // The FP32-main_grad weight gradients take their short-token-loop shape when the routed
 // experts average at most this many slots (T K / E).
@@ -463,8 +462,8 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   MOE_TRY(launch(again ? "recompute_fc1_swiglu" : "fc1_swiglu", st, [&] {
     using S1 = gemm::Shapes<true>::FC1;
     using S0 = gemm::Shapes<false>::FC1;
-    if (d.mx) hipLaunchKernelGGL(gemm::k_fc1_swiglu<true>, dim3(tok_grid(mt * (2 * I / S1::TN))), dim3(S1::NTH), 0, st, a1);
-    else hipLaunchKernelGGL(gemm::k_fc1_swiglu<false>, dim3(tok_grid(mt * (2 * I / S0::TN))), dim3(S0::NTH), 0, st, a1);
+    if (d.mx) gemm::launch_fc1<true>(dim3(tok_grid(mt * (2 * I / S1::TN))), st, a1);
+    else gemm::launch_fc1<false>(dim3(tok_grid(mt * (2 * I / S0::TN))), st, a1);
   }));
 
   // F5 + F6: routed and shared FC2 -> y (unweighted)
@@ -490,8 +489,8 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   MOE_TRY(launch(again ? "recompute_fc2" : "fc2", st, [&] {
     using S1 = gemm::Shapes<true>::FC2;
     using S0 = gemm::Shapes<false>::FC2;
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, true>), dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a2);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::KC, false>), dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a2);
+    if (d.mx) gemm::launch_plain<gemm::KC, true>(dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), st, a2);
+    else gemm::launch_plain<gemm::KC, false>(dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), st, a2);
   }));
   return MOE_OK;
 }
@@ -787,8 +786,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   MOE_TRY(launch("dgrad_fc2_swiglu", st, [&] {
     using S1 = gemm::Shapes<true>::DG2;
     using S0 = gemm::Shapes<false>::DG2;
-    if (d.mx) hipLaunchKernelGGL(gemm::k_dgrad_swiglu<true>, dim3(tok_grid(mt * ((I + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a3);
-    else hipLaunchKernelGGL(gemm::k_dgrad_swiglu<false>, dim3(tok_grid(mt * ((I + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a3);
+    if (d.mx) gemm::launch_dgrad_swiglu<true>(dim3(tok_grid(mt * ((I + S1::TN - 1) / S1::TN))), st, a3);
+    else gemm::launch_dgrad_swiglu<false>(dim3(tok_grid(mt * ((I + S0::TN - 1) / S0::TN))), st, a3);
   }));
 
   // B3 (+B6): FC1 data gradient -> dxp (routed rows) and the shared rows
@@ -814,8 +813,8 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   MOE_TRY(launch("dgrad_fc1", st, [&] {
     using S1 = gemm::Shapes<true>::DG1;
     using S0 = gemm::Shapes<false>::DG1;
-    if (d.mx) hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, true>), dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), dim3(S1::NTH), 0, st, a4);
-    else hipLaunchKernelGGL((gemm::k_gemm_plain<gemm::RC, false>), dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), dim3(S0::NTH), 0, st, a4);
+    if (d.mx) gemm::launch_plain<gemm::RC, true>(dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), st, a4);
+    else gemm::launch_plain<gemm::RC, false>(dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), st, a4);
   }));
 
   // B7 dx combine
