@@ -684,6 +684,15 @@ struct MxOperands {
 #ifndef MOE_TL_WG16
 #define MOE_TL_WG16 128, 128, 2, 2, 2, 4, 0, 64
 #endif
+// BF16, many tokens per expert: two 4-wave workgroups per CU on 192 x 128 tiles (the same
+// 96 x 64 wave tiles, two 128-byte stages, exactly 80 KB of LDS each).  Where the tiles
+// are MFMA-bound, one workgroup's barrier and DMA waits and its epilogue overlap the other
+// workgroup's multiplies (EP16 share: fc1 -8%, dgrad_fc2 -4%); where the weight panels
+// stream from HBM they lose the three-stage weight ring (4096-token layer: fc1 +3%,
+// dgrad_fc2 +9%), so the library takes them above kWideSlots slots per expert.
+#ifndef MOE_TL_WIDE
+#define MOE_TL_WIDE 192, 128, 2, 2, 2, 2, 0, 128
+#endif
 template <bool MX> struct Shapes;
 template <> struct Shapes<false> {
   using FC1 = Tile<MOE_TL_FC1>; using FC2 = Tile<MOE_TL_FC2>;
@@ -693,6 +702,13 @@ template <> struct Shapes<true> {
   using FC1 = Tile<MOE_TL_FC1_MX>; using FC2 = Tile<MOE_TL_FC2_MX>;
   using DG2 = Tile<MOE_TL_DG2_MX>; using DG1 = Tile<MOE_TL_DG1_MX>;
 };
+struct ShapesWide {
+  using FC1 = Tile<MOE_TL_WIDE>; using FC2 = Tile<MOE_TL_WIDE>;
+  using DG2 = Tile<MOE_TL_WIDE>; using DG1 = Tile<MOE_TL_WIDE>;
+};
+// the shapes of one launch: MXFP8, BF16, or BF16 with many tokens per expert (WIDE)
+template <bool MX, bool WIDE>
+using ShapesOf = typename std::conditional<WIDE, ShapesWide, Shapes<MX>>::type;
 // weight gradients: FP32 main_grad (MG16 = false; SHORT: the short-token-loop shape)
 // and BF16 main_grad (true; half the read-modify-write bytes per tile, so smaller tiles at
 // higher occupancy win there)
@@ -705,6 +721,7 @@ static_assert(Shapes<false>::FC2::TM == bm_of<false>() && Shapes<false>::DG2::TM
               Shapes<false>::DG1::TM == bm_of<false>(), "BF16 token-dimension tiles share their M tile");
 static_assert(Shapes<true>::FC2::TM == bm_of<true>() && Shapes<true>::DG2::TM == bm_of<true>() &&
               Shapes<true>::DG1::TM == bm_of<true>(), "MXFP8 token-dimension tiles share their M tile");
+static_assert(ShapesWide::FC1::TM == bm_of<false>(), "both BF16 shape sets share the M tile");
 
 template <class TL>
 __device__ __forceinline__ int wave_m() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / TL::NWN; }
@@ -798,15 +815,21 @@ struct Fc1Args {
                  // tells the backward it was clamped
 };
 
-template <bool MX>
-__global__ __launch_bounds__(Shapes<MX>::FC1::NTH, Shapes<MX>::FC1::MINB) void k_fc1_swiglu(Fc1Args p) {
-  using TL = typename Shapes<MX>::FC1;
+template <bool MX, bool WIDE = false>
+__global__ __launch_bounds__((ShapesOf<MX, WIDE>::FC1::NTH), (ShapesOf<MX, WIDE>::FC1::MINB)) void k_fc1_swiglu(
+    Fc1Args p) {
+  using TL = typename ShapesOf<MX, WIDE>::FC1;
   static_assert(TL::WNC % 64 == 0 && TL::TN <= 256, "gate/up pairs per wave; 2I is a multiple of TN");
-  __shared__ __align__(16) uint8_t lds[TL::LDS];
-  __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
-  __shared__ __align__(16) uint8_t sc[MX ? TL::SC_LDS : 16];
-  __shared__ int sp[kMaxExperts + 2];
-  __shared__ int tok[TL::TM];   // token (x row) of each tile row
+  // BF16: the tile map's scratch and the token list live in the second A stage, which the
+  // K loop first writes after its first barrier, when both are dead (the token rows are
+  // in the DMA sources by then); MXFP8 reads the token list for its scale rows all along
+  constexpr int XTRA = MX ? 4 * (kMaxExperts + 2) + 4 * TL::TM : 0;
+  static_assert(MX || TL::A_BYTES >= 4 * (kMaxExperts + 2 + TL::TM), "map scratch in an A stage");
+  __shared__ __align__(16) uint8_t lds[TL::LDS + (TL::PF ? 256 : 0) + (MX ? TL::SC_LDS : 0) + XTRA];
+  uint8_t* pfb = lds + TL::LDS;
+  uint8_t* sc = pfb + (TL::PF ? 256 : 0);
+  int* sp = reinterpret_cast<int*>(MX ? sc + (MX ? TL::SC_LDS : 0) : lds + TL::A_BYTES);
+  int* tok = sp + (kMaxExperts + 2);   // token (x row) of each tile row
   const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, 2 * p.I / TL::TN, p.t.E, p.t.counts, p.t.T, sp);
   if (!tt.ok) return;
   const bool shared = tt.g == p.t.E;
@@ -921,16 +944,19 @@ struct PlainArgs {
   int N, K;
 };
 
-template <int BMODE, bool MX>
-using TL_PLAIN = typename std::conditional<BMODE == KC, typename Shapes<MX>::FC2, typename Shapes<MX>::DG1>::type;
+template <int BMODE, bool MX, bool WIDE = false>
+using TL_PLAIN =
+    typename std::conditional<BMODE == KC, typename ShapesOf<MX, WIDE>::FC2, typename ShapesOf<MX, WIDE>::DG1>::type;
 
-template <int BMODE, bool MX>
-__global__ __launch_bounds__((TL_PLAIN<BMODE, MX>::NTH), (TL_PLAIN<BMODE, MX>::MINB)) void k_gemm_plain(PlainArgs p) {
-  using TL = TL_PLAIN<BMODE, MX>;
-  __shared__ __align__(16) uint8_t lds[TL::LDS];
-  __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
-  __shared__ __align__(16) uint8_t sc[MX ? TL::SC_LDS : 16];
-  __shared__ int sp[kMaxExperts + 2];
+template <int BMODE, bool MX, bool WIDE = false>
+__global__ __launch_bounds__((TL_PLAIN<BMODE, MX, WIDE>::NTH), (TL_PLAIN<BMODE, MX, WIDE>::MINB)) void k_gemm_plain(
+    PlainArgs p) {
+  using TL = TL_PLAIN<BMODE, MX, WIDE>;
+  constexpr int XTRA = MX ? 4 * (kMaxExperts + 2) : 0;   // BF16: the map scratch in the second A stage
+  __shared__ __align__(16) uint8_t lds[TL::LDS + (TL::PF ? 256 : 0) + (MX ? TL::SC_LDS : 0) + XTRA];
+  uint8_t* pfb = lds + TL::LDS;
+  uint8_t* sc = pfb + (TL::PF ? 256 : 0);
+  int* sp = reinterpret_cast<int*>(MX ? sc + (MX ? TL::SC_LDS : 0) : lds + TL::A_BYTES);
   const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, (p.N + TL::TN - 1) / TL::TN, p.t.E, p.t.counts,
                                           p.t.T, sp);
   if (!tt.ok) return;
@@ -1020,13 +1046,15 @@ struct DgradSwigluArgs {
                  // which the forward stored as +-infinity
 };
 
-template <bool MX>
-__global__ __launch_bounds__(Shapes<MX>::DG2::NTH, Shapes<MX>::DG2::MINB) void k_dgrad_swiglu(DgradSwigluArgs p) {
-  using TL = typename Shapes<MX>::DG2;
-  __shared__ __align__(16) uint8_t lds[TL::LDS];
-  __shared__ __align__(16) uint8_t pfb[TL::PF ? 256 : 4];
-  __shared__ __align__(16) uint8_t sc[MX ? TL::SC_LDS : 16];
-  __shared__ int sp[kMaxExperts + 2];
+template <bool MX, bool WIDE = false>
+__global__ __launch_bounds__((ShapesOf<MX, WIDE>::DG2::NTH), (ShapesOf<MX, WIDE>::DG2::MINB)) void k_dgrad_swiglu(
+    DgradSwigluArgs p) {
+  using TL = typename ShapesOf<MX, WIDE>::DG2;
+  constexpr int XTRA = MX ? 4 * (kMaxExperts + 2) : 0;   // BF16: the map scratch in the second A stage
+  __shared__ __align__(16) uint8_t lds[TL::LDS + (TL::PF ? 256 : 0) + (MX ? TL::SC_LDS : 0) + XTRA];
+  uint8_t* pfb = lds + TL::LDS;
+  uint8_t* sc = pfb + (TL::PF ? 256 : 0);
+  int* sp = reinterpret_cast<int*>(MX ? sc + (MX ? TL::SC_LDS : 0) : lds + TL::A_BYTES);
   const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, (p.I + TL::TN - 1) / TL::TN, p.t.E, p.t.counts,
                                           p.t.T, sp);
   if (!tt.ok) return;
@@ -1284,11 +1312,11 @@ __global__ __launch_bounds__((TL_WG<MG16, SHORT>::NTH), (TL_WG<MG16, SHORT>::MIN
 // GEMMs; gemm_wgrad.hip: the weight gradients), so that each family can take its own
 // instruction-scheduling strategy.
 // ---------------------------------------------------------------------------------
-template <bool MX>
+template <bool MX, bool WIDE>
 void launch_fc1(dim3 grid, hipStream_t st, const Fc1Args& a);
-template <int BMODE, bool MX>
+template <int BMODE, bool MX, bool WIDE>
 void launch_plain(dim3 grid, hipStream_t st, const PlainArgs& a);
-template <bool MX>
+template <bool MX, bool WIDE>
 void launch_dgrad_swiglu(dim3 grid, hipStream_t st, const DgradSwigluArgs& a);
 template <int FC, bool MG16, bool SHORT>
 void launch_wgrad(dim3 grid, hipStream_t st, const WgradArgs& a);

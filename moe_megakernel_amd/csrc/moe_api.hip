@@ -388,6 +388,14 @@ unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
 // an even split (the shared and routed tiles are split separately)
 unsigned tok_grid(int64_t n) { return grid8(n) + 8; }
 
+// The BF16 token GEMMs take the wide shape set (192 x 128 tiles, two workgroups per CU)
+// above this many routed slots per expert on average: their tiles are MFMA-bound there,
+// and a second workgroup's multiplies cover each one's waits and epilogue.  Fewer slots
+// per expert (171 at the 4096-token, 96-expert layer) keep the 192 x 256 shapes, whose
+// three-stage weight ring feeds the HBM-bound weight stream.
+constexpr int64_t kWideSlots = 1024;
+bool tok_wide(const Dims& d) { return !d.mx && d.SM > kWideSlots * d.E; }
+
 // Weight-gradient launch: the shared expert's tiles first (when present), then E groups
 // of routed tiles rounded up to a multiple of 8 blocks (one chunk per XCD).
 template <int FC, bool MG16, bool SHORT>
@@ -462,8 +470,10 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   MOE_TRY(launch(again ? "recompute_fc1_swiglu" : "fc1_swiglu", st, [&] {
     using S1 = gemm::Shapes<true>::FC1;
     using S0 = gemm::Shapes<false>::FC1;
-    if (d.mx) gemm::launch_fc1<true>(dim3(tok_grid(mt * (2 * I / S1::TN))), st, a1);
-    else gemm::launch_fc1<false>(dim3(tok_grid(mt * (2 * I / S0::TN))), st, a1);
+    using SW = gemm::ShapesWide::FC1;
+    if (d.mx) gemm::launch_fc1<true, false>(dim3(tok_grid(mt * (2 * I / S1::TN))), st, a1);
+    else if (tok_wide(d)) gemm::launch_fc1<false, true>(dim3(tok_grid(mt * (2 * I / SW::TN))), st, a1);
+    else gemm::launch_fc1<false, false>(dim3(tok_grid(mt * (2 * I / S0::TN))), st, a1);
   }));
 
   // F5 + F6: routed and shared FC2 -> y (unweighted)
@@ -489,8 +499,11 @@ moe_status experts_forward(const Dims& d, const FwdPtrs& P, const uint16_t* x, c
   MOE_TRY(launch(again ? "recompute_fc2" : "fc2", st, [&] {
     using S1 = gemm::Shapes<true>::FC2;
     using S0 = gemm::Shapes<false>::FC2;
-    if (d.mx) gemm::launch_plain<gemm::KC, true>(dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), st, a2);
-    else gemm::launch_plain<gemm::KC, false>(dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), st, a2);
+    using SW = gemm::ShapesWide::FC2;
+    if (d.mx) gemm::launch_plain<gemm::KC, true, false>(dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), st, a2);
+    else if (tok_wide(d))
+      gemm::launch_plain<gemm::KC, false, true>(dim3(tok_grid(mt * ((H + SW::TN - 1) / SW::TN))), st, a2);
+    else gemm::launch_plain<gemm::KC, false, false>(dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), st, a2);
   }));
   return MOE_OK;
 }
@@ -786,8 +799,11 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   MOE_TRY(launch("dgrad_fc2_swiglu", st, [&] {
     using S1 = gemm::Shapes<true>::DG2;
     using S0 = gemm::Shapes<false>::DG2;
-    if (d.mx) gemm::launch_dgrad_swiglu<true>(dim3(tok_grid(mt * ((I + S1::TN - 1) / S1::TN))), st, a3);
-    else gemm::launch_dgrad_swiglu<false>(dim3(tok_grid(mt * ((I + S0::TN - 1) / S0::TN))), st, a3);
+    using SW = gemm::ShapesWide::DG2;
+    if (d.mx) gemm::launch_dgrad_swiglu<true, false>(dim3(tok_grid(mt * ((I + S1::TN - 1) / S1::TN))), st, a3);
+    else if (tok_wide(d))
+      gemm::launch_dgrad_swiglu<false, true>(dim3(tok_grid(mt * ((I + SW::TN - 1) / SW::TN))), st, a3);
+    else gemm::launch_dgrad_swiglu<false, false>(dim3(tok_grid(mt * ((I + S0::TN - 1) / S0::TN))), st, a3);
   }));
 
   // B3 (+B6): FC1 data gradient -> dxp (routed rows) and the shared rows
@@ -813,8 +829,11 @@ moe_status moe_backward(const moe_problem* p, const void* grad_out, const void* 
   MOE_TRY(launch("dgrad_fc1", st, [&] {
     using S1 = gemm::Shapes<true>::DG1;
     using S0 = gemm::Shapes<false>::DG1;
-    if (d.mx) gemm::launch_plain<gemm::RC, true>(dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), st, a4);
-    else gemm::launch_plain<gemm::RC, false>(dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), st, a4);
+    using SW = gemm::ShapesWide::DG1;
+    if (d.mx) gemm::launch_plain<gemm::RC, true, false>(dim3(tok_grid(mt * ((H + S1::TN - 1) / S1::TN))), st, a4);
+    else if (tok_wide(d))
+      gemm::launch_plain<gemm::RC, false, true>(dim3(tok_grid(mt * ((H + SW::TN - 1) / SW::TN))), st, a4);
+    else gemm::launch_plain<gemm::RC, false, false>(dim3(tok_grid(mt * ((H + S0::TN - 1) / S0::TN))), st, a4);
   }));
 
   // B7 dx combine

@@ -145,6 +145,32 @@ def test_all_tokens_on_one_expert(gpu_lib):
     _check_backward(dp, W)
 
 
+@pytest.mark.parametrize("shape", [
+    (1300, 256, 2, 2, 384),    # 1300 slots per expert, ragged row tiles, 3 SwiGLU-backward N tiles
+    (2200, 384, 3, 2, 256),    # three experts, shared and routed rows in every launch
+])
+def test_many_tokens_per_expert_wide_shapes(gpu_lib, shape):
+    """BF16 layers with more than 1024 routed slots per expert take the two-workgroups-per-
+    CU token-GEMM shapes (192 x 128 tiles): parity with the oracle, and two runs bit for bit."""
+    T, H, E, K, I = shape
+    assert T * K > 1024 * E   # above the library's threshold for the wide shapes
+    cfg = gen.custom(T, H, E, K, I, short_frac=0.1, short_max=1, idx=500 + T)
+    print(f"[case] wide shapes T={T} H={H} E={E} K={K} I={I}", flush=True)
+    dp = _dp(cfg)
+    snaps = []
+    for _ in range(2):
+        dp.reset_main_grads()
+        dp.forward()
+        dp.backward()
+        torch.cuda.synchronize()
+        snaps.append(_bitwise_snapshot(dp))
+    assert _same_bits(*snaps)
+    check_routing_state(dp)
+    W = oracle_weights(dp)
+    _check_forward(dp, W)
+    _check_backward(dp, W)
+
+
 def test_route_overflow_sets_status_word(gpu_lib):
     T, E, K = 64, 8, 2
     cfg = gen.custom(T, 128, E, K, 128, idx=303)
