@@ -389,11 +389,15 @@ unsigned grid8(int64_t n) { return (unsigned)(((n + 7) / 8) * 8); }
 unsigned tok_grid(int64_t n) { return grid8(n) + 8; }
 
 // The BF16 token GEMMs take the wide shape set (192 x 128 tiles, two workgroups per CU)
-// above this many routed slots per expert on average: their tiles are MFMA-bound there,
-// and a second workgroup's multiplies cover each one's waits and epilogue.  Fewer slots
-// per expert (171 at the 4096-token, 96-expert layer) keep the 192 x 256 shapes, whose
-// three-stage weight ring feeds the HBM-bound weight stream.
-constexpr int64_t kWideSlots = 1024;
+// above this many routed slots per expert on average: a second workgroup's multiplies
+// cover each one's waits and epilogue.  At the 4096-token layer (H 4096, I 1024, top-4)
+// the step is 0.5-2.6% faster with them from 341 slots per expert up, and 1.4% slower at
+// 171 (96 experts), where each weight panel is read by one m-tile and the 192 x 256
+// shapes' three-stage weight ring feeds the HBM-bound weight stream better.
+#ifndef MOE_WIDE_SLOTS
+#define MOE_WIDE_SLOTS 256
+#endif
+constexpr int64_t kWideSlots = MOE_WIDE_SLOTS;
 bool tok_wide(const Dims& d) { return !d.mx && d.SM > kWideSlots * d.E; }
 
 // Weight-gradient launch: the shared expert's tiles first (when present), then E groups

@@ -148,12 +148,13 @@ def test_all_tokens_on_one_expert(gpu_lib):
 @pytest.mark.parametrize("shape", [
     (1300, 256, 2, 2, 384),    # 1300 slots per expert, ragged row tiles, 3 SwiGLU-backward N tiles
     (2200, 384, 3, 2, 256),    # three experts, shared and routed rows in every launch
+    (700, 256, 7, 3, 128),     # 300 slots per expert, just above the threshold, uneven experts
 ])
 def test_many_tokens_per_expert_wide_shapes(gpu_lib, shape):
-    """BF16 layers with more than 1024 routed slots per expert take the two-workgroups-per-
+    """BF16 layers with more than 256 routed slots per expert take the two-workgroups-per-
     CU token-GEMM shapes (192 x 128 tiles): parity with the oracle, and two runs bit for bit."""
     T, H, E, K, I = shape
-    assert T * K > 1024 * E   # above the library's threshold for the wide shapes
+    assert T * K > 256 * E   # above the library's threshold for the wide shapes
     cfg = gen.custom(T, H, E, K, I, short_frac=0.1, short_max=1, idx=500 + T)
     print(f"[case] wide shapes T={T} H={H} E={E} K={K} I={I}", flush=True)
     dp = _dp(cfg)
