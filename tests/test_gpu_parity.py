@@ -446,6 +446,7 @@ def test_hip_graph_replay_matches_eager(gpu_lib):
     ("bf16", "table", (1, 128, 3, 2, 128)),
     ("mxfp8", "table", (300, 256, 6, 3, 128)),
     ("mxfp8", "single", (520, 384, 9, 2, 256)),
+    ("bf16", "single", (900, 256, 3, 3, 128)),   # 900 slots per expert: the wide BF16 shapes
 ])
 def test_routed_only_forward_backward_matches_oracle(gpu_lib, routed, layout, shape):
     T, H, E, K, I = shape
@@ -526,6 +527,7 @@ def _assert_same_bits(a, b):
     ("bf16", "single", (777, 384, 13, 4, 256), True),
     ("mxfp8", "table", (300, 256, 6, 3, 128), True),
     ("mxfp8", "single", (520, 384, 9, 2, 256), False),
+    ("bf16", "table", (900, 256, 3, 3, 128), False),   # the wide BF16 shapes
 ])
 def test_recompute_is_bit_identical_and_matches_oracle(gpu_lib, routed, layout, shape, shared):
     T, H, E, K, I = shape
