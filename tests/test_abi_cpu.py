@@ -36,6 +36,21 @@ def test_library_exports_every_declared_symbol():
     assert set(mk.EXPORTED) == set(_declared_functions())
 
 
+def test_every_hip_source_is_a_build_unit():
+    """The library is linked from one object per csrc/*.hip file (each with its own
+    compiler flags): a launcher file left out of the build would leave its kernels'
+    launchers undefined in the shared library."""
+    from moe_megakernel_amd import build as B
+    units = sorted(src for src, _ in B.SOURCES)
+    on_disk = sorted(f for f in os.listdir(os.path.join(ROOT, "moe_megakernel_amd", "csrc")) if f.endswith(".hip"))
+    assert units == on_disk
+    # and the linked library defines every launcher the C ABI unit calls
+    out = subprocess.run(["nm", "-D", "--defined-only", "-C", mk.LIB_PATH], capture_output=True, text=True).stdout
+    for fn in ("moe::gemm::launch_fc1", "moe::gemm::launch_plain", "moe::gemm::launch_dgrad_swiglu",
+               "moe::gemm::launch_wgrad"):
+        assert fn in out, fn
+
+
 def test_status_strings():
     for s in range(9):
         assert mk.moe_status_str(s) and mk.moe_status_str(s) != "unknown status"
