@@ -46,12 +46,13 @@ typedef __attribute__((address_space(1))) u32x2_t glb_u32x2;
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 
 
-template <int TM_, int TN_, int NWM_, int NWN_, int NS_, int MINB_, int PF_ = 0, int KB_ = 128, int NSB_ = 0>
+template <int TM_, int TN_, int NWM_, int NWN_, int NS_, int MINB_, int PF_ = 0, int KB_ = 128, int NSB_ = 0,
+          int SCG_ = 8>
 struct Tile {
   static constexpr int TM = TM_, TN = TN_, NWM = NWM_, NWN = NWN_, NS = NS_, MINB = MINB_;
   static constexpr int PF = PF_;   // L2 prefetch distance in stages past the newest DMA stage (0: off)
   static constexpr int KB = KB_;   // K bytes per row per stage: 128, or 64 (BF16 only)
-  // Stages of the B operand in LDS: NS, or (BF16, NS = 2) three, so the B DMAs run one stage
+  // Stages of the B operand in LDS: NS, or (NS = 2) three, so the B DMAs run one stage
   // further ahead than the A DMAs.  The two operands have separate rings, A first.
   static constexpr int NSB = NSB_ ? NSB_ : NS;
   static constexpr int NW = NWM * NWN, NTH = 64 * NW;
@@ -65,11 +66,13 @@ struct Tile {
   // bytes per row, in two group buffers: fetching a row's scales once per group instead
   // of once per stage cuts the L2 requests of these rows by SCG.  B in RC mode ([K/32][TN]
   // bytes, contiguous along N) keeps one [4][TN] block per stage in an NS-deep ring.
-  static constexpr int SCG = 8;                           // stages per scale group
+  static constexpr int SCG = SCG_;                        // stages per scale group: 8 or 4
   static constexpr int SCG_A = TM * 4 * SCG, SCG_B = TN * 4 * SCG;   // group buffer parts
   static constexpr int SC_RCB = 4 * TN;                   // RC B scales of one stage
   static constexpr int LDS = NS * A_BYTES + NSB * B_BYTES;
-  static constexpr int SC_LDS = 2 * (SCG_A + SCG_B) + NS * SC_RCB;
+  static constexpr int SC_KC = 2 * (SCG_A + SCG_B);       // scale LDS with a K-contiguous B
+  static constexpr int SC_LDS = SC_KC + NS * SC_RCB;      // ... with a row-contiguous B
+  static_assert(SCG == 8 || SCG == 4, "scale group of 8 or 4 stages");
   // L2 prefetch: one dword per 128-byte line of a stage (TM + TN lines), PF_N per wave
   static constexpr int PF_N = PF ? (TM + TN + NTH - 1) / NTH : 0;
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "DMA split");
@@ -209,23 +212,25 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       cb[i] = 16 * c;
     }
   }
-  // MXFP8 scale groups.  Dword DMA instruction q of a group covers 8 scale rows x SCG
-  // stages: A rows 8q.. for q < GA, then (KC B) B rows.  Lane l loads row 8q' + l / 8 at
-  // group stage (l % 8) ^ (q' % 8) to byte 4 l of the instruction's 256-byte block, so
-  // row R's stage s sits at byte 32 R + 4 (s ^ (R / 8 % 8)) and 32 consecutive rows read
-  // at one stage hit 32 different banks.  Stages past K come from the zero page.  A group
-  // is issued in SCG pieces, piece p with the data of the group before's stage p + 1.
-  constexpr int GA = TL::TM / 8, GB = (BMODE == KC) ? TL::TN / 8 : 0;
+  // MXFP8 scale groups.  Dword DMA instruction q of a group covers RPI = 64 / SCG scale
+  // rows x SCG stages: A rows RPI q.. for q < GA, then (KC B) B rows.  Lane l loads row
+  // RPI q' + l / SCG at group stage (l % SCG) ^ (q' % SCG) to byte 4 l of the
+  // instruction's 256-byte block, so row R's stage s sits at byte 4 SCG R +
+  // 4 (s ^ (R / RPI % SCG)) and 32 consecutive rows read at one stage hit 32 different
+  // banks.  Stages past K come from the zero page.  A group is issued in SCG pieces,
+  // piece p with the data of the group before's stage p + 1.
+  constexpr int RPI = 64 / TL::SCG;
+  constexpr int GA = TL::TM / RPI, GB = (BMODE == KC) ? TL::TN / RPI : 0;
   constexpr int GPP = (GA + GB) / TL::SCG;   // instructions per piece
-  static_assert(!FP8 || (TL::SCG == 8 && (GA + GB) % TL::SCG == 0), "scale group split");
+  static_assert(!FP8 || (TL::TM % RPI == 0 && TL::TN % RPI == 0 && (GA + GB) % TL::SCG == 0), "scale group split");
   auto scale_piece = [&](int G, int piece) __attribute__((always_inline)) {
     if constexpr (FP8) {
       const uint32_t gbase = scg0 + (G & 1) * (TL::SCG_A + TL::SCG_B);
       for (int q = piece * GPP + w; q < (piece + 1) * GPP; q += TL::NW) {
         const bool isa = q < GA;
         const int qq = isa ? q : q - GA;
-        const int R = 8 * qq + (lane >> 3);
-        const int kt = G * TL::SCG + ((lane & 7) ^ (qq & 7));
+        const int R = RPI * qq + lane / TL::SCG;
+        const int kt = G * TL::SCG + ((lane % TL::SCG) ^ (qq % TL::SCG));
         const uint8_t* src = reinterpret_cast<const uint8_t*>(g_zero_page) + 4 * lane;
         if (kt < nk) {
           if (isa) {
@@ -311,14 +316,9 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       }
     }
   };
-  // one whole stage (equal rings): A, B, then the stage's map, scale and prefetch loads
-  auto issue = [&](int kt) __attribute__((always_inline)) {
+  // the MXFP8 scale loads that go out with stage kt
+  auto issue_sc = [&](int kt) __attribute__((always_inline)) {
     const int slot = kt % TL::NS;
-    issue_a(kt);
-    issue_b(kt);
-    if constexpr (BMAP) {
-      if (bmap) map_issue(kt + TL::NS - 1);
-    }
     if constexpr (FP8) {
       if constexpr (BMODE == RC) {   // this stage's [4][TN] block of B scales
         for (int q = w; q < TL::SC_RCB / 256; q += TL::NW) {
@@ -336,6 +336,15 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
         if (G * TL::SCG < nk) scale_piece(G, (kt - 1) % TL::SCG);
       }
     }
+  };
+  // one whole stage (equal rings): A, B, then the stage's map, scale and prefetch loads
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    issue_a(kt);
+    issue_b(kt);
+    if constexpr (BMAP) {
+      if (bmap) map_issue(kt + TL::NS - 1);
+    }
+    issue_sc(kt);
     if constexpr (TL::PF > 0) pf_issue(min(kt + TL::PF, nk - 1));
   };
 
@@ -421,7 +430,7 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       const uint8_t* sB = sA + TL::SCG_A;
       const uint8_t* sR = sc + 2 * (TL::SCG_A + TL::SCG_B) + slot * TL::SC_RCB;
       auto gsc = [&](const uint8_t* base, int R, int ks) __attribute__((always_inline)) {
-        return base[32 * R + 4 * (gs ^ ((R >> 3) & 7)) + 2 * ks + g];
+        return base[4 * TL::SCG * R + 4 * (gs ^ ((R / RPI) % TL::SCG)) + 2 * ks + g];
       };
       constexpr bool PRE = 2 * (TL::MI + TL::NJ) * 8 <= 64;
       i32x8_t a[2][TL::MI], b[2][TL::NJ];
@@ -496,16 +505,19 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
       __syncthreads();
     }
   }
-  static_assert(TL::NSB == TL::NS || (!FP8 && !BMAP), "deeper B ring: BF16 token GEMMs");
+  // (MXFP8: a K-contiguous B only, so that every scale load goes out with its A stage)
+  static_assert(TL::NSB == TL::NS || (!BMAP && (!FP8 || BMODE == KC)), "deeper B ring: token GEMMs");
   if constexpr (TL::NSB == TL::NS) {
 #pragma unroll
     for (int s = 0; s < TL::NS - 1; ++s)
       if (s < nk) issue(s);
   } else {
-    // B(0), A(0), B(1): at the top of step kt the newest loads are A(kt) and then B(kt + 1)
+    // B(0), A(0), B(1): at the top of step kt the newest loads are A(kt) (with the MXFP8
+    // scale loads that go out with it) and then B(kt + 1)
     if (nk > 0) {
       issue_b(0);
       issue_a(0);
+      issue_sc(0);
     }
     if (nk > 1) issue_b(1);
   }
@@ -519,7 +531,10 @@ __device__ __forceinline__ void tile_mma(Acc<TL>& acc, int kdim, const FA& fa, c
         if (kt + 1 < nk) wait_vm<TL::B_DMA>();
         else wait_vm<0>();
         __syncthreads();
-        if (kt + 1 < nk) issue_a(kt + 1);
+        if (kt + 1 < nk) {
+          issue_a(kt + 1);
+          issue_sc(kt + 1);
+        }
         if (kt + 2 < nk) issue_b(kt + 2);
         if constexpr (decltype(act)::value) compute(kt);
       }
@@ -660,8 +675,12 @@ struct MxOperands {
 #ifndef MOE_TL_DG1
 #define MOE_TL_DG1 192, 256, 2, 4, 2, 1
 #endif
+// MXFP8 FC1: the weight panel in three stages too, which fits beside the scale staging
+// with scale groups of 4 stages (158 KB of LDS): fc1 0.5% faster at the 4096-token layer,
+// 2% at the 8192-token one.  (Groups of 4 alone cost 0.3%; FC2 with the deeper ring ran
+// 1-1.5% slower at the larger layers and keeps two stages.)
 #ifndef MOE_TL_FC1_MX
-#define MOE_TL_FC1_MX 192, 256, 2, 4, 2, 1
+#define MOE_TL_FC1_MX 192, 256, 2, 4, 2, 1, 0, 128, 3, 4
 #endif
 #ifndef MOE_TL_FC2_MX
 #define MOE_TL_FC2_MX 192, 256, 2, 4, 2, 1
@@ -825,10 +844,10 @@ __global__ __launch_bounds__((ShapesOf<MX, WIDE>::FC1::NTH), (ShapesOf<MX, WIDE>
   // in the DMA sources by then); MXFP8 reads the token list for its scale rows all along
   constexpr int XTRA = MX ? 4 * (kMaxExperts + 2) + 4 * TL::TM : 0;
   static_assert(MX || TL::A_BYTES >= 4 * (kMaxExperts + 2 + TL::TM), "map scratch in an A stage");
-  __shared__ __align__(16) uint8_t lds[TL::LDS + (TL::PF ? 256 : 0) + (MX ? TL::SC_LDS : 0) + XTRA];
+  __shared__ __align__(16) uint8_t lds[TL::LDS + (TL::PF ? 256 : 0) + (MX ? TL::SC_KC : 0) + XTRA];
   uint8_t* pfb = lds + TL::LDS;
   uint8_t* sc = pfb + (TL::PF ? 256 : 0);
-  int* sp = reinterpret_cast<int*>(MX ? sc + (MX ? TL::SC_LDS : 0) : lds + TL::A_BYTES);
+  int* sp = reinterpret_cast<int*>(MX ? sc + (MX ? TL::SC_KC : 0) : lds + TL::A_BYTES);
   int* tok = sp + (kMaxExperts + 2);   // token (x row) of each tile row
   const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, 2 * p.I / TL::TN, p.t.E, p.t.counts, p.t.T, sp);
   if (!tt.ok) return;
@@ -953,10 +972,11 @@ __global__ __launch_bounds__((TL_PLAIN<BMODE, MX, WIDE>::NTH), (TL_PLAIN<BMODE, 
     PlainArgs p) {
   using TL = TL_PLAIN<BMODE, MX, WIDE>;
   constexpr int XTRA = MX ? 4 * (kMaxExperts + 2) : 0;   // BF16: the map scratch in the second A stage
-  __shared__ __align__(16) uint8_t lds[TL::LDS + (TL::PF ? 256 : 0) + (MX ? TL::SC_LDS : 0) + XTRA];
+  constexpr int SCB = BMODE == KC ? TL::SC_KC : TL::SC_LDS;   // MXFP8 scale staging
+  __shared__ __align__(16) uint8_t lds[TL::LDS + (TL::PF ? 256 : 0) + (MX ? SCB : 0) + XTRA];
   uint8_t* pfb = lds + TL::LDS;
   uint8_t* sc = pfb + (TL::PF ? 256 : 0);
-  int* sp = reinterpret_cast<int*>(MX ? sc + (MX ? TL::SC_LDS : 0) : lds + TL::A_BYTES);
+  int* sp = reinterpret_cast<int*>(MX ? sc + (MX ? SCB : 0) : lds + TL::A_BYTES);
   const TokTile tt = map_tok_tile<TL::TM>(p.t.tile_prefix, p.t.groups, (p.N + TL::TN - 1) / TL::TN, p.t.E, p.t.counts,
                                           p.t.T, sp);
   if (!tt.ok) return;
