@@ -273,6 +273,7 @@ def test_full_size_ep_share_bf16_sampled(gpu_lib):
 @pytest.mark.parametrize("layout,shape", [
     ("table", (300, 256, 6, 3, 128)),
     ("single", (520, 384, 9, 2, 256)),
+    ("single", (260, 128, 5, 2, 256)),   # H = 128: FC1's K loop is a single 128-code stage
 ])
 def test_mxfp8_forward_backward_matches_oracle(gpu_lib, layout, shape):
     T, H, E, K, I = shape
