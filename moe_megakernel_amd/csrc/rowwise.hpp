@@ -19,6 +19,16 @@ __device__ __forceinline__ void load_slots(const int32_t* __restrict__ slot_of, 
   for (int k = 0; k < kMaxTopk; ++k) s[k] = (k < K) ? slot_of[(int64_t)t * K + k] : -1;
 }
 
+// A 16-byte load marked non-temporal, for expert-output rows that the combines read
+// exactly once.  Keeping them out of the way of the caches' replacement order took the
+// two combines at 8192 tokens x H 7168 from 0.18 to 0.16 ms, and at 4096 x 4096 from
+// 0.0365 to 0.035 ms (the other operands keep ordinary loads).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_once(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ uint4 pack_bf8(const float (&a)[8]) {
   uint4 o;
   o.x = pack_bf2(a[0], a[1]); o.y = pack_bf2(a[2], a[3]);
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(
       v[u] = ys ? ys[c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int k = 0; k < kMaxTopk; ++k)
-        if (s[k] >= 0) r[u][k] = reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H)[c];
+        if (s[k] >= 0) r[u][k] = ld_once(reinterpret_cast<const uint4*>(y + (int64_t)s[k] * H) + c);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -268,7 +278,7 @@ __global__ __launch_bounds__(kRowThreads) void k_dx_combine(
       v[u] = src ? src[c] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int k = 0; k < kMaxTopk; ++k)
-        if (s[k] >= 0) r[u][k] = reinterpret_cast<const uint4*>(dxp + (int64_t)s[k] * H)[c];
+        if (s[k] >= 0) r[u][k] = ld_once(reinterpret_cast<const uint4*>(dxp + (int64_t)s[k] * H) + c);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
