@@ -251,20 +251,26 @@ def test_full_size_bf16_layer_full_tensors(gpu_lib):
     check_full(dp, oracle_weights(dp), BF16_TOL)
 
 
-def test_full_size_ep_share_bf16_sampled(gpu_lib):
+def test_full_size_ep_share_bf16_full_tensors(gpu_lib):
     """The same 4096 tokens on 6 local experts (one GPU's share under 16-way expert
-    parallelism, about 2731 rows per expert).  Routing state in full; out / dx / dprobs
-    on sampled tokens; main_grad deltas of sampled experts and of the shared expert."""
+    parallelism, 2730 or 2731 rows per expert), which runs the 192 x 128 token-GEMM tiles at
+    two workgroups per CU: run twice, bit for bit the same; then every token's out, dx and
+    dprobs and the main_grad deltas of all 6 routed experts and the shared expert against
+    the oracle."""
     cfg = gen.config(5)
-    dp = _dp(cfg)
-    dp.forward()
-    dp.backward()
-    torch.cuda.synchronize()
+    dp = _dp(cfg, threads=16)
+    runs = []
+    for _ in range(2):
+        dp.reset_main_grads()
+        dp.forward()
+        dp.backward()
+        torch.cuda.synchronize()
+        runs.append(_bitwise_snapshot(dp))
+    assert _same_bits(*runs), "two runs of the 6-expert share differ"
+    del runs
+    print("[determinism] two runs bit-identical", flush=True)
     check_routing_state(dp)
-    W = oracle_weights(dp)
-    toks = sample_tokens(cfg.tokens, 64, seed=5)
-    _check_forward(dp, W, tokens=toks)
-    _check_backward(dp, W, tokens=toks, experts=[0, 3, 5])
+    check_full(dp, oracle_weights(dp), BF16_TOL)
 
 
 # ----------------------------------------------------------------------------------
@@ -327,19 +333,28 @@ def test_large_mxfp8_layer_every_token(gpu_lib):
     check_full(dp, oracle_weights(dp), MXFP8_TOL, experts=sorted({0, int(np.argmax(counts)), cfg.experts - 1}))
 
 
-def test_full_size_ep_share_mxfp8_sampled(gpu_lib):
-    """4096 tokens on 6 local experts with MXFP8 routed weights (balanced); sampled tokens
-    and experts."""
+def test_full_size_ep_share_mxfp8_full_tensors(gpu_lib):
+    """4096 tokens on 6 local experts with MXFP8 routed weights (balanced): run twice, bit
+    for bit the same; the x and w dy codes bit for bit; every token's out, dx and dprobs and
+    the main_grad deltas of all 6 routed experts and the shared expert against the oracle."""
     cfg = gen.config(6)
     dp = _dp(cfg, threads=16)
-    dp.forward()
-    dp.backward()
-    torch.cuda.synchronize()
+    runs = []
+    for i in range(2):
+        dp.reset_main_grads()
+        dp.forward()
+        torch.cuda.synchronize()
+        if i == 1:
+            check_x_codes(dp)
+        dp.backward()
+        torch.cuda.synchronize()
+        runs.append(_bitwise_snapshot(dp))
+    assert _same_bits(*runs), "two runs of the MXFP8 6-expert share differ"
+    del runs
+    print("[determinism] two runs bit-identical", flush=True)
+    check_dy_codes(dp)
     check_routing_state(dp)
-    W = oracle_weights(dp)
-    toks = sample_tokens(cfg.tokens, 64, seed=6)
-    _check_forward(dp, W, tokens=toks, tol=MXFP8_TOL)
-    _check_backward(dp, W, tokens=toks, experts=[0, 2, 5], tol=MXFP8_TOL)
+    check_full(dp, oracle_weights(dp), MXFP8_TOL)
 
 
 def test_saved_context_is_relocatable(gpu_lib):
