@@ -318,8 +318,8 @@ def test_full_size_mxfp8_layer_full_tensors(gpu_lib):
 def test_large_mxfp8_layer_every_token(gpu_lib):
     """8192 tokens, hidden 7168, 64 experts, top-6, inter 2048, 2% of tokens with fewer
     than 6 routes, MXFP8 routed weights: x codes in full and w dy codes on sampled slots
-    bit for bit; every token's out, dx and dprobs, and the main_grad deltas of three routed
-    experts (the first, the busiest, the last) and of the shared expert."""
+    bit for bit; every token's out, dx and dprobs, and the main_grad deltas of all 64
+    routed experts and of the shared expert."""
     cfg = gen.config(4)
     dp = _dp(cfg, threads=16)
     dp.forward()
@@ -329,8 +329,7 @@ def test_large_mxfp8_layer_every_token(gpu_lib):
     torch.cuda.synchronize()
     check_dy_codes(dp, max_slots=8192)
     check_routing_state(dp)
-    counts = np.asarray(dp.layer.routing_state()["counts"].cpu())
-    check_full(dp, oracle_weights(dp), MXFP8_TOL, experts=sorted({0, int(np.argmax(counts)), cfg.experts - 1}))
+    check_full(dp, oracle_weights(dp), MXFP8_TOL)
 
 
 def test_full_size_ep_share_mxfp8_full_tensors(gpu_lib):
