@@ -10,7 +10,7 @@ import torch
 import moe_inputs as gen
 from oracle import moe_oracle as O
 from tests.gpu_parity_util import (BF16_TOL, MXFP8_TOL, check_dy_codes, check_full, check_routing_state,
-                                   check_x_codes, oracle_weights, rel_err, sample_tokens, to_f64, tol_of)
+                                   check_x_codes, oracle_weights, rel_err, to_f64, tol_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -492,10 +492,11 @@ def test_routed_only_empty_map_gives_exact_zeros(gpu_lib):
     _check_backward(dp, W)
 
 
-def test_routed_only_full_size_sampled(gpu_lib):
-    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 without the shared expert;
-    sampled tokens and experts.  The fused run minus the routed-only run is the shared
-    expert's output, a dense SwiGLU MLP on every token."""
+def test_routed_only_full_size_full_tensors(gpu_lib):
+    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 without the shared expert:
+    every token's out, dx and dprobs and the main_grad deltas of all 96 experts against
+    the oracle.  The fused run minus the routed-only run is the shared expert's output, a
+    dense SwiGLU MLP on every token."""
     cfg = gen.config(2)
     dp = _dp(cfg, shared=False)
     dp.forward()
@@ -503,18 +504,17 @@ def test_routed_only_full_size_sampled(gpu_lib):
     torch.cuda.synchronize()
     check_routing_state(dp)
     W = oracle_weights(dp)
-    toks = sample_tokens(cfg.tokens, 32, seed=7)
-    _check_forward(dp, W, tokens=toks)
-    _check_backward(dp, W, tokens=toks, experts=[0, 50, cfg.experts - 1])
-    routed_out = to_f64(dp.out[torch.as_tensor(toks, device=dp.out.device)])
-    del dp
+    _check_forward(dp, W)
+    _check_backward(dp, W)
+    routed_out = to_f64(dp.out)
+    del dp, W
     full = _dp(cfg, backward=False)
     full.forward()
     torch.cuda.synchronize()
     Wf = oracle_weights(full)
-    x = O.bf16_decode(full.np_x[toks])
+    x = O.bf16_decode(full.np_x)
     _, _, _, mlp = O.swiglu_ffn(x, *Wf.shared)
-    diff = to_f64(full.out[torch.as_tensor(toks, device=full.out.device)]) - routed_out
+    diff = to_f64(full.out) - routed_out
     err = rel_err(diff, mlp)
     print(f"[parity] fused - routed-only vs shared MLP: rel err {err:.3e}", flush=True)
     assert err <= 2 * BF16_TOL
@@ -672,8 +672,10 @@ def mk_status(name):
     return getattr(mk, name)
 
 
-def test_topk_table_full_size_sampled(gpu_lib):
-    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 from the router's table."""
+def test_topk_table_full_size_full_tensors(gpu_lib):
+    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 from the router's table:
+    every token's out, dx and router-weight gradients and the main_grad deltas of all 96
+    routed experts and the shared expert against the oracle."""
     cfg = gen.config(2)
     top, rw = gen.routing_table(cfg)
     dp = _dp(cfg, routing_table=(top, rw))
@@ -682,17 +684,29 @@ def test_topk_table_full_size_sampled(gpu_lib):
     torch.cuda.synchronize()
     assert _check_table_state(dp, top) == 0
     W = oracle_weights(dp)
-    toks = sample_tokens(cfg.tokens, 32, seed=11)
-    ref = O.moe_forward_table(dp.np_x, top, rw, cfg.experts, W, tokens=toks)
-    assert rel_err(to_f64(dp.out[torch.as_tensor(toks, device=dp.out.device)]), ref) <= BF16_TOL
-    g = O.moe_backward_table(dp.np_dy, dp.np_x, top, rw, cfg.experts, W, tokens=toks, experts=[3, 60])
-    sel = torch.as_tensor(toks, device=dp.dx.device)
-    assert rel_err(to_f64(dp.dx[sel]), g["dx"]) <= BF16_TOL
-    assert rel_err(dp.dprobs[sel].cpu().numpy().astype(np.float64), g["dprobs"]) <= BF16_TOL
-    I = cfg.inter
-    for e in (3, 60):
-        d1 = to_f64(dp.mg_r1_list[e]) - dp.main_grad_start((2 * I, cfg.hidden), e)
-        assert rel_err(d1[:I], g["dW"][e][0]) <= BF16_TOL
+    ref = O.moe_forward_table(dp.np_x, top, rw, cfg.experts, W)
+    errs = {"out": rel_err(to_f64(dp.out), ref)}
+    del ref
+    g = O.moe_backward_table(dp.np_dy, dp.np_x, top, rw, cfg.experts, W)
+    errs["dx"] = rel_err(to_f64(dp.dx), g["dx"])
+    dpr = dp.dprobs.cpu().numpy().astype(np.float64)
+    errs["dprobs"] = rel_err(dpr, g["dprobs"])
+    assert np.all(dpr[np.asarray(top) < 0] == 0), "pad entries must get a zero gradient"
+    I, H = cfg.inter, cfg.hidden
+    for e in range(cfg.experts):
+        d1 = to_f64(dp.mg_r1_list[e]) - dp.main_grad_start((2 * I, H), e)
+        d2 = to_f64(dp.mg_r2_list[e]) - dp.main_grad_start((H, I), e)
+        dg, du, dd = g["dW"][e]
+        errs[f"gate{e}"], errs[f"up{e}"], errs[f"down{e}"] = rel_err(d1[:I], dg), rel_err(d1[I:], du), rel_err(d2, dd)
+    s1 = to_f64(dp.mg_s1) - dp.main_grad_start((2 * I, H), 0)
+    s2 = to_f64(dp.mg_s2) - dp.main_grad_start((H, I), 0)
+    dg, du, dd = g["dW"]["shared"]
+    errs["shared_gate"], errs["shared_up"], errs["shared_down"] = rel_err(s1[:I], dg), rel_err(s1[I:], du), rel_err(s2, dd)
+    worst = max(errs, key=lambda k: errs[k])
+    print(f"[parity] table input, full tensors: out {errs['out']:.3e} dx {errs['dx']:.3e} "
+          f"dprobs {errs['dprobs']:.3e} worst {worst} {errs[worst]:.3e} (tol {BF16_TOL})", flush=True)
+    bad = {k: v for k, v in errs.items() if not (v <= BF16_TOL)}
+    assert not bad, f"over tolerance {BF16_TOL}: {bad}"
 
 
 # ----------------------------------------------------------------------------------
@@ -736,6 +750,35 @@ def test_bf16_main_grad_matches_oracle(gpu_lib, routed, layout, shape):
     assert min(match) >= 0.999
 
 
+def test_bf16_main_grad_full_size(gpu_lib):
+    """The 4096-token BF16 layer with BF16 main_grad: every token's dx and dprobs and the
+    main_grad deltas of all 96 routed experts and the shared expert against the oracle, and
+    every routed main_grad element against bf16(before + bf16(contribution)) of the same
+    call with FP32 main_grad."""
+    cfg = gen.config(2)
+    dp = _dp(cfg, main_grad_dtype="bf16")
+    dp.forward()
+    dp.backward()
+    torch.cuda.synchronize()
+    W = oracle_weights(dp)
+    _check_backward(dp, W)
+    dp32 = _dp(cfg, main_grad_dtype="fp32")
+    dp32.forward()
+    dp32.backward()
+    torch.cuda.synchronize()
+    I, H = cfg.inter, cfg.hidden
+    match = []
+    for e in range(cfg.experts):
+        for t16, t32, shape in ((dp.mg_r1_list[e], dp32.mg_r1_list[e], (2 * I, H)),
+                                (dp.mg_r2_list[e], dp32.mg_r2_list[e], (H, I))):
+            start = dp.main_grad_start(shape, e)
+            model = O.main_grad_after(start, to_f64(t32) - start, "bf16")
+            match.append(np.mean(to_f64(t16) == model))
+    print(f"[parity] bf16 main_grad = bf16(before + bf16(fp32 contribution)): exact fraction min "
+          f"{min(match):.5f}", flush=True)
+    assert min(match) >= 0.999
+
+
 # ----------------------------------------------------------------------------------
 # the shared expert's output gate
 # ----------------------------------------------------------------------------------
@@ -768,18 +811,18 @@ def test_shared_output_gate_matches_oracle(gpu_lib, routed, layout, shape):
     assert torch.equal(_bits(dp.mg_gate), _bits(rc.mg_gate))
 
 
-def test_shared_output_gate_full_size_sampled(gpu_lib):
-    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 with the shared output gate."""
+def test_shared_output_gate_full_size_full_tensors(gpu_lib):
+    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 with the shared output gate:
+    every token's out, dx and dprobs, the main_grad deltas of all 96 routed experts and the
+    shared expert, and the gate weight's main_grad delta against the oracle."""
     cfg = gen.config(2)
     dp = _dp(cfg, shared_gate=True)
     dp.forward()
     dp.backward()
     torch.cuda.synchronize()
     W = oracle_weights(dp)
-    toks = sample_tokens(cfg.tokens, 32, seed=13)
-    _check_forward(dp, W, tokens=toks)
-    # the gate weight gradient sums over every token: compare it in full (experts sampled)
-    _check_backward(dp, W, tokens=toks, experts=[1, 90])
+    _check_forward(dp, W)
+    _check_backward(dp, W)
 
 
 # ----------------------------------------------------------------------------------
@@ -848,7 +891,8 @@ def test_swiglu_clamp_matches_oracle(gpu_lib, routed, layout):
 def test_swiglu_clamp_full_size_bf16(gpu_lib):
     """The 4096-token BF16 layer with a clamp: limit in the tail of the pre-activations,
     clear of every one of them by more than the FP32 accumulation error over 4096 terms;
-    elementwise parity on sampled tokens and experts and the shared expert."""
+    every token's out, dx and dprobs and the main_grad deltas of all 96 routed experts and
+    the shared expert against the oracle."""
     cfg = gen.config(2)
     dp = _dp(cfg, backward=False)
     a_s, b_s = _preacts(dp, oracle_weights(dp))
@@ -861,9 +905,8 @@ def test_swiglu_clamp_full_size_bf16(gpu_lib):
     dp.backward()
     torch.cuda.synchronize()
     W = oracle_weights(dp)
-    toks = sample_tokens(cfg.tokens, 256, seed=19)
-    _check_forward(dp, W, tokens=toks)
-    _check_backward(dp, W, tokens=toks, experts=[0, 37, cfg.experts - 1])
+    _check_forward(dp, W)
+    _check_backward(dp, W)
 
 
 # ----------------------------------------------------------------------------------
