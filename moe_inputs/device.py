@@ -24,9 +24,28 @@ def _u8(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def _padded(a: np.ndarray, pad_bytes: int) -> np.ndarray:
+    """a with pad_bytes more bytes at the end of every row, set to all-ones bits (NaN for
+    BF16, E4M3 and E8M0), so that a kernel reading a pad poisons its result."""
+    if pad_bytes == 0:
+        return a
+    pe = pad_bytes // a.itemsize
+    out = np.full(a.shape[:-1] + (a.shape[-1] + pe,), np.iinfo(a.dtype).max, dtype=a.dtype)
+    out[..., :a.shape[-1]] = a
+    return out
+
+
+MAIN_GRAD_PAD_FILL = 7.0   # the pad columns of padded main_grad rows; no call may change them
+
+
 def fill_main_grad_pattern(t: torch.Tensor, phase: int = 0) -> None:
-    """In-place ((i mod 7) - 3) * 2^-10 over the flat index, the same exact pattern
-    as moe_inputs.main_grad_pattern, built on the device in slices."""
+    """In-place ((i mod 7) - 3) * 2^-10 over the flat index of t's logical elements, the
+    same exact pattern as moe_inputs.main_grad_pattern, built on the device in slices."""
+    if not t.is_contiguous():
+        tmp = torch.empty(t.shape, dtype=t.dtype, device=t.device)
+        fill_main_grad_pattern(tmp, phase)
+        t.copy_(tmp)
+        return
     flat = t.view(-1)
     n = flat.numel()
     step = 1 << 26
@@ -40,7 +59,7 @@ class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
                  routing=None, main_grad_dtype: str = "fp32", shared: bool = True,
                  recompute: bool = False, routing_table=None, shared_gate: bool = False,
-                 swiglu_limit: float = 0.0):
+                 swiglu_limit: float = 0.0, pad_bytes: int = 0):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
         configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16".
         shared=False: routed-only mode; the shared weight and main_grad descriptors are
@@ -49,7 +68,12 @@ class DeviceProblem:
         activations).  routing_table: optional (top_experts [T,K] int32, router_weights
         [T,K] float32), the router's fixed-width table given to moe_forward_topk instead of
         the dense map; grad_probs is then [T,K].  shared_gate: the shared expert's output gate
-        (a seeded [H] weight and its main_grad).  swiglu_limit: the SwiGLU clamp (0: none)."""
+        (a seeded [H] weight and its main_grad).  swiglu_limit: the SwiGLU clamp (0: none).
+        pad_bytes: every weight and main_grad matrix (payload, scales, shared and routed) gets
+        rows this many bytes longer than its columns (a multiple of 16), the pads filled with
+        NaN bits (weights) or MAIN_GRAD_PAD_FILL (main_grad)."""
+        assert pad_bytes % 16 == 0
+        self.pad_bytes = pad_bytes
         self.cfg = cfg
         self.device = device
         T, H, E, K, I = cfg.tokens, cfg.hidden, cfg.experts, cfg.topk, cfg.inter
@@ -74,8 +98,9 @@ class DeviceProblem:
             self.top = torch.from_numpy(self.np_top).to(device)
             self.rw = torch.from_numpy(self.np_rw).to(device)
         self.dy = _bf16(self.np_dy, device) if self.np_dy is not None else None
-        self.s1 = _bf16(self.np_s1, device)
-        self.s2 = _bf16(self.np_s2, device)
+        self.s1 = _bf16(_padded(self.np_s1, pad_bytes), device)
+        self.s2 = _bf16(_padded(self.np_s2, pad_bytes), device)
+        ldp = lambda cols, elem: cols + pad_bytes // elem   # padded row stride in elements
         self._keep = []
         mx = cfg.routed == "mxfp8"
         dt = mk.MOE_MXFP8_E4M3 if mx else mk.MOE_BF16
@@ -88,14 +113,15 @@ class DeviceProblem:
 
         def routed_mat(key, rows, cols, conv, elem_cols):
             """moe_mat for a routed tensor stored [E][rows][cols] (single) or per expert (table)."""
+            ld = ldp(elem_cols, self.np_routed[0][key].itemsize)
             if cfg.layout == "single":
-                t = conv(np.stack([r[key] for r in self.np_routed]), device)
+                t = conv(_padded(np.stack([r[key] for r in self.np_routed]), pad_bytes), device)
                 self._keep.append(t)
-                return mk.mat(base=t, expert_stride=rows * cols, ld=elem_cols), t
-            ts = [conv(r[key], device) for r in self.np_routed]
+                return mk.mat(base=t, expert_stride=rows * ld, ld=ld), t
+            ts = [conv(_padded(r[key], pad_bytes), device) for r in self.np_routed]
             tab = torch.tensor([int(t.data_ptr()) for t in ts], dtype=torch.int64, device=device)
             self._keep += ts + [tab]
-            return mk.mat(table=tab, ld=elem_cols), ts
+            return mk.mat(table=tab, ld=ld), ts
 
         if not mx:
             fc1, self.fc1 = routed_mat("fc1", 2 * I, H, _bf16, H)
@@ -116,9 +142,9 @@ class DeviceProblem:
             ru = mk.weight(dt, I, H, fc1, I, fc1s, fc1c, fc1cs)
             rd = mk.weight(dt, H, I, fc2, 0, fc2s, fc2c, fc2cs)
         if shared:
-            sg = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=0)
-            su = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=H), row_offset=I)
-            sd = mk.weight(mk.MOE_BF16, H, I, mk.mat(base=self.s2, ld=I))
+            sg = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=ldp(H, 2)), row_offset=0)
+            su = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=ldp(H, 2)), row_offset=I)
+            sd = mk.weight(mk.MOE_BF16, H, I, mk.mat(base=self.s2, ld=ldp(I, 2)))
         else:
             sg, su, sd = mk.moe_weight(), mk.moe_weight(), mk.moe_weight()
         self.weights = mk.moe_weights(sg, su, sd, rg, ru, rd)
@@ -134,33 +160,45 @@ class DeviceProblem:
             self.dprobs = torch.empty(T, K if self.table else E, dtype=torch.float32, device=device)
             mgt = {"fp32": torch.float32, "bf16": torch.bfloat16}[main_grad_dtype]
             mgd = mk.MOE_BF16 if main_grad_dtype == "bf16" else mk.MOE_FP32
-            self.mg_s1 = torch.empty(2 * I, H, dtype=mgt, device=device)
-            self.mg_s2 = torch.empty(H, I, dtype=mgt, device=device)
+            eb = 2 if main_grad_dtype == "bf16" else 4
+            lh, li = ldp(H, eb), ldp(I, eb)   # main_grad row strides
+
+            def mg(*shape):
+                """A main_grad buffer with padded rows: (the padded tensor, its logical view)."""
+                t = torch.full(shape[:-1] + (shape[-1] + pad_bytes // eb,), MAIN_GRAD_PAD_FILL, dtype=mgt,
+                               device=device)
+                return t, t[..., :shape[-1]]
+            self._mg_padded = []
+            (p1, self.mg_s1), (p2, self.mg_s2) = mg(2 * I, H), mg(H, I)
+            self._mg_padded += [p1, p2]
             self.mg_gate = torch.empty(H, dtype=mgt, device=device)
             if cfg.layout == "single":
-                self.mg_r1 = torch.empty(E, 2 * I, H, dtype=mgt, device=device)
-                self.mg_r2 = torch.empty(E, H, I, dtype=mgt, device=device)
-                g1 = dict(base=self.mg_r1, expert_stride=2 * I * H)
-                g2 = dict(base=self.mg_r2, expert_stride=H * I)
+                (p1, self.mg_r1), (p2, self.mg_r2) = mg(E, 2 * I, H), mg(E, H, I)
+                self._mg_padded += [p1, p2]
+                g1 = dict(base=p1, expert_stride=2 * I * lh)
+                g2 = dict(base=p2, expert_stride=H * li)
                 self.mg_r1_list = [self.mg_r1[e] for e in range(E)]
                 self.mg_r2_list = [self.mg_r2[e] for e in range(E)]
             else:
-                self.mg_r1_list = [torch.empty(2 * I, H, dtype=mgt, device=device) for _ in range(E)]
-                self.mg_r2_list = [torch.empty(H, I, dtype=mgt, device=device) for _ in range(E)]
-                t1 = torch.tensor([int(t.data_ptr()) for t in self.mg_r1_list], dtype=torch.int64, device=device)
-                t2 = torch.tensor([int(t.data_ptr()) for t in self.mg_r2_list], dtype=torch.int64, device=device)
+                r1 = [mg(2 * I, H) for _ in range(E)]
+                r2 = [mg(H, I) for _ in range(E)]
+                self._mg_padded += [t for t, _ in r1 + r2]
+                self.mg_r1_list = [v for _, v in r1]
+                self.mg_r2_list = [v for _, v in r2]
+                t1 = torch.tensor([int(t.data_ptr()) for t, _ in r1], dtype=torch.int64, device=device)
+                t2 = torch.tensor([int(t.data_ptr()) for t, _ in r2], dtype=torch.int64, device=device)
                 self._keep += [t1, t2]
                 g1 = dict(table=t1)
                 g2 = dict(table=t2)
             self.reset_main_grads()
-            sh = ((mk.grad(base=self.mg_s1, ld=H, row_offset=0, dtype=mgd),
-                   mk.grad(base=self.mg_s1, ld=H, row_offset=I, dtype=mgd),
-                   mk.grad(base=self.mg_s2, ld=I, dtype=mgd)) if shared
+            sh = ((mk.grad(base=self.mg_s1, ld=lh, row_offset=0, dtype=mgd),
+                   mk.grad(base=self.mg_s1, ld=lh, row_offset=I, dtype=mgd),
+                   mk.grad(base=self.mg_s2, ld=li, dtype=mgd)) if shared
                   else (mk.moe_grad(), mk.moe_grad(), mk.moe_grad()))
             self.main_grads = mk.moe_main_grads(
                 *sh,
-                mk.grad(ld=H, row_offset=0, dtype=mgd, **g1), mk.grad(ld=H, row_offset=I, dtype=mgd, **g1),
-                mk.grad(ld=I, dtype=mgd, **g2))
+                mk.grad(ld=lh, row_offset=0, dtype=mgd, **g1), mk.grad(ld=lh, row_offset=I, dtype=mgd, **g1),
+                mk.grad(ld=li, dtype=mgd, **g2))
             if shared_gate:
                 self.main_grads.shared_out_gate = mk.grad(base=self.mg_gate, ld=H, dtype=mgd)
 
@@ -173,6 +211,15 @@ class DeviceProblem:
         for e, (a, b) in enumerate(zip(self.mg_r1_list, self.mg_r2_list)):
             fill_main_grad_pattern(a, e)
             fill_main_grad_pattern(b, e)
+
+    def main_grad_pads_untouched(self) -> bool:
+        """True when every pad column of the padded main_grad rows still holds its fill."""
+        H, I = self.cfg.hidden, self.cfg.inter
+        for t in self._mg_padded:
+            cols = H if t.shape[-1] - self.pad_bytes // t.element_size() == H else I
+            if not bool((t[..., cols:] == MAIN_GRAD_PAD_FILL).all()):
+                return False
+        return True
 
     def main_grad_start(self, shape, phase) -> np.ndarray:
         n = int(np.prod(shape))

@@ -413,6 +413,36 @@ def test_single_expert_top1(gpu_lib, routed):
     _check_backward(dp, W, tol=tol_of(dp))
 
 
+@pytest.mark.parametrize("routed,layout,shape,mgd", [
+    ("bf16", "single", (300, 256, 6, 3, 128), "fp32"),
+    ("bf16", "table", (900, 256, 3, 3, 128), "fp32"),    # the wide BF16 shapes
+    ("bf16", "single", (300, 384, 6, 3, 256), "bf16"),
+    ("mxfp8", "single", (260, 384, 5, 2, 256), "fp32"),
+    ("mxfp8", "table", (300, 256, 6, 3, 128), "bf16"),
+])
+def test_padded_row_strides(gpu_lib, routed, layout, shape, mgd):
+    """Every weight (payload and scales, shared and routed) and every main_grad with rows 48
+    bytes longer than their columns, the weight pads NaN and the main_grad pads a fill value:
+    the results equal the unpadded call's bit for bit, no pad is written, and they match the
+    oracle."""
+    T, H, E, K, I = shape
+    cfg = gen.custom(T, H, E, K, I, routed=routed, layout=layout, short_frac=0.1, short_max=max(1, K - 1),
+                     idx=1100 + T)
+    runs = []
+    for pad in (0, 48):
+        dp = _dp(cfg, main_grad_dtype=mgd, pad_bytes=pad)
+        dp.forward()
+        dp.backward()
+        torch.cuda.synchronize()
+        runs.append(dp)
+    plain, padded = runs
+    assert padded.main_grad_pads_untouched(), "a main_grad pad was written"
+    _assert_same_bits(plain, padded)
+    W = oracle_weights(padded)
+    _check_forward(padded, W, tol=tol_of(padded))
+    _check_backward(padded, W, tol=tol_of(padded))
+
+
 def test_hip_graph_replay_matches_eager(gpu_lib):
     """Both calls enqueue only kernels on the caller's stream, so a captured graph of
     forward + backward replays bit-identically to the eager calls (main_grad reset
