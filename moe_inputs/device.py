@@ -59,7 +59,7 @@ class DeviceProblem:
     def __init__(self, cfg: gen.Config, device="cuda", threads: int = 8, backward: bool | None = None,
                  routing=None, main_grad_dtype: str = "fp32", shared: bool = True,
                  recompute: bool = False, routing_table=None, shared_gate: bool = False,
-                 swiglu_limit: float = 0.0, pad_bytes: int = 0):
+                 swiglu_limit: float = 0.0, pad_bytes: int = 0, separate_gate_up: bool = False):
         """routing: optional (probs [T,E] float32, routing_map [T,E] uint8) replacing the
         configuration's router output (edge cases).  main_grad_dtype: "fp32" or "bf16".
         shared=False: routed-only mode; the shared weight and main_grad descriptors are
@@ -71,7 +71,11 @@ class DeviceProblem:
         (a seeded [H] weight and its main_grad).  swiglu_limit: the SwiGLU clamp (0: none).
         pad_bytes: every weight and main_grad matrix (payload, scales, shared and routed) gets
         rows this many bytes longer than its columns (a multiple of 16), the pads filled with
-        NaN bits (weights) or MAIN_GRAD_PAD_FILL (main_grad)."""
+        NaN bits (weights) or MAIN_GRAD_PAD_FILL (main_grad).  separate_gate_up: the gate and
+        up halves of every FC1 weight (payload and scales, shared and routed) and of every FC1
+        main_grad in allocations of their own, each described with row offset 0, instead of
+        row views of one combined tensor; mg_s1 and mg_r1_list then return fresh [2I, H]
+        concatenations of the two halves."""
         assert pad_bytes % 16 == 0
         self.pad_bytes = pad_bytes
         self.cfg = cfg
@@ -98,7 +102,12 @@ class DeviceProblem:
             self.top = torch.from_numpy(self.np_top).to(device)
             self.rw = torch.from_numpy(self.np_rw).to(device)
         self.dy = _bf16(self.np_dy, device) if self.np_dy is not None else None
-        self.s1 = _bf16(_padded(self.np_s1, pad_bytes), device)
+        self.sep = separate_gate_up
+        if self.sep:
+            self.s1g = _bf16(_padded(self.np_s1[:I], pad_bytes), device)
+            self.s1u = _bf16(_padded(self.np_s1[I:], pad_bytes), device)
+        else:
+            self.s1 = _bf16(_padded(self.np_s1, pad_bytes), device)
         self.s2 = _bf16(_padded(self.np_s2, pad_bytes), device)
         ldp = lambda cols, elem: cols + pad_bytes // elem   # padded row stride in elements
         self._keep = []
@@ -111,24 +120,43 @@ class DeviceProblem:
         self.swiglu_limit = float(swiglu_limit)
         self.p = mk.problem(T, H, I, E, K, dt, flags=flags, swiglu_limit=self.swiglu_limit)
 
-        def routed_mat(key, rows, cols, conv, elem_cols):
-            """moe_mat for a routed tensor stored [E][rows][cols] (single) or per expert (table)."""
+        def routed_mat(key, rows, cols, conv, elem_cols, rsel=slice(None)):
+            """moe_mat for a routed tensor stored [E][rows][cols] (single) or per expert (table);
+            rsel picks the rows of each expert's array that the tensor holds."""
             ld = ldp(elem_cols, self.np_routed[0][key].itemsize)
             if cfg.layout == "single":
-                t = conv(_padded(np.stack([r[key] for r in self.np_routed]), pad_bytes), device)
+                t = conv(_padded(np.stack([r[key][rsel] for r in self.np_routed]), pad_bytes), device)
                 self._keep.append(t)
                 return mk.mat(base=t, expert_stride=rows * ld, ld=ld), t
-            ts = [conv(_padded(r[key], pad_bytes), device) for r in self.np_routed]
+            ts = [conv(_padded(r[key][rsel], pad_bytes), device) for r in self.np_routed]
             tab = torch.tensor([int(t.data_ptr()) for t in ts], dtype=torch.int64, device=device)
             self._keep += ts + [tab]
             return mk.mat(table=tab, ld=ld), ts
 
-        if not mx:
+        halves = (slice(0, I), slice(I, 2 * I))
+        if not mx and self.sep:
+            rg, ru = (mk.weight(mk.MOE_BF16, I, H, routed_mat("fc1", I, H, _bf16, H, rs)[0]) for rs in halves)
+            fc2, _ = routed_mat("fc2", H, I, _bf16, I)
+            rd = mk.weight(mk.MOE_BF16, H, I, fc2)
+        elif not mx:
             fc1, self.fc1 = routed_mat("fc1", 2 * I, H, _bf16, H)
             fc2, self.fc2 = routed_mat("fc2", H, I, _bf16, I)
             rg = mk.weight(mk.MOE_BF16, I, H, fc1, row_offset=0)
             ru = mk.weight(mk.MOE_BF16, I, H, fc1, row_offset=I)
             rd = mk.weight(mk.MOE_BF16, H, I, fc2)
+        elif self.sep:
+            def half(h):
+                rs, rc = halves[h], slice(h * I // 32, (h + 1) * I // 32)
+                return mk.weight(dt, I, H, routed_mat("fc1", I, H, _u8, H, rs)[0], 0,
+                                 routed_mat("fc1_s", I, H // 32, _u8, H // 32, rs)[0],
+                                 routed_mat("fc1_c", I, H, _u8, H, rs)[0],
+                                 routed_mat("fc1_cs", I // 32, H, _u8, H, rc)[0])
+            rg, ru = half(0), half(1)
+            fc2, _ = routed_mat("fc2", H, I, _u8, I)
+            fc2s, _ = routed_mat("fc2_s", H, I // 32, _u8, I // 32)
+            fc2c, _ = routed_mat("fc2_c", H, I, _u8, I)
+            fc2cs, _ = routed_mat("fc2_cs", H // 32, I, _u8, I)
+            rd = mk.weight(dt, H, I, fc2, 0, fc2s, fc2c, fc2cs)
         else:
             fc1, _ = routed_mat("fc1", 2 * I, H, _u8, H)
             fc1s, _ = routed_mat("fc1_s", 2 * I, H // 32, _u8, H // 32)
@@ -141,7 +169,11 @@ class DeviceProblem:
             rg = mk.weight(dt, I, H, fc1, 0, fc1s, fc1c, fc1cs)
             ru = mk.weight(dt, I, H, fc1, I, fc1s, fc1c, fc1cs)
             rd = mk.weight(dt, H, I, fc2, 0, fc2s, fc2c, fc2cs)
-        if shared:
+        if shared and self.sep:
+            sg = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1g, ld=ldp(H, 2)))
+            su = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1u, ld=ldp(H, 2)))
+            sd = mk.weight(mk.MOE_BF16, H, I, mk.mat(base=self.s2, ld=ldp(I, 2)))
+        elif shared:
             sg = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=ldp(H, 2)), row_offset=0)
             su = mk.weight(mk.MOE_BF16, I, H, mk.mat(base=self.s1, ld=ldp(H, 2)), row_offset=I)
             sd = mk.weight(mk.MOE_BF16, H, I, mk.mat(base=self.s2, ld=ldp(I, 2)))
@@ -169,47 +201,109 @@ class DeviceProblem:
                                device=device)
                 return t, t[..., :shape[-1]]
             self._mg_padded = []
-            (p1, self.mg_s1), (p2, self.mg_s2) = mg(2 * I, H), mg(H, I)
-            self._mg_padded += [p1, p2]
             self.mg_gate = torch.empty(H, dtype=mgt, device=device)
-            if cfg.layout == "single":
-                (p1, self.mg_r1), (p2, self.mg_r2) = mg(E, 2 * I, H), mg(E, H, I)
-                self._mg_padded += [p1, p2]
-                g1 = dict(base=p1, expert_stride=2 * I * lh)
-                g2 = dict(base=p2, expert_stride=H * li)
-                self.mg_r1_list = [self.mg_r1[e] for e in range(E)]
-                self.mg_r2_list = [self.mg_r2[e] for e in range(E)]
+            if self.sep:
+                self._sep_main_grads(mg, mgd, lh, li)
             else:
-                r1 = [mg(2 * I, H) for _ in range(E)]
-                r2 = [mg(H, I) for _ in range(E)]
-                self._mg_padded += [t for t, _ in r1 + r2]
-                self.mg_r1_list = [v for _, v in r1]
-                self.mg_r2_list = [v for _, v in r2]
-                t1 = torch.tensor([int(t.data_ptr()) for t, _ in r1], dtype=torch.int64, device=device)
-                t2 = torch.tensor([int(t.data_ptr()) for t, _ in r2], dtype=torch.int64, device=device)
-                self._keep += [t1, t2]
-                g1 = dict(table=t1)
-                g2 = dict(table=t2)
-            self.reset_main_grads()
-            sh = ((mk.grad(base=self.mg_s1, ld=lh, row_offset=0, dtype=mgd),
-                   mk.grad(base=self.mg_s1, ld=lh, row_offset=I, dtype=mgd),
-                   mk.grad(base=self.mg_s2, ld=li, dtype=mgd)) if shared
-                  else (mk.moe_grad(), mk.moe_grad(), mk.moe_grad()))
-            self.main_grads = mk.moe_main_grads(
-                *sh,
-                mk.grad(ld=lh, row_offset=0, dtype=mgd, **g1), mk.grad(ld=lh, row_offset=I, dtype=mgd, **g1),
-                mk.grad(ld=li, dtype=mgd, **g2))
+                self._packed_main_grads(mg, mgd, lh, li)
             if shared_gate:
                 self.main_grads.shared_out_gate = mk.grad(base=self.mg_gate, ld=H, dtype=mgd)
 
+    def _packed_main_grads(self, mg, mgd, lh, li):
+        """FC1 main_grads as one [2I, H] matrix per expert, gate and up as row views."""
+        cfg, device = self.cfg, self.device
+        H, E, I = cfg.hidden, cfg.experts, cfg.inter
+        (p1, self._mg_s1), (p2, self.mg_s2) = mg(2 * I, H), mg(H, I)
+        self._mg_padded += [p1, p2]
+        if cfg.layout == "single":
+            (p1, self.mg_r1), (p2, self.mg_r2) = mg(E, 2 * I, H), mg(E, H, I)
+            self._mg_padded += [p1, p2]
+            g1 = dict(base=p1, expert_stride=2 * I * lh)
+            g2 = dict(base=p2, expert_stride=H * li)
+            self._mg_r1_list = [self.mg_r1[e] for e in range(E)]
+            self.mg_r2_list = [self.mg_r2[e] for e in range(E)]
+        else:
+            r1 = [mg(2 * I, H) for _ in range(E)]
+            r2 = [mg(H, I) for _ in range(E)]
+            self._mg_padded += [t for t, _ in r1 + r2]
+            self._mg_r1_list = [v for _, v in r1]
+            self.mg_r2_list = [v for _, v in r2]
+            t1 = torch.tensor([int(t.data_ptr()) for t, _ in r1], dtype=torch.int64, device=device)
+            t2 = torch.tensor([int(t.data_ptr()) for t, _ in r2], dtype=torch.int64, device=device)
+            self._keep += [t1, t2]
+            g1 = dict(table=t1)
+            g2 = dict(table=t2)
+        self.reset_main_grads()
+        sh = ((mk.grad(base=self._mg_s1, ld=lh, row_offset=0, dtype=mgd),
+               mk.grad(base=self._mg_s1, ld=lh, row_offset=I, dtype=mgd),
+               mk.grad(base=self.mg_s2, ld=li, dtype=mgd)) if self.shared
+              else (mk.moe_grad(), mk.moe_grad(), mk.moe_grad()))
+        self.main_grads = mk.moe_main_grads(
+            *sh,
+            mk.grad(ld=lh, row_offset=0, dtype=mgd, **g1), mk.grad(ld=lh, row_offset=I, dtype=mgd, **g1),
+            mk.grad(ld=li, dtype=mgd, **g2))
+
+    def _sep_main_grads(self, mg, mgd, lh, li):
+        """FC1 main_grads with the gate and up halves in allocations of their own."""
+        cfg, device = self.cfg, self.device
+        H, E, I = cfg.hidden, cfg.experts, cfg.inter
+        (a, sg_), (b, su_), (c, self.mg_s2) = mg(I, H), mg(I, H), mg(H, I)
+        self._mg_padded += [a, b, c]
+        self._s1_parts = (sg_, su_)
+        descs = []
+        if cfg.layout == "single":
+            (a, rg_), (b, ru_), (c, self.mg_r2) = mg(E, I, H), mg(E, I, H), mg(E, H, I)
+            self._mg_padded += [a, b, c]
+            self._r1_parts = [(rg_[e], ru_[e]) for e in range(E)]
+            self.mg_r2_list = [self.mg_r2[e] for e in range(E)]
+            descs = [dict(base=a, expert_stride=I * lh), dict(base=b, expert_stride=I * lh),
+                     dict(base=c, expert_stride=H * li)]
+        else:
+            parts = [[mg(I, H) for _ in range(E)], [mg(I, H) for _ in range(E)], [mg(H, I) for _ in range(E)]]
+            self._mg_padded += [t for lst in parts for t, _ in lst]
+            self._r1_parts = [(parts[0][e][1], parts[1][e][1]) for e in range(E)]
+            self.mg_r2_list = [v for _, v in parts[2]]
+            for lst in parts:
+                tab = torch.tensor([int(t.data_ptr()) for t, _ in lst], dtype=torch.int64, device=device)
+                self._keep.append(tab)
+                descs.append(dict(table=tab))
+        self.reset_main_grads()
+        sh = ((mk.grad(base=sg_, ld=lh, dtype=mgd), mk.grad(base=su_, ld=lh, dtype=mgd),
+               mk.grad(base=self.mg_s2, ld=li, dtype=mgd)) if self.shared
+              else (mk.moe_grad(), mk.moe_grad(), mk.moe_grad()))
+        self.main_grads = mk.moe_main_grads(*sh, mk.grad(ld=lh, dtype=mgd, **descs[0]),
+                                            mk.grad(ld=lh, dtype=mgd, **descs[1]),
+                                            mk.grad(ld=li, dtype=mgd, **descs[2]))
+
+    @property
+    def mg_s1(self) -> torch.Tensor:
+        """The shared FC1 main_grad as [2I, H] (a fresh concatenation with separate halves)."""
+        return torch.cat(self._s1_parts) if self.sep else self._mg_s1
+
+    @property
+    def mg_r1_list(self) -> list:
+        """Each routed expert's FC1 main_grad as [2I, H] (fresh concatenations with separate halves)."""
+        return [torch.cat(p) for p in self._r1_parts] if self.sep else self._mg_r1_list
+
     # ------------------------------------------------------------------
     def reset_main_grads(self):
-        """Every main_grad buffer starts from the exact pattern (expert e's phase = e)."""
-        fill_main_grad_pattern(self.mg_s1, 0)
+        """Every main_grad buffer starts from the exact pattern (expert e's phase = e), over
+        the logical [2I, H] FC1 matrix also when its halves are separate."""
+        def fill_fc1(dst, phase):
+            if not self.sep:
+                fill_main_grad_pattern(dst, phase)
+                return
+            g, u = dst
+            tmp = torch.empty((2 * g.shape[0], g.shape[1]), dtype=g.dtype, device=g.device)
+            fill_main_grad_pattern(tmp, phase)
+            g.copy_(tmp[:g.shape[0]])
+            u.copy_(tmp[g.shape[0]:])
+        fill_fc1(self._s1_parts if self.sep else self._mg_s1, 0)
         fill_main_grad_pattern(self.mg_gate, 0)
         fill_main_grad_pattern(self.mg_s2, 0)
-        for e, (a, b) in enumerate(zip(self.mg_r1_list, self.mg_r2_list)):
-            fill_main_grad_pattern(a, e)
+        r1 = self._r1_parts if self.sep else self._mg_r1_list
+        for e, (a, b) in enumerate(zip(r1, self.mg_r2_list)):
+            fill_fc1(a, e)
             fill_main_grad_pattern(b, e)
 
     def main_grad_pads_untouched(self) -> bool:

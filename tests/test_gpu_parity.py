@@ -443,6 +443,35 @@ def test_padded_row_strides(gpu_lib, routed, layout, shape, mgd):
     _check_backward(padded, W, tol=tol_of(padded))
 
 
+@pytest.mark.parametrize("routed,layout,shape,mgd,pad", [
+    ("bf16", "single", (300, 256, 6, 3, 128), "fp32", 0),
+    ("bf16", "table", (900, 256, 3, 3, 128), "bf16", 48),   # the wide BF16 shapes
+    ("mxfp8", "single", (260, 384, 5, 2, 256), "fp32", 0),
+    ("mxfp8", "table", (300, 256, 6, 3, 128), "fp32", 48),
+])
+def test_separate_gate_up_allocations(gpu_lib, routed, layout, shape, mgd, pad):
+    """The gate and up halves of every FC1 weight (payload and scales, shared and routed) and
+    of every FC1 main_grad in allocations of their own, described with row offset 0: the
+    results equal the call on row views of combined tensors bit for bit and match the
+    oracle."""
+    T, H, E, K, I = shape
+    cfg = gen.custom(T, H, E, K, I, routed=routed, layout=layout, short_frac=0.1, short_max=max(1, K - 1),
+                     idx=1200 + T)
+    runs = []
+    for sep in (False, True):
+        dp = _dp(cfg, main_grad_dtype=mgd, pad_bytes=pad, separate_gate_up=sep)
+        dp.forward()
+        dp.backward()
+        torch.cuda.synchronize()
+        runs.append(dp)
+    packed, sep = runs
+    assert sep.main_grad_pads_untouched(), "a main_grad pad was written"
+    _assert_same_bits(packed, sep)
+    W = oracle_weights(sep)
+    _check_forward(sep, W, tol=tol_of(sep))
+    _check_backward(sep, W, tol=tol_of(sep))
+
+
 def test_hip_graph_replay_matches_eager(gpu_lib):
     """Both calls enqueue only kernels on the caller's stream, so a captured graph of
     forward + backward replays bit-identically to the eager calls (main_grad reset
