@@ -472,11 +472,15 @@ def test_separate_gate_up_allocations(gpu_lib, routed, layout, shape, mgd, pad):
     _check_backward(sep, W, tol=tol_of(sep))
 
 
-def test_hip_graph_replay_matches_eager(gpu_lib):
+@pytest.mark.parametrize("which", ["small", 2, 4])
+def test_hip_graph_replay_matches_eager(gpu_lib, which):
     """Both calls enqueue only kernels on the caller's stream, so a captured graph of
     forward + backward replays bit-identically to the eager calls (main_grad reset
-    eagerly between replays, other eager work in between)."""
-    cfg = gen.custom(300, 256, 6, 3, 128, short_frac=0.1, short_max=2, idx=503)
+    eagerly between replays, other eager work in between): a small ragged layer, the
+    4096-token BF16 layer and the 8192-token MXFP8 layer in their benchmark launch
+    configurations."""
+    cfg = (gen.custom(300, 256, 6, 3, 128, short_frac=0.1, short_max=2, idx=503) if which == "small"
+           else gen.config(which))
     dp = _dp(cfg)
     names = ("out", "dx", "dprobs", "mg_r1", "mg_r2", "mg_s1", "mg_s2")
     dp.reset_main_grads()
@@ -625,11 +629,13 @@ def test_recompute_is_bit_identical_and_matches_oracle(gpu_lib, routed, layout, 
     _check_backward(rc, W, tol=tol)
 
 
-def test_recompute_full_size_bit_identical(gpu_lib):
-    """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024: recompute mode against
-    the saving mode, every output and main_grad bit for bit; the saved context shrinks
-    from the activations to the routing state."""
-    cfg = gen.config(2)
+@pytest.mark.parametrize("idx", [2, 3, 5])
+def test_recompute_full_size_bit_identical(gpu_lib, idx):
+    """Recompute mode against the saving mode at full size, every output and main_grad bit
+    for bit: the 4096-token layer with BF16 and with MXFP8 routed weights (pointer tables),
+    and the 6-expert share on the wide BF16 shapes; the saved context shrinks from the
+    activations to the routing state."""
+    cfg = gen.config(idx)
     ref = _dp(cfg)
     ref.forward()
     ref.backward()
