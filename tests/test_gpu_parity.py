@@ -230,6 +230,23 @@ def _same_bits(a, b):
                for x, y in zip(a, b))
 
 
+def _run_twice_same_bits(dp, after_forward=None):
+    """Forward + backward twice from the same main_grad start; every output and main_grad
+    bit must match.  after_forward(dp) runs between the second forward and backward."""
+    runs = []
+    for i in range(2):
+        dp.reset_main_grads()
+        dp.forward()
+        torch.cuda.synchronize()
+        if i == 1 and after_forward is not None:
+            after_forward(dp)
+        dp.backward()
+        torch.cuda.synchronize()
+        runs.append(_bitwise_snapshot(dp))
+    assert _same_bits(*runs), f"two runs of {dp.cfg.name} differ"
+    print("[determinism] two runs bit-identical", flush=True)
+
+
 def test_full_size_bf16_layer_full_tensors(gpu_lib):
     """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024 (force-balanced routing),
     the benchmark's launch configuration: run twice, bit for bit the same; then every
@@ -237,16 +254,7 @@ def test_full_size_bf16_layer_full_tensors(gpu_lib):
     shared expert against the oracle."""
     cfg = gen.config(2)
     dp = _dp(cfg, threads=16)
-    runs = []
-    for _ in range(2):
-        dp.reset_main_grads()
-        dp.forward()
-        dp.backward()
-        torch.cuda.synchronize()
-        runs.append(_bitwise_snapshot(dp))
-    assert _same_bits(*runs), "two runs of the 4096-token layer differ"
-    del runs
-    print("[determinism] two runs bit-identical", flush=True)
+    _run_twice_same_bits(dp)
     check_routing_state(dp)
     check_full(dp, oracle_weights(dp), BF16_TOL)
 
@@ -259,16 +267,7 @@ def test_full_size_ep_share_bf16_full_tensors(gpu_lib):
     the oracle."""
     cfg = gen.config(5)
     dp = _dp(cfg, threads=16)
-    runs = []
-    for _ in range(2):
-        dp.reset_main_grads()
-        dp.forward()
-        dp.backward()
-        torch.cuda.synchronize()
-        runs.append(_bitwise_snapshot(dp))
-    assert _same_bits(*runs), "two runs of the 6-expert share differ"
-    del runs
-    print("[determinism] two runs bit-identical", flush=True)
+    _run_twice_same_bits(dp)
     check_routing_state(dp)
     check_full(dp, oracle_weights(dp), BF16_TOL)
 
@@ -300,16 +299,13 @@ def test_mxfp8_forward_backward_matches_oracle(gpu_lib, layout, shape):
 
 def test_full_size_mxfp8_layer_full_tensors(gpu_lib):
     """4096 tokens, hidden 4096, 96 experts, top-4, inter 1024, skewed softmax routing,
-    MXFP8 routed weights in per-expert allocations through device pointer tables: the x and
-    w dy codes bit for bit; every token's out, dx and dprobs and the main_grad deltas of all
-    96 routed experts and the shared expert against the oracle."""
+    MXFP8 routed weights in per-expert allocations through device pointer tables: run twice,
+    bit for bit the same; the x and w dy codes bit for bit; every token's out, dx and dprobs
+    and the main_grad deltas of all 96 routed experts and the shared expert against the
+    oracle."""
     cfg = gen.config(3)
     dp = _dp(cfg, threads=16)
-    dp.forward()
-    torch.cuda.synchronize()
-    check_x_codes(dp)
-    dp.backward()
-    torch.cuda.synchronize()
+    _run_twice_same_bits(dp, check_x_codes)
     check_dy_codes(dp)
     check_routing_state(dp)
     check_full(dp, oracle_weights(dp), MXFP8_TOL)
@@ -317,16 +313,12 @@ def test_full_size_mxfp8_layer_full_tensors(gpu_lib):
 
 def test_large_mxfp8_layer_every_token(gpu_lib):
     """8192 tokens, hidden 7168, 64 experts, top-6, inter 2048, 2% of tokens with fewer
-    than 6 routes, MXFP8 routed weights: x codes in full and w dy codes on sampled slots
-    bit for bit; every token's out, dx and dprobs, and the main_grad deltas of all 64
-    routed experts and of the shared expert."""
+    than 6 routes, MXFP8 routed weights: run twice, bit for bit the same; x codes in full
+    and w dy codes on sampled slots bit for bit; every token's out, dx and dprobs, and the
+    main_grad deltas of all 64 routed experts and of the shared expert."""
     cfg = gen.config(4)
     dp = _dp(cfg, threads=16)
-    dp.forward()
-    torch.cuda.synchronize()
-    check_x_codes(dp)
-    dp.backward()
-    torch.cuda.synchronize()
+    _run_twice_same_bits(dp, check_x_codes)
     check_dy_codes(dp, max_slots=8192)
     check_routing_state(dp)
     check_full(dp, oracle_weights(dp), MXFP8_TOL)
@@ -338,19 +330,7 @@ def test_full_size_ep_share_mxfp8_full_tensors(gpu_lib):
     the main_grad deltas of all 6 routed experts and the shared expert against the oracle."""
     cfg = gen.config(6)
     dp = _dp(cfg, threads=16)
-    runs = []
-    for i in range(2):
-        dp.reset_main_grads()
-        dp.forward()
-        torch.cuda.synchronize()
-        if i == 1:
-            check_x_codes(dp)
-        dp.backward()
-        torch.cuda.synchronize()
-        runs.append(_bitwise_snapshot(dp))
-    assert _same_bits(*runs), "two runs of the MXFP8 6-expert share differ"
-    del runs
-    print("[determinism] two runs bit-identical", flush=True)
+    _run_twice_same_bits(dp, check_x_codes)
     check_dy_codes(dp)
     check_routing_state(dp)
     check_full(dp, oracle_weights(dp), MXFP8_TOL)
