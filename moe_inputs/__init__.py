@@ -285,9 +285,21 @@ def routed_expert(cfg: Config, e: int) -> dict:
 
 
 def routed_all(cfg: Config, threads: int = 8) -> list[dict]:
-    """All routed experts, generated in parallel (numpy releases the GIL)."""
+    """All routed experts, generated in parallel (numpy releases the GIL).  The last three
+    configurations' results are kept, so that several problems built on one configuration
+    generate its weights once; callers must not write into the arrays."""
+    if cfg in _ROUTED_CACHE:
+        _ROUTED_CACHE[cfg] = _ROUTED_CACHE.pop(cfg)   # most recently used last
+        return _ROUTED_CACHE[cfg]
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
-        return list(ex.map(lambda e: routed_expert(cfg, e), range(cfg.experts)))
+        out = list(ex.map(lambda e: routed_expert(cfg, e), range(cfg.experts)))
+    _ROUTED_CACHE[cfg] = out
+    while len(_ROUTED_CACHE) > 3:
+        _ROUTED_CACHE.pop(next(iter(_ROUTED_CACHE)))
+    return out
+
+
+_ROUTED_CACHE: dict = {}
 
 
 def main_grad_pattern(n: int, phase: int = 0) -> np.ndarray:

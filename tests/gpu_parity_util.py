@@ -75,16 +75,28 @@ def _mg_errs(dp, g, experts, errs):
         errs[f"down{e}"] = rel_err(d2, dd) if np.abs(dd).max() > 0 else float(np.abs(d2).max())
 
 
-def check_full(dp, W, tol, experts=None, chunk=16):
-    """Every token's out, dx and dprobs, and the main_grad deltas of `experts` (every routed
-    expert when None) and of the shared expert, against the oracle.  The oracle runs in
-    phases (forward; token gradients; weight gradients a few experts at a time; the shared
-    expert), each printing when it ends."""
+def check_full(dp, W, tol, experts=None, chunk=16, tokens=True, weights=True):
+    """Every token's out, dx and dprobs (tokens=True), and the main_grad deltas of `experts`
+    (every routed expert when None) and of the shared expert (weights=True), against the
+    oracle.  The oracle runs in phases (forward; token gradients; weight gradients a few
+    experts at a time; the shared expert), each printing when it ends."""
     cfg = dp.cfg
-    I, H = cfg.inter, cfg.hidden
     args = (dp.np_probs, dp.np_rmap, cfg.topk, W)
     errs = {}
     t0 = time.time()
+    if tokens:
+        _check_full_tokens(dp, args, errs, t0)
+    if weights:
+        _check_full_weights(dp, args, errs, t0, experts, chunk)
+    worst = max(errs, key=lambda k: errs[k])
+    print(f"[parity] full tensors: " + " ".join(f"{k} {errs[k]:.3e}" for k in ("out", "dx", "dprobs") if k in errs)
+          + f" worst {worst} {errs[worst]:.3e} (tol {tol})", flush=True)
+    bad = {k: v for k, v in errs.items() if not (v <= tol)}
+    assert not bad, f"over tolerance {tol}: {bad}"
+    return errs
+
+
+def _check_full_tokens(dp, args, errs, t0):
     ref = O.moe_forward(dp.np_x, *args)
     errs["out"] = rel_err(to_f64(dp.out), ref)
     del ref
@@ -96,6 +108,11 @@ def check_full(dp, W, tol, experts=None, chunk=16):
     assert np.all(dpr[dp.np_rmap == 0] == 0), "dprobs must be exactly zero off the routing map"
     del g, dpr
     print(f"[full] dx {errs['dx']:.3e} dprobs {errs['dprobs']:.3e} ({time.time() - t0:.0f} s)", flush=True)
+
+
+def _check_full_weights(dp, args, errs, t0, experts, chunk):
+    cfg = dp.cfg
+    I, H = cfg.inter, cfg.hidden
     none = np.zeros(0, dtype=np.int64)
     ex = list(range(cfg.experts)) if experts is None else list(experts)
     for i in range(0, len(ex), chunk):
@@ -115,12 +132,6 @@ def check_full(dp, W, tol, experts=None, chunk=16):
         errs["shared_down"] = rel_err(s2, dd)
         print(f"[full] shared main_grad gate {errs['shared_gate']:.3e} up {errs['shared_up']:.3e} down "
               f"{errs['shared_down']:.3e} ({time.time() - t0:.0f} s)", flush=True)
-    worst = max(errs, key=lambda k: errs[k])
-    print(f"[parity] full tensors: out {errs['out']:.3e} dx {errs['dx']:.3e} dprobs {errs['dprobs']:.3e} "
-          f"worst {worst} {errs[worst]:.3e} (tol {tol})", flush=True)
-    bad = {k: v for k, v in errs.items() if not (v <= tol)}
-    assert not bad, f"over tolerance {tol}: {bad}"
-    return errs
 
 
 # ----------------------------------------------------------------------------------
